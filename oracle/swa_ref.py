@@ -1,0 +1,296 @@
+"""Plain float64 definitions of sliding-window attention.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): the HIP library never
+imports or calls this module.
+
+Sources (the five pages this method is described on):
+  * robocikowo.com glossary entry "Sliding Window Attention" (Polish), the
+    opening definition paragraph: query i may take keys only from
+    [i-W+1, i] (causal) or [i-W/2, i+W/2] (symmetric); every other logit is
+    set to -inf before the softmax, which zeroes its share.
+  * aivaro.ru answer 629 "Как работает sliding window attention в Mistral и
+    Longformer?" (Russian), section 3: Mistral's window is the previous 4096
+    tokens including the token itself; section 4.1: Longformer takes W/2
+    neighbours on the left and W/2 on the right.
+  * Ultralytics glossary "Sliding Window Attention" (Italian), section
+    "Come cresce la finestra con la profondita": the causal window as the
+    boolean mask 0 <= i-j < w, its per-layer score count, the reach of the
+    last token through stacked layers, and the w-slot circular KV buffer that
+    writes position i into slot i mod w.
+  * "Finding 15 - sliding-window attention architectures (Mistral-style)
+    compile with zero code changes", section "Why this needed no exporter
+    changes": attention is Q@K^T + mask, softmax, @V with the window living
+    only in an additive mask tensor.
+  * "Sliding-window and hybrid attention" (serving guide), section "Check
+    yourself": a windowed layer's KV stops growing once it holds W tokens.
+
+Shapes (head-major, contiguous):
+  q, out : [B, Hq, T, d]      k, v : [B, Hkv, T, d]
+  k_ring, v_ring : [B, Hkv, W, d]
+Query head h reads KV head h // (Hq // Hkv) (grouped-query attention with
+contiguous groups; the pages only say "GQA 32/8").
+
+Readings of points the pages leave open (each also listed in the design doc):
+  * symmetric window: |i-j| <= floor(W/2), inclusive on both sides, so an
+    interior row sees W+1 keys when W is even;
+  * windows are clipped to [0, T): no padding, no sink tokens;
+  * scale is an argument (the workloads use 1/sqrt(d));
+  * decode: the query at position p is appended first, then sees positions
+    [max(0, p-W+1), p]; a sequence with p < 0 holds no tokens and its output
+    is defined as zeros.
+"""
+
+import math
+
+import numpy as np
+
+CAUSAL = 0
+SYMMETRIC = 1
+
+
+# --------------------------------------------------------------------------
+# The window
+# --------------------------------------------------------------------------
+
+def allowed(i, j, T, W, mode):
+    """True when query i may attend to key j.
+
+    Causal: j in [i-W+1, i] (robocikowo definition paragraph; Ultralytics mask
+    0 <= i-j < w).  Symmetric: j in [i-W/2, i+W/2] (robocikowo definition
+    paragraph; aivaro section 4.1), read as |i-j| <= floor(W/2).  Both are
+    clipped to the sequence 0 <= j < T.
+    """
+    if not (0 <= j < T):
+        return False
+    if mode == CAUSAL:
+        return 0 <= i - j <= W - 1
+    if mode == SYMMETRIC:
+        return abs(i - j) <= W // 2
+    raise ValueError("unknown mode %r" % (mode,))
+
+
+def band(i, T, W, mode):
+    """Inclusive key range [lo, hi] that query i may attend to."""
+    if mode == CAUSAL:
+        return max(0, i - W + 1), i
+    if mode == SYMMETRIC:
+        h = W // 2
+        return max(0, i - h), min(T - 1, i + h)
+    raise ValueError("unknown mode %r" % (mode,))
+
+
+def window_mask(T, W, mode):
+    """Boolean [T, T] mask, True where query i (row) may see key j (column).
+
+    Built from the offset i - j exactly as the Ultralytics section builds the
+    causal mask; the symmetric mask bounds |i - j| instead.
+    """
+    pos = np.arange(T)
+    offset = pos[:, None] - pos[None, :]
+    if mode == CAUSAL:
+        return (offset >= 0) & (offset < W)
+    if mode == SYMMETRIC:
+        return np.abs(offset) <= W // 2
+    raise ValueError("unknown mode %r" % (mode,))
+
+
+def additive_mask(T, W, mode):
+    """float64 [T, T]: 0 where allowed, -inf elsewhere (the additive mask
+    tensor of Finding 15, "Why this needed no exporter changes")."""
+    return np.where(window_mask(T, W, mode), 0.0, -np.inf)
+
+
+def scores_per_layer(T, W, mode):
+    """Number of (query, key) scores one layer computes: the mask's count."""
+    return int(window_mask(T, W, mode).sum())
+
+
+def stacked_reach(T, W, layers, mode=CAUSAL):
+    """Reach of the last token after 1..layers stacked windowed layers.
+
+    The Ultralytics section traces how far information travels by multiplying
+    the boolean mask by itself: after layer L the set of positions that can
+    influence a token is the support of mask^L.  Returns the list of counts
+    for the last row, one per layer.
+    """
+    mask = window_mask(T, W, mode).astype(np.int64)
+    reach = mask.copy()
+    out = []
+    for _ in range(layers):
+        out.append(int((reach[-1] > 0).sum()))
+        reach = ((mask @ reach) > 0).astype(np.int64)
+    return out
+
+
+def kv_head(h, Hq, Hkv):
+    """KV head read by query head h: contiguous groups of Hq // Hkv heads."""
+    return h // (Hq // Hkv)
+
+
+# --------------------------------------------------------------------------
+# Attention: three forms of the same definition
+#   O = softmax(scale * Q K^T + M) V,   M = 0 inside the window, -inf outside
+# --------------------------------------------------------------------------
+
+def _as64(*arrays):
+    return [np.asarray(a, dtype=np.float64) for a in arrays]
+
+
+def _check_shapes(q, k, v):
+    B, Hq, T, d = q.shape
+    Bk, Hkv, Tk, dk = k.shape
+    if (Bk, Tk, dk) != (B, T, d) or v.shape != k.shape:
+        raise ValueError("shape mismatch q%s k%s v%s" % (q.shape, k.shape, v.shape))
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return B, Hq, Hkv, T, d
+
+
+def attention_loop(q, k, v, W, mode, scale):
+    """Pure-Python loops over (b, h, i, j, c) for tiny inputs.
+
+    For each query row: score every allowed key, subtract the row maximum,
+    exponentiate, normalise, and take the weighted sum of value rows.
+    """
+    q, k, v = _as64(q, k, v)
+    B, Hq, Hkv, T, d = _check_shapes(q, k, v)
+    out = np.zeros((B, Hq, T, d))
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            for i in range(T):
+                keys = [j for j in range(T) if allowed(i, j, T, W, mode)]
+                s = []
+                for j in keys:
+                    acc = 0.0
+                    for c in range(d):
+                        acc += float(q[b, h, i, c]) * float(k[b, g, j, c])
+                    s.append(scale * acc)
+                m = max(s)
+                e = [math.exp(x - m) for x in s]
+                tot = sum(e)
+                for c in range(d):
+                    acc = 0.0
+                    for w, j in zip(e, keys):
+                        acc += w * float(v[b, g, j, c])
+                    out[b, h, i, c] = acc / tot
+    return out
+
+
+def _softmax_rows(S):
+    m = S.max(axis=-1, keepdims=True)
+    P = np.exp(S - m)
+    return P / P.sum(axis=-1, keepdims=True)
+
+
+def attention_dense(q, k, v, W, mode, scale):
+    """Dense [T, T] scores plus the explicit additive mask, for T <= ~4096."""
+    q, k, v = _as64(q, k, v)
+    B, Hq, Hkv, T, d = _check_shapes(q, k, v)
+    M = additive_mask(T, W, mode)
+    out = np.empty((B, Hq, T, d))
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            S = scale * (q[b, h] @ k[b, g].T) + M
+            out[b, h] = _softmax_rows(S) @ v[b, g]
+    return out
+
+
+def attention_banded(q, k, v, W, mode, scale, block=128, heads=None):
+    """Row blocks of `block` queries against the key range their windows
+    cover, with the explicit additive mask on that block.  Identical to the
+    dense form because every key outside the range is masked to an exact zero
+    weight.  `heads` optionally restricts the computation to a list of
+    (b, h) pairs; other rows of the result are left as NaN.
+    """
+    q, k, v = _as64(q, k, v)
+    B, Hq, Hkv, T, d = _check_shapes(q, k, v)
+    out = np.full((B, Hq, T, d), np.nan)
+    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
+    pos = np.arange(T)
+    for b, h in pairs:
+        g = kv_head(h, Hq, Hkv)
+        for r0 in range(0, T, block):
+            r1 = min(T, r0 + block)
+            lo = band(r0, T, W, mode)[0]
+            hi = band(r1 - 1, T, W, mode)[1]
+            rows = pos[r0:r1, None]
+            cols = pos[None, lo:hi + 1]
+            off = rows - cols
+            if mode == CAUSAL:
+                ok = (off >= 0) & (off < W)
+            else:
+                ok = np.abs(off) <= W // 2
+            M = np.where(ok, 0.0, -np.inf)
+            S = scale * (q[b, h, r0:r1] @ k[b, g, lo:hi + 1].T) + M
+            out[b, h, r0:r1] = _softmax_rows(S) @ v[b, g, lo:hi + 1]
+    return out
+
+
+def attention_rows(q, k, v, W, mode, scale, b, h, rows):
+    """Selected query rows of one (b, h), each over exactly its own window.
+    Used to check sampled outputs of full-size problems one by one.
+    Returns float64 [len(rows), d]."""
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    g = kv_head(h, Hq, Hkv)
+    res = np.empty((len(rows), d))
+    for n, i in enumerate(rows):
+        lo, hi = band(int(i), T, W, mode)
+        qi = np.asarray(q[b, h, i], dtype=np.float64)
+        kk = np.asarray(k[b, g, lo:hi + 1], dtype=np.float64)
+        vv = np.asarray(v[b, g, lo:hi + 1], dtype=np.float64)
+        s = scale * (kk @ qi)
+        p = np.exp(s - s.max())
+        res[n] = (p / p.sum()) @ vv
+    return res
+
+
+# --------------------------------------------------------------------------
+# Ring-buffer KV cache and decode
+# --------------------------------------------------------------------------
+
+def ring_append(k_ring, v_ring, pos, k_new, v_new):
+    """Write the new K/V row of each sequence into slot pos mod W, in place.
+
+    Ultralytics ring-buffer paragraph: a buffer of w slots, position i goes
+    to slot i mod w and overwrites the oldest entry; robocikowo: only the last
+    W tokens per layer are kept, new tokens overwrite the oldest (FIFO).
+    Works on any dtype (a bit copy).  k_ring [B, Hkv, W, d], k_new [B, Hkv, d],
+    pos [B].  A negative position writes nothing.
+    """
+    W = k_ring.shape[2]
+    for b, p in enumerate(np.asarray(pos).tolist()):
+        if p < 0:
+            continue
+        s = p % W
+        k_ring[b, :, s, :] = k_new[b]
+        v_ring[b, :, s, :] = v_new[b]
+
+
+def decode(q, k_ring, v_ring, pos, scale):
+    """One query token per sequence against its ring cache.
+
+    q [B, Hq, d]; rings [B, Hkv, W, d]; pos [B] = position of the query,
+    whose own K/V row is already in the ring.  The query sees positions
+    [max(0, p-W+1), p] (the causal window), stored at slots p' mod W.
+    Returns float64 [B, Hq, d]; a sequence with p < 0 gives zeros.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, d = q.shape
+    Hkv, W = k_ring.shape[1], k_ring.shape[2]
+    out = np.zeros((B, Hq, d))
+    for b, p in enumerate(np.asarray(pos).tolist()):
+        if p < 0:
+            continue
+        positions = np.arange(max(0, p - W + 1), p + 1)
+        slots = positions % W
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            kk = np.asarray(k_ring[b, g, slots], dtype=np.float64)
+            vv = np.asarray(v_ring[b, g, slots], dtype=np.float64)
+            s = scale * (kk @ q[b, h])
+            e = np.exp(s - s.max())
+            out[b, h] = (e / e.sum()) @ vv
+    return out

@@ -1,0 +1,324 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself alone: each check ties it to a
+value a page prints (tests/golden/), a closed form, a library routine that
+computes a special case (torch's scaled_dot_product_attention in float64 on
+the CPU), or brute force.  The mutation tests at the end plant plausible
+mistakes in copies of oracle routines and show that a pin catches each one.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle import swa_ref
+
+CAUSAL, SYMMETRIC = oracle.CAUSAL, oracle.SYMMETRIC
+
+
+def rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def sdpa(q, k, v, scale, mask=None, is_causal=False):
+    """torch's own attention in float64 on the CPU (GQA by repeat-interleave)."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))
+    am = None if mask is None else torch.from_numpy(mask)
+    o = F.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=am, is_causal=is_causal,
+                                       scale=scale, enable_gqa=q.shape[1] != k.shape[1])
+    return o.numpy()
+
+
+def torch_band(T, W, mode):
+    """Band mask from torch's triangle routines (no offset arithmetic)."""
+    ones = torch.ones(T, T, dtype=torch.bool)
+    if mode == CAUSAL:
+        return ones.tril(0).triu(-(W - 1)).numpy()
+    h = W // 2
+    return ones.tril(h).triu(-h).numpy()
+
+
+# ---------------------------------------------------------------- page values
+
+def test_page_score_counts(golden):
+    g = golden("mask_counts_t16_w4.txt")
+    T, W = g["seq_len"], g["window"]
+    assert oracle.scores_per_layer(T, W, CAUSAL) == g["scores_window"]
+    # full causal attention is the window with W >= T
+    assert oracle.scores_per_layer(T, T, CAUSAL) == g["scores_full_causal"]
+    assert oracle.scores_per_layer(T, 10 * T, CAUSAL) == g["scores_full_causal"]
+
+
+def test_page_stacked_reach(golden):
+    g = golden("mask_counts_t16_w4.txt")
+    T, W = g["seq_len"], g["window"]
+    assert oracle.stacked_reach(T, W, len(g["reach"])) == g["reach"]
+
+
+def test_reach_closed_form_and_upper_bound(golden):
+    # brute force boolean mask powers agree with 1 + L(W-1) while the reach
+    # stays inside the sequence, and never exceed the L*W bound
+    for T, W, L in [(64, 5, 6), (100, 8, 9), (40, 2, 12), (33, 1, 4)]:
+        got = oracle.stacked_reach(T, W, L)
+        for layer, r in enumerate(got, start=1):
+            assert r == min(T, 1 + layer * (W - 1))
+            assert r <= layer * W
+    g = golden("receptive_field_mistral.txt")
+    L, W = g["layers"], g["window"]
+    assert L * W == g["upper_bound"]
+    assert 1 + L * (W - 1) <= g["upper_bound"]
+
+
+def test_band_sum_closed_forms():
+    # causal: sum_i min(i+1, W) = W(W+1)/2 + (T-W)W for T >= W
+    for T, W in [(2048, 32), (16384, 4096), (16, 4), (37, 5)]:
+        want = W * (W + 1) // 2 + (T - W) * W
+        got = sum(oracle.band(i, T, W, CAUSAL)[1] - oracle.band(i, T, W, CAUSAL)[0] + 1
+                  for i in range(T))
+        assert got == want
+        if T <= 4096:
+            assert oracle.scores_per_layer(T, W, CAUSAL) == want
+    # symmetric with h = W//2 and T >= 2h+1: T(2h+1) - h(h+1)
+    for T, W in [(4096, 512), (50, 7), (50, 8)]:
+        h = W // 2
+        want = T * (2 * h + 1) - h * (h + 1)
+        got = sum(oracle.band(i, T, W, SYMMETRIC)[1] - oracle.band(i, T, W, SYMMETRIC)[0] + 1
+                  for i in range(T))
+        assert got == want
+        assert oracle.scores_per_layer(T, W, SYMMETRIC) == want
+    # the in-window work of the three full-size prefill workloads
+    assert 32 * 65 == 2080 and (32 * 33 // 2 + (2048 - 32) * 32) == 65040
+    assert 4096 * 4097 // 2 + (16384 - 4096) * 4096 == 58722304
+
+
+def test_band_matches_mask_rows():
+    for mode, W in [(CAUSAL, 5), (SYMMETRIC, 5), (SYMMETRIC, 6), (CAUSAL, 1)]:
+        T = 23
+        M = oracle.window_mask(T, W, mode)
+        for i in range(T):
+            lo, hi = oracle.band(i, T, W, mode)
+            idx = np.flatnonzero(M[i])
+            assert idx[0] == lo and idx[-1] == hi and len(idx) == hi - lo + 1
+            assert all(oracle.allowed(i, j, T, W, mode) == bool(M[i, j]) for j in range(T))
+            assert not any(oracle.allowed(i, j, T, W, mode) for j in (-2, -1, T, T + 1))
+
+
+# --------------------------------------------------- special cases vs library
+
+@pytest.mark.parametrize("T,d,Hq,Hkv", [(16, 64, 1, 1), (40, 8, 4, 2), (33, 16, 6, 3)])
+def test_full_window_equals_library_causal(T, d, Hq, Hkv):
+    q, k, v = rand((2, Hq, T, d), 1), rand((2, Hkv, T, d), 2), rand((2, Hkv, T, d), 3)
+    scale = 1 / math.sqrt(d)
+    want = sdpa(q, k, v, scale, is_causal=True)
+    for W in (T, T + 1, 3 * T):
+        np.testing.assert_allclose(oracle.attention_dense(q, k, v, W, CAUSAL, scale), want,
+                                   rtol=0, atol=1e-12)
+        np.testing.assert_allclose(oracle.attention_banded(q, k, v, W, CAUSAL, scale, block=8),
+                                   want, rtol=0, atol=1e-12)
+
+
+def test_wide_symmetric_equals_library_bidirectional():
+    T, d = 21, 8
+    q, k, v = rand((1, 4, T, d), 4), rand((1, 2, T, d), 5), rand((1, 2, T, d), 6)
+    want = sdpa(q, k, v, 0.3)
+    for W in (2 * (T - 1), 2 * T + 1, 100):
+        np.testing.assert_allclose(oracle.attention_dense(q, k, v, W, SYMMETRIC, 0.3), want,
+                                   rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode,W", [(CAUSAL, 4), (CAUSAL, 7), (SYMMETRIC, 6), (SYMMETRIC, 7),
+                                    (CAUSAL, 1), (SYMMETRIC, 1)])
+def test_window_equals_library_with_triangle_mask(mode, W):
+    T, d = 29, 16
+    q, k, v = rand((2, 8, T, d), 7), rand((2, 2, T, d), 8), rand((2, 2, T, d), 9)
+    want = sdpa(q, k, v, 0.25, mask=torch_band(T, W, mode))
+    for got in (oracle.attention_dense(q, k, v, W, mode, 0.25),
+                oracle.attention_banded(q, k, v, W, mode, 0.25, block=8)):
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_window_one_is_identity():
+    # one key per row: softmax weight exactly 1, so O = V bit for bit
+    q, k, v = rand((2, 4, 19, 8), 10), rand((2, 2, 19, 8), 11), rand((2, 2, 19, 8), 12)
+    o = oracle.attention_dense(q, k, v, 1, CAUSAL, 0.5)
+    assert np.array_equal(o, np.repeat(v, 2, axis=1))
+    o = oracle.attention_dense(q, k, v, 1, SYMMETRIC, 0.5)  # floor(1/2) = 0: self only
+    assert np.array_equal(o, np.repeat(v, 2, axis=1))
+
+
+def test_constant_values_give_constant_output():
+    T, d = 30, 8
+    q, k = rand((1, 2, T, d), 13), rand((1, 1, T, d), 14)
+    c = rand((d,), 15)
+    v = np.broadcast_to(c, (1, 1, T, d)).copy()
+    for mode, W in [(CAUSAL, 6), (SYMMETRIC, 9)]:
+        o = oracle.attention_dense(q, k, v, W, mode, 0.4)
+        np.testing.assert_allclose(o, np.broadcast_to(c, o.shape), rtol=0, atol=1e-14)
+
+
+# --------------------------------------------------------------- brute force
+
+@pytest.mark.parametrize("mode,W,T,Hq,Hkv,d", [
+    (CAUSAL, 4, 16, 1, 1, 8), (CAUSAL, 16, 16, 2, 1, 4), (CAUSAL, 3, 11, 4, 2, 5),
+    (SYMMETRIC, 4, 12, 2, 2, 6), (SYMMETRIC, 5, 9, 3, 1, 3), (SYMMETRIC, 30, 7, 1, 1, 4),
+])
+def test_three_forms_agree(mode, W, T, Hq, Hkv, d):
+    q, k, v = rand((2, Hq, T, d), 16), rand((2, Hkv, T, d), 17), rand((2, Hkv, T, d), 18)
+    loop = oracle.attention_loop(q, k, v, W, mode, 0.7)
+    dense = oracle.attention_dense(q, k, v, W, mode, 0.7)
+    banded = oracle.attention_banded(q, k, v, W, mode, 0.7, block=3)
+    np.testing.assert_allclose(dense, loop, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(banded, loop, rtol=0, atol=1e-12)
+    for b in range(2):
+        for h in range(Hq):
+            rows = oracle.attention_rows(q, k, v, W, mode, 0.7, b, h, list(range(T)))
+            np.testing.assert_allclose(rows, loop[b, h], rtol=0, atol=1e-12)
+
+
+def test_locality_outside_window_is_ignored():
+    T, d, W = 40, 8, 6
+    q, k, v = rand((1, 1, T, d), 19), rand((1, 1, T, d), 20), rand((1, 1, T, d), 21)
+    base = oracle.attention_dense(q, k, v, W, CAUSAL, 0.5)
+    i = 25
+    k2, v2 = k.copy(), v.copy()
+    out_of_window = [j for j in range(T) if not oracle.allowed(i, j, T, W, CAUSAL)]
+    k2[0, 0, out_of_window] += 100.0
+    v2[0, 0, out_of_window] -= 50.0
+    pert = oracle.attention_dense(q, k2, v2, W, CAUSAL, 0.5)
+    assert np.array_equal(pert[0, 0, i], base[0, 0, i])
+    assert not np.array_equal(pert[0, 0, i + 1], base[0, 0, i + 1])
+
+
+# ---------------------------------------------------------- ring and decode
+
+def ring_last_writer_holds(append_impl, W=5, P=17, B=2, Hkv=2, d=3):
+    """After appending positions 0..P, slot s holds the row of the latest
+    position p <= P with p = s (mod W); slots never written keep the fill."""
+    rng = np.random.default_rng(22)
+    seq_k = rng.standard_normal((P + 1, B, Hkv, d))
+    seq_v = rng.standard_normal((P + 1, B, Hkv, d))
+    kr = np.full((B, Hkv, W, d), -7.0)
+    vr = np.full((B, Hkv, W, d), -7.0)
+    for p in range(P + 1):
+        append_impl(kr, vr, np.full(B, p), seq_k[p], seq_v[p])
+    for s in range(W):
+        writers = [p for p in range(P + 1) if p % W == s]
+        if not writers:
+            if not (np.all(kr[:, :, s] == -7.0) and np.all(vr[:, :, s] == -7.0)):
+                return False
+            continue
+        p = max(writers)
+        if not (np.array_equal(kr[:, :, s], seq_k[p]) and np.array_equal(vr[:, :, s], seq_v[p])):
+            return False
+    return True
+
+
+def test_ring_last_writer():
+    assert ring_last_writer_holds(oracle.ring_append)
+    assert ring_last_writer_holds(oracle.ring_append, W=4, P=2)  # ring never fills
+    assert ring_last_writer_holds(oracle.ring_append, W=1, P=6)
+
+
+def test_ring_memory_is_constant(golden):
+    g = golden("kv_ring_memory.txt")
+    # the ring holds W slots whatever the position; a full cache holds every token
+    assert g["tokens"] // g["window"] == g["ratio"]
+    W = g["check_window"]
+    rows_at = lambda n: min(n, W)
+    assert rows_at(g["check_from"]) == rows_at(g["check_to"]) == W
+
+
+@pytest.mark.parametrize("W,Hq,Hkv,mode_T", [(4, 1, 1, 16), (16, 1, 1, 16), (3, 4, 2, 13)])
+def test_decode_equals_prefill_row(W, Hq, Hkv, mode_T):
+    T, d, B = mode_T, 8, 2
+    q, k, v = rand((B, Hq, T, d), 23), rand((B, Hkv, T, d), 24), rand((B, Hkv, T, d), 25)
+    scale = 1 / math.sqrt(d)
+    pre = sdpa(q, k, v, scale, mask=torch_band(T, W, CAUSAL))  # library, not the oracle
+    kr = np.full((B, Hkv, W, d), np.nan)
+    vr = np.full((B, Hkv, W, d), np.nan)
+    for p in range(T):
+        oracle.ring_append(kr, vr, np.full(B, p), k[:, :, p], v[:, :, p])
+        got = oracle.decode(q[:, :, p], kr, vr, np.full(B, p), scale)
+        np.testing.assert_allclose(got, pre[:, :, p], rtol=0, atol=1e-12)
+
+
+def test_decode_mixed_positions_and_empty_sequence():
+    B, Hq, Hkv, W, d = 3, 2, 1, 4, 5
+    rng = np.random.default_rng(26)
+    q = rng.standard_normal((B, Hq, d))
+    kr, vr = rng.standard_normal((B, Hkv, W, d)), rng.standard_normal((B, Hkv, W, d))
+    pos = np.array([-1, 1, 9])
+    out = oracle.decode(q, kr, vr, pos, 0.5)
+    assert np.all(out[0] == 0.0)
+    # position 1 sees slots 0 and 1 only; position 9 sees all four slots
+    for b, slots in [(1, [0, 1]), (2, [0, 1, 2, 3])]:
+        for h in range(Hq):
+            s = 0.5 * kr[b, 0, slots] @ q[b, h]
+            w = np.exp(s - s.max())
+            want = (w / w.sum()) @ vr[b, 0, slots]
+            np.testing.assert_allclose(out[b, h], want, rtol=0, atol=1e-13)
+
+
+# ----------------------------------------------- planted mistakes are caught
+
+def test_mutant_window_off_by_one_is_caught(monkeypatch, golden):
+    g = golden("mask_counts_t16_w4.txt")
+
+    def wide_mask(T, W, mode):
+        pos = np.arange(T)
+        off = pos[:, None] - pos[None, :]
+        return (off >= 0) & (off <= W)  # one key too many
+
+    monkeypatch.setattr(swa_ref, "window_mask", wide_mask)
+    assert oracle.scores_per_layer(g["seq_len"], g["window"], CAUSAL) != g["scores_window"]
+    assert swa_ref.stacked_reach(g["seq_len"], g["window"], 4) != g["reach"]
+
+
+def test_mutant_window_without_self_is_caught(monkeypatch, golden):
+    g = golden("mask_counts_t16_w4.txt")
+
+    def shifted_mask(T, W, mode):
+        pos = np.arange(T)
+        off = pos[:, None] - pos[None, :]
+        return (off > 0) & (off <= W)
+
+    monkeypatch.setattr(swa_ref, "window_mask", shifted_mask)
+    assert oracle.scores_per_layer(g["seq_len"], g["window"], CAUSAL) != g["scores_window"]
+
+
+def test_mutant_gqa_mapping_is_caught(monkeypatch):
+    T, d = 12, 4
+    q, k, v = rand((1, 4, T, d), 27), rand((1, 2, T, d), 28), rand((1, 2, T, d), 29)
+    want = sdpa(q, k, v, 0.5, mask=torch_band(T, 3, CAUSAL))
+    monkeypatch.setattr(swa_ref, "kv_head", lambda h, Hq, Hkv: h % Hkv)  # interleaved groups
+    got = swa_ref.attention_dense(q, k, v, 3, CAUSAL, 0.5)
+    assert np.abs(got - want).max() > 1e-3
+
+
+def test_mutant_swapped_operands_and_missing_scale_are_caught():
+    T, d = 12, 4
+    q, k, v = rand((1, 1, T, d), 30), rand((1, 1, T, d), 31), rand((1, 1, T, d), 32)
+    want = sdpa(q, k, v, 0.5, mask=torch_band(T, 3, CAUSAL))
+    assert np.abs(oracle.attention_dense(k, q, v, 3, CAUSAL, 0.5) - want).max() > 1e-3
+    assert np.abs(oracle.attention_dense(q, k, v, 3, CAUSAL, 1.0) - want).max() > 1e-3
+
+
+def test_mutant_ring_slot_is_caught():
+    def shifted_append(k_ring, v_ring, pos, k_new, v_new):
+        W = k_ring.shape[2]
+        for b, p in enumerate(pos):
+            k_ring[b, :, (p + 1) % W] = k_new[b]
+            v_ring[b, :, (p + 1) % W] = v_new[b]
+
+    assert not ring_last_writer_holds(shifted_append)
+
+
+def test_mutant_symmetric_as_causal_is_caught():
+    T, d, W = 15, 4, 6
+    q, k, v = rand((1, 1, T, d), 33), rand((1, 1, T, d), 34), rand((1, 1, T, d), 35)
+    want = sdpa(q, k, v, 0.5, mask=torch_band(T, W, SYMMETRIC))
+    assert np.abs(oracle.attention_dense(q, k, v, W, CAUSAL, 0.5) - want).max() > 1e-3
