@@ -1,0 +1,267 @@
+"""Benchmark of the sliding-window attention hot path on one MI355X.
+
+One step = one pass of the whole path on Mistral-7B shapes:
+  1. swa_prefill   causal, B=1, T=16384, W=4096, 32 query / 8 KV heads, d=128, bf16
+  2. swa_cache_append  one new K/V row for each of 64 sequences (8 KV heads, d=128)
+  3. swa_decode    64 sequences, 32/8 heads, d=128, full W=4096-slot rings,
+                   positions uniform in [4096, 32768)
+Inputs are seeded synthetic N(0,1) values rounded to bf16 (swa_inputs.py),
+resident in HBM before timing starts.
+
+Printed: one JSON line.  `value` is the in-window TFLOP/s of the whole step
+(in-window FLOPs of prefill and decode, 4*d per (query, key) pair in a
+window, over the step time); `parts` gives the prefill TFLOP/s against the
+bf16 matrix peak and the decode KV-read GB/s against the HBM peak, each from
+HIP events around its own launches; `roofline` describes the dominant kernel
+(the prefill); `cpu_baseline` times the fp64 oracle on the host cores on a
+bounded sample of the same work.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import swa_inputs as si  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+METRIC = "SWA prefill in-window TFLOP/s + decode KV-read GB/s, % of MI355X peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_mistral7b_traffic.md")
+
+
+def band_pairs_causal(T, W):
+    """Number of (query, key) pairs inside causal windows of one head."""
+    if T <= W:
+        return T * (T + 1) // 2
+    return W * (W + 1) // 2 + (T - W) * W
+
+
+def prefill_work():
+    c = si.WORKLOADS[3]
+    pairs = band_pairs_causal(c["T"], c["W"]) * c["Hq"] * c["B"]
+    flops = 4 * c["d"] * pairs
+    elem = 2
+    bytes_ = elem * c["T"] * c["d"] * c["B"] * (2 * c["Hq"] + 2 * c["Hkv"])  # Q, O, K, V
+    return flops, bytes_
+
+
+def decode_work(pos):
+    c = si.WORKLOADS[4]
+    rows = np.minimum(pos.astype(np.int64) + 1, c["W"]).sum()  # valid slots per sequence
+    kv_bytes = int(rows) * c["Hkv"] * c["d"] * 2 * 2          # K and V, bf16
+    qo_bytes = 2 * c["B"] * c["Hq"] * c["d"] * 2 + 4 * c["B"]
+    flops = 4 * c["d"] * int(rows) * c["Hq"]
+    return flops, kv_bytes, qo_bytes
+
+
+def read_traffic(kernel_hash):
+    """HBM bytes per launch of the prefill kernel from the committed counter
+    summary, if it was taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_FILE):
+        if line.startswith("traffic_") and ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("traffic_kernel_sha256") != kernel_hash:
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def kernel_source_hash():
+    import hashlib
+    p = os.path.join(ROOT, "sliding_window_attention_swa_amd", "csrc", "swa_prefill_bf16.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()
+
+
+def cpu_baseline(pos_np, q_dec, kr, vr, qkv_pre):
+    """fp64 oracle on the host cores over a bounded sample of one step:
+    8 of the 32 prefill query heads (all 16384 rows each) and 8 of the 64
+    decode sequences (all 32 heads).  Reported as in-window TFLOP/s."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        cores = len(os.sched_getaffinity(0))
+    c3, c4 = si.WORKLOADS[3], si.WORKLOADS[4]
+    q, k, v = qkv_pre
+    heads = [(0, h) for h in range(0, 32, 4)]
+    t0 = time.perf_counter()
+    oracle.attention_banded(q.values, k.values, v.values, c3["W"], c3["mode"],
+                            1 / math.sqrt(c3["d"]), heads=heads)
+    t1 = time.perf_counter()
+    nb = 8
+    oracle.decode(q_dec.values[:nb], kr.values[:nb], vr.values[:nb], pos_np[:nb],
+                  1 / math.sqrt(c4["d"]))
+    t2 = time.perf_counter()
+    pre_flops = 4 * c3["d"] * band_pairs_causal(c3["T"], c3["W"]) * len(heads)
+    dec_rows = int(np.minimum(pos_np[:nb].astype(np.int64) + 1, c4["W"]).sum())
+    dec_flops = 4 * c4["d"] * dec_rows * c4["Hq"]
+    secs = t2 - t0
+    return {
+        "value": (pre_flops + dec_flops) / secs / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": "fp64 numpy oracle: prefill rows of 8 of 32 query heads (T=16384, W=4096, "
+                  "d=128; %.1f s) + decode of 8 of 64 sequences (32 heads, W=4096; %.1f s)"
+                  % (t1 - t0, t2 - t1),
+        "seconds": secs,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the sliding-window attention path here is a "
+              "single-device library (heads and sequences shard without communication); "
+              "run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import sliding_window_attention_swa_amd as swa
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    swa.load()
+    c3, c4 = si.WORKLOADS[3], si.WORKLOADS[4]
+
+    # ---- inputs, resident in HBM before timing
+    qkv_pre = si.prefill_inputs(3)
+    q_pre, k_pre, v_pre = (si.to_torch(t, dev) for t in qkv_pre)
+    out_pre = torch.empty_like(q_pre)
+    q_dec_np, kr_np, vr_np, pos_np = si.decode_inputs(4)
+    q_dec = si.to_torch(q_dec_np, dev)
+    k_ring = si.to_torch(kr_np, dev)
+    v_ring = si.to_torch(vr_np, dev)
+    pos = torch.from_numpy(pos_np).to(dev)
+    new_k = si.to_torch(si.normal(si.seed_for(4, 4), (c4["B"], c4["Hkv"], c4["d"]), si.BF16), dev)
+    new_v = si.to_torch(si.normal(si.seed_for(4, 5), (c4["B"], c4["Hkv"], c4["d"]), si.BF16), dev)
+    out_dec = torch.empty_like(q_dec)
+    ws = torch.empty(swa.decode_workspace_bytes(c4["B"], c4["Hq"], c4["W"], c4["d"]),
+                     dtype=torch.uint8, device=dev)
+    s_pre = 1.0 / math.sqrt(c3["d"])
+    s_dec = 1.0 / math.sqrt(c4["d"])
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        swa.prefill(q_pre, k_pre, v_pre, c3["W"], mode=c3["mode"], scale=s_pre, out=out_pre)
+        if ev is not None:
+            ev[1].record()
+        swa.cache_append(k_ring, v_ring, pos, new_k, new_v)
+        if ev is not None:
+            ev[2].record()
+        swa.decode(q_dec, k_ring, v_ring, pos, scale=s_dec, out=out_dec, workspace=ws)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(events[i])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_step = start.elapsed_time(stop) / args.steps
+    ms_pre = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    ms_app = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    ms_dec = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+
+    pre_flops, pre_bytes = prefill_work()
+    dec_flops, dec_kv_bytes, dec_qo_bytes = decode_work(pos_np)
+    step_flops = pre_flops + dec_flops
+    value = step_flops / (ms_step * 1e-3) / 1e12
+    pre_tflops = pre_flops / (ms_pre * 1e-3) / 1e12
+    dec_gbs = dec_kv_bytes / (ms_dec * 1e-3) / 1e9
+
+    traffic = read_traffic(kernel_source_hash())
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) rounded to bf16, resident in HBM",
+        "config": {
+            "workload": "Mistral-7B-shaped SWA step: causal prefill B=1 T=16384 W=4096 "
+                        "Hq/Hkv=32/8 d=128 + ring append + split-K ring decode B=64 "
+                        "W=4096 Hq/Hkv=32/8 d=128 pos~U[4096,32768)",
+            "prefill": {"B": c3["B"], "T": c3["T"], "W": c3["W"], "Hq": c3["Hq"],
+                        "Hkv": c3["Hkv"], "d": c3["d"], "mode": "causal"},
+            "decode": {"B": c4["B"], "W": c4["W"], "Hq": c4["Hq"], "Hkv": c4["Hkv"],
+                       "d": c4["d"], "pos": [int(c4["pos_lo"]), int(c4["pos_hi"])]},
+        },
+        "parts": {
+            "prefill": {"ms": round(ms_pre, 4), "in_window_tflops": round(pre_tflops, 2),
+                        "frac_bf16_peak": round(pre_tflops / PEAK_BF16_TFLOPS, 4)},
+            "append": {"ms": round(ms_app, 4)},
+            "decode": {"ms": round(ms_dec, 4), "kv_read_gbs": round(dec_gbs, 1),
+                       "frac_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4),
+                       "kv_bytes": dec_kv_bytes},
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(pre_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": "prefill_bf16_kernel<128, causal>",
+            "algorithmic_flops_per_launch": pre_flops,
+            "algorithmic_bytes_per_launch": pre_bytes,
+        },
+        "decode_roofline": {
+            "bound": "hbm",
+            "achieved": round(dec_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes_per_launch": dec_kv_bytes + dec_qo_bytes,
+        },
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(pos_np, q_dec_np, kr_np, vr_np, qkv_pre)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,147 @@
+/*
+ * swa.h - C ABI of the gfx950 (MI355X) sliding-window attention library.
+ *
+ * Sliding-window attention (SWA): query i attends only to the keys inside a
+ * fixed window around it, with the softmax taken over the in-window logits
+ * (every out-of-window logit counts as -inf).  Sources:
+ *   - robocikowo.com glossary "Sliding Window Attention", opening definition:
+ *     causal window [i-W+1, i], symmetric window [i-W/2, i+W/2], masked logits
+ *     set to -inf before the softmax;
+ *   - Ultralytics glossary "Sliding Window Attention", section "Come cresce la
+ *     finestra con la profondita": the causal mask 0 <= i-j < w, and the
+ *     w-slot circular KV buffer that stores position i in slot i mod w;
+ *   - aivaro.ru answer 629, section 4.1: the Longformer window takes W/2
+ *     neighbours on each side;
+ *   - "Sliding-window and hybrid attention", section "Walking through it":
+ *     windowed decode reads only the window's KV for each new token.
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are dense, contiguous and head-major:
+ *       q, out        [B, Hq,  T, d]   (prefill)      [B, Hq, d]   (decode)
+ *       k, v          [B, Hkv, T, d]
+ *       k_ring, v_ring[B, Hkv, W, d]
+ *       k_new, v_new  [B, Hkv, d]
+ *       pos           [B] int32
+ *     Element type is selected by `dtype` (swa_dtype): IEEE fp32 or bfloat16.
+ *   - Query head h reads KV head h / (Hq / Hkv) (contiguous GQA groups); Hq
+ *     must be a multiple of Hkv.
+ *   - Every pointer is a device pointer the caller owns.  The library never
+ *     allocates or frees memory and keeps no state between calls.  Every
+ *     device pointer must be 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously; calls are thread-safe.
+ *   - Arguments are validated on the host before anything is enqueued.  An
+ *     invalid call returns a negative swa_status and launches nothing; a
+ *     failed launch returns SWA_ERR_LAUNCH.  Device-side contents (e.g. pos)
+ *     are not validated on the host; the behaviour for out-of-range positions
+ *     is stated per entry point and never touches memory outside the buffers.
+ *   - Accumulation and softmax run in fp32; bf16 outputs are rounded to
+ *     nearest-even.
+ */
+#ifndef SWA_H
+#define SWA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SWA_OK = 0,
+  SWA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, Hq % Hkv != 0,
+                               non-finite scale, misaligned pointer */
+  SWA_ERR_UNSUPPORTED = -2, /* d not in {32, 64, 128}, unknown mode or dtype,
+                               launch grid beyond the int32 range */
+  SWA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  SWA_ERR_LAUNCH = -4       /* the HIP runtime rejected a kernel launch */
+} swa_status;
+
+typedef enum {
+  SWA_CAUSAL = 0,   /* keys j with 0 <= i - j <= W - 1                        */
+  SWA_SYMMETRIC = 1 /* keys j with |i - j| <= floor(W / 2); W + 1 keys inside
+                       the sequence when W is even                           */
+} swa_mode;
+
+typedef enum { SWA_F32 = 0, SWA_BF16 = 1 } swa_dtype;
+
+/*
+ * swa_prefill - windowed attention over a whole sequence (every query row).
+ *
+ *   out[b,h,i,:] = sum_j softmax_j(scale * q[b,h,i,:].k[b,g,j,:]) v[b,g,j,:]
+ *   over the keys j in the window of i (mode), clipped to 0 <= j < T,
+ *   g = h / (Hq / Hkv).
+ *
+ * Causal window from the robocikowo definition and the Ultralytics mask
+ * snippet; symmetric window from the robocikowo definition and aivaro
+ * section 4.1.  Only key tiles that intersect the window are visited; the
+ * [T, T] score matrix is never formed.
+ *
+ * Batch is folded into the heads: for tensors [B, H, T, d] pass Hq = B*Hq_model
+ * and Hkv = B*Hkv_model (exact, because B*Hq_model/(B*Hkv_model) keeps the
+ * group size and b*Hq_model + h maps to b*Hkv_model + h/group).
+ *
+ *   q, k, v  input, layouts above, element type `dtype`.
+ *   out      output [Hq, T, d] (may not alias q, k or v).
+ *   T >= 1, W >= 1, Hq >= 1, Hkv >= 1, Hq % Hkv == 0, d in {32, 64, 128},
+ *   mode in swa_mode, scale finite, dtype in swa_dtype.
+ * Returns SWA_OK or a negative swa_status.
+ */
+int swa_prefill(const void* q, const void* k, const void* v, void* out, int T, int W, int Hq,
+                int Hkv, int d, int mode, float scale, int dtype, void* stream);
+
+/*
+ * swa_cache_append - write one new K/V row per sequence into the ring cache.
+ *
+ *   k_ring[b, :, pos[b] mod W, :] = k_new[b, :, :]   (and the same for v)
+ *
+ * Ultralytics ring-buffer paragraph (slot i mod w, the oldest entry is
+ * overwritten); robocikowo rolling KV buffer (FIFO over the last W tokens).
+ * A bit-exact copy.  A sequence with pos[b] < 0 is left untouched.
+ *
+ *   k_ring, v_ring  in/out [B, Hkv, W, d].
+ *   pos             device int32 [B], the position of the new token.
+ *   k_new, v_new    input [B, Hkv, d].
+ *   B, Hkv, W >= 1, d in {32, 64, 128}, dtype in swa_dtype.
+ */
+int swa_cache_append(void* k_ring, void* v_ring, const int32_t* pos, const void* k_new,
+                     const void* v_new, int B, int Hkv, int W, int d, int dtype, void* stream);
+
+/*
+ * swa_decode - one query token per sequence against its ring cache (causal).
+ *
+ * The query at position p = pos[b] sees positions [max(0, p-W+1), p], held in
+ * slots p' mod W, i.e. the slots [0, min(p+1, W)).  Call swa_cache_append for
+ * position p first, so that the query sees its own key.  Equals row p of
+ * swa_prefill (causal, same W) over the sequence that filled the ring.
+ * "Sliding-window and hybrid attention", section "Walking through it": each
+ * decoded token reads at most W cached rows rather than the whole history.
+ * A sequence with pos[b] < 0 gets an all-zero output row.
+ *
+ *   q          input [B, Hq, d].
+ *   k_ring, v_ring  input [B, Hkv, W, d].
+ *   pos        device int32 [B].
+ *   out        output [B, Hq, d].
+ *   workspace  device scratch of at least swa_decode_workspace_bytes(B, Hq, W, d)
+ *              bytes (partial results of the split-K passes); its contents
+ *              need no initialisation and are garbage afterwards.  Concurrent
+ *              calls must use distinct workspaces.
+ *   mode is implicitly causal: there is no symmetric decode (the symmetric
+ *   window needs keys that have not been generated yet).
+ */
+int swa_decode(const void* q, const void* k_ring, const void* v_ring, const int32_t* pos,
+               void* out, int B, int Hq, int Hkv, int W, int d, float scale, int dtype,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes swa_decode needs for these sizes (0 for invalid sizes). */
+size_t swa_decode_workspace_bytes(int B, int Hq, int W, int d);
+
+/* Static, human-readable text for a swa_status value. */
+const char* swa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWA_H */

@@ -1,0 +1,168 @@
+"""Python binding of libswa.so, the gfx950 sliding-window attention library.
+
+Argument marshalling only: every function checks shapes, dtypes and devices
+of torch tensors, then passes raw device pointers and the current HIP stream
+to the C ABI declared in include/swa.h.  All arithmetic runs in the HIP
+kernels; there is no fallback.  If the library has not been built, every call
+raises.
+
+Layouts (contiguous, head-major):
+  prefill  q, out [B, Hq, T, d]   k, v [B, Hkv, T, d]
+  ring     k_ring, v_ring [B, Hkv, W, d]   k_new, v_new [B, Hkv, d]   pos [B] int32
+  decode   q, out [B, Hq, d]
+"""
+
+import ctypes
+import math
+import os
+
+CAUSAL = 0
+SYMMETRIC = 1
+
+SWA_F32 = 0
+SWA_BF16 = 1
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswa.so")
+
+_lib = None
+
+
+class SwaError(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (fn, status_string(status), status))
+
+
+def load():
+    """Load libswa.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libswa.so not found at %s; build it with "
+                           "`python -m sliding_window_attention_swa_amd.build`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.swa_prefill.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    lib.swa_prefill.restype = i
+    lib.swa_cache_append.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+    lib.swa_cache_append.restype = i
+    lib.swa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.swa_decode.restype = i
+    lib.swa_decode_workspace_bytes.argtypes = [i, i, i, i]
+    lib.swa_decode_workspace_bytes.restype = sz
+    lib.swa_status_string.argtypes = [i]
+    lib.swa_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status):
+    return load().swa_status_string(int(status)).decode()
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return SWA_BF16
+    if t.dtype == torch.float32:
+        return SWA_F32
+    raise TypeError("unsupported dtype %s (bfloat16 or float32)" % t.dtype)
+
+
+def _check(t, name, ndim, dtype=None):
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if t.dim() != ndim:
+        raise ValueError("%s must have %d dims, got shape %s" % (name, ndim, tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _raise(fn, status):
+    if status != 0:
+        raise SwaError(fn, status)
+
+
+def prefill(q, k, v, W, mode=CAUSAL, scale=None, out=None, stream=None):
+    """Windowed attention over whole sequences; returns `out` [B, Hq, T, d]."""
+    import torch
+    _check(q, "q", 4)
+    _check(k, "k", 4, q.dtype)
+    _check(v, "v", 4, q.dtype)
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, T, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("shape mismatch q%s k%s v%s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", 4, q.dtype)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = load().swa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), T, int(W),
+                            B * Hq, B * Hkv, d, int(mode), float(scale), _dtype_code(q),
+                            _stream(stream))
+    _raise("swa_prefill", st)
+    return out
+
+
+def cache_append(k_ring, v_ring, pos, k_new, v_new, stream=None):
+    """Write k_new/v_new [B, Hkv, d] into slot pos[b] mod W of the rings."""
+    import torch
+    _check(k_ring, "k_ring", 4)
+    _check(v_ring, "v_ring", 4, k_ring.dtype)
+    _check(pos, "pos", 1, torch.int32)
+    _check(k_new, "k_new", 3, k_ring.dtype)
+    _check(v_new, "v_new", 3, k_ring.dtype)
+    B, Hkv, W, d = k_ring.shape
+    if tuple(v_ring.shape) != tuple(k_ring.shape) or tuple(k_new.shape) != (B, Hkv, d) \
+            or tuple(v_new.shape) != (B, Hkv, d) or pos.shape[0] != B:
+        raise ValueError("shape mismatch")
+    st = load().swa_cache_append(k_ring.data_ptr(), v_ring.data_ptr(), pos.data_ptr(),
+                                 k_new.data_ptr(), v_new.data_ptr(), B, Hkv, W, d,
+                                 _dtype_code(k_ring), _stream(stream))
+    _raise("swa_cache_append", st)
+
+
+def decode_workspace_bytes(B, Hq, W, d):
+    return int(load().swa_decode_workspace_bytes(int(B), int(Hq), int(W), int(d)))
+
+
+def decode(q, k_ring, v_ring, pos, scale=None, out=None, workspace=None, stream=None):
+    """One query token per sequence against its ring; returns out [B, Hq, d]."""
+    import torch
+    _check(q, "q", 3)
+    _check(k_ring, "k_ring", 4, q.dtype)
+    _check(v_ring, "v_ring", 4, q.dtype)
+    _check(pos, "pos", 1, torch.int32)
+    B, Hq, d = q.shape
+    Hkv, W = k_ring.shape[1], k_ring.shape[2]
+    if tuple(k_ring.shape) != (B, Hkv, W, d) or tuple(v_ring.shape) != tuple(k_ring.shape) \
+            or pos.shape[0] != B:
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", 3, q.dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = decode_workspace_bytes(B, Hq, W, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = load().swa_decode(q.data_ptr(), k_ring.data_ptr(), v_ring.data_ptr(), pos.data_ptr(),
+                           out.data_ptr(), B, Hq, Hkv, W, d, float(scale), _dtype_code(q),
+                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                           _stream(stream))
+    _raise("swa_decode", st)
+    return out

@@ -1,0 +1,106 @@
+// C ABI of the SWA library: host-side argument checks, then dispatch to the
+// gfx950 kernels.  The checks run before any HIP call, so an invalid call
+// never touches the device (and can be exercised on a machine without one).
+
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/swa.h"
+#include "swa_launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_d(int d) { return d == 32 || d == 64 || d == 128; }
+
+bool known_dtype(int dtype) { return dtype == SWA_F32 || dtype == SWA_BF16; }
+
+int elem_bytes(int dtype) { return dtype == SWA_BF16 ? 2 : 4; }
+
+constexpr long long kMaxGrid = 2147483647LL;
+
+}  // namespace
+
+extern "C" {
+
+int swa_prefill(const void* q, const void* k, const void* v, void* out, int T, int W, int Hq,
+                int Hkv, int d, int mode, float scale, int dtype, void* stream) {
+  if (!q || !k || !v || !out) return SWA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SWA_ERR_INVALID_ARG;
+  if (T <= 0 || W <= 0 || Hq <= 0 || Hkv <= 0) return SWA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return SWA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return SWA_ERR_INVALID_ARG;
+  if (!supported_d(d) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
+  if (mode != SWA_CAUSAL && mode != SWA_SYMMETRIC) return SWA_ERR_UNSUPPORTED;
+  // workgroup count (16-row blocks for fp32 is the larger) must fit the grid
+  if ((long long)((T + 15) / 16) * Hq > kMaxGrid) return SWA_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = (dtype == SWA_BF16)
+                     ? swa::launch_prefill_bf16(q, k, v, out, T, W, Hq, Hkv, d, mode, scale, s)
+                     : swa::launch_prefill_f32(q, k, v, out, T, W, Hq, Hkv, d, mode, scale, s);
+  return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH;
+}
+
+int swa_cache_append(void* k_ring, void* v_ring, const int32_t* pos, const void* k_new,
+                     const void* v_new, int B, int Hkv, int W, int d, int dtype, void* stream) {
+  if (!k_ring || !v_ring || !pos || !k_new || !v_new) return SWA_ERR_INVALID_ARG;
+  if (!aligned16(k_ring) || !aligned16(v_ring) || !aligned16(pos) || !aligned16(k_new) ||
+      !aligned16(v_new))
+    return SWA_ERR_INVALID_ARG;
+  if (B <= 0 || Hkv <= 0 || W <= 0) return SWA_ERR_INVALID_ARG;
+  if (!supported_d(d) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
+  const long long row_bytes = (long long)d * elem_bytes(dtype);
+  if ((long long)B * Hkv * (row_bytes / 16) / 256 + 1 > kMaxGrid) return SWA_ERR_UNSUPPORTED;
+  hipError_t e = swa::launch_append(k_ring, v_ring, pos, k_new, v_new, B, Hkv, W, (int)row_bytes,
+                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH;
+}
+
+size_t swa_decode_workspace_bytes(int B, int Hq, int W, int d) {
+  if (B <= 0 || Hq <= 0 || W <= 0 || !supported_d(d)) return 0;
+  const int S = swa::decode_splits(B, Hq, W);
+  return (size_t)B * Hq * S * (size_t)(d + 2) * sizeof(float);
+}
+
+int swa_decode(const void* q, const void* k_ring, const void* v_ring, const int32_t* pos,
+               void* out, int B, int Hq, int Hkv, int W, int d, float scale, int dtype,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_ring || !v_ring || !pos || !out) return SWA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_ring) || !aligned16(v_ring) || !aligned16(pos) ||
+      !aligned16(out))
+    return SWA_ERR_INVALID_ARG;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || W <= 0) return SWA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return SWA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return SWA_ERR_INVALID_ARG;
+  if (!supported_d(d) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
+  const size_t need = swa_decode_workspace_bytes(B, Hq, W, d);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return SWA_ERR_WORKSPACE;
+  const int S = swa::decode_splits(B, Hq, W);
+  if ((long long)B * Hq * S > kMaxGrid) return SWA_ERR_UNSUPPORTED;
+  hipError_t e = swa::launch_decode(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, d, scale, dtype,
+                                    static_cast<float*>(workspace),
+                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH;
+}
+
+const char* swa_status_string(int status) {
+  switch (status) {
+    case SWA_OK:
+      return "ok";
+    case SWA_ERR_INVALID_ARG:
+      return "invalid argument";
+    case SWA_ERR_UNSUPPORTED:
+      return "unsupported configuration";
+    case SWA_ERR_WORKSPACE:
+      return "workspace missing or too small";
+    case SWA_ERR_LAUNCH:
+      return "kernel launch failed";
+    default:
+      return "unknown status";
+  }
+}
+
+}  // extern "C"

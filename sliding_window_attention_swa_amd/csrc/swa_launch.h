@@ -1,0 +1,31 @@
+// Internal launchers behind the C ABI (not exported).  Each one enqueues its
+// kernels on `stream` and returns the launch status; arguments have already
+// been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace swa {
+
+hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* out, int T,
+                               int W, int Hq, int Hkv, int d, int mode, float scale,
+                               hipStream_t stream);
+
+hipError_t launch_prefill_f32(const void* q, const void* k, const void* v, void* out, int T,
+                              int W, int Hq, int Hkv, int d, int mode, float scale,
+                              hipStream_t stream);
+
+hipError_t launch_append(void* k_ring, void* v_ring, const int32_t* pos, const void* k_new,
+                         const void* v_new, int B, int Hkv, int W, int row_bytes,
+                         hipStream_t stream);
+
+// Number of slot chunks ("splits") the decode pass divides each ring into.
+int decode_splits(int B, int Hq, int W);
+
+hipError_t launch_decode(const void* q, const void* k_ring, const void* v_ring,
+                         const int32_t* pos, void* out, int B, int Hq, int Hkv, int W, int d,
+                         float scale, int dtype, float* workspace, hipStream_t stream);
+
+}  // namespace swa

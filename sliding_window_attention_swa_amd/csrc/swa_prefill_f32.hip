@@ -1,0 +1,103 @@
+// Sliding-window attention prefill in IEEE fp32 (vector ALU, full-precision
+// products: the fp32 workloads are held to an absolute error of 1e-5).
+//
+// Same definition as the bf16 kernel (robocikowo glossary "Sliding Window
+// Attention", opening definition; Ultralytics glossary, section "Come cresce
+// la finestra con la profondita"): each query row takes the softmax of its
+// in-window logits only.  16 lanes share one query row, each holding d/16
+// dims; a row walks exactly the keys of its own window, one key at a time,
+// with a running maximum and sum.
+
+#include "swa_device.h"
+#include "swa_launch.h"
+
+namespace swa {
+namespace {
+
+constexpr int kRowsPerBlock = 16;
+constexpr int kLanesPerRow = 16;
+
+template <int D, int MODE>
+__global__ __launch_bounds__(256) void prefill_f32_kernel(const float* __restrict__ q,
+                                                          const float* __restrict__ k,
+                                                          const float* __restrict__ v,
+                                                          float* __restrict__ out, int T,
+                                                          int W, int Hq, int Hkv, float scale,
+                                                          int n_rowblocks) {
+  constexpr int DPL = D / kLanesPerRow;
+  const int h = blockIdx.x / n_rowblocks;
+  const int i = (blockIdx.x % n_rowblocks) * kRowsPerBlock + threadIdx.x / kLanesPerRow;
+  const int c = threadIdx.x % kLanesPerRow;
+  if (i >= T) return;  // whole 16-lane groups leave together
+  const int kvh = h / (Hq / Hkv);
+  const float* qrow = q + ((size_t)h * T + i) * D + c * DPL;
+  const float* kh = k + (size_t)kvh * T * D + c * DPL;
+  const float* vh = v + (size_t)kvh * T * D + c * DPL;
+
+  float qv[DPL], acc[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) {
+    qv[e] = qrow[e];
+    acc[e] = 0.f;
+  }
+  int lo, hi;
+  if (MODE == 0) {
+    lo = max(0, i - W + 1);
+    hi = i;
+  } else {
+    lo = max(0, i - W / 2);
+    hi = min(T - 1, i + W / 2);
+  }
+  float m = -INFINITY, l = 0.f;
+  for (int j = lo; j <= hi; ++j) {
+    const float* kr = kh + (size_t)j * D;
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) s = fmaf(qv[e], kr[e], s);
+#pragma unroll
+    for (int off = kLanesPerRow / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, kLanesPerRow);
+    s *= scale;
+    const float m_new = fmaxf(m, s);
+    const float alpha = expf(m - m_new);  // m = -inf on the first key: 0
+    const float p = expf(s - m_new);
+    l = l * alpha + p;
+    const float* vr = vh + (size_t)j * D;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[e] = fmaf(p, vr[e], acc[e] * alpha);
+    m = m_new;
+  }
+  float* orow = out + ((size_t)h * T + i) * D + c * DPL;
+  const float inv = 1.0f / l;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) orow[e] = acc[e] * inv;
+}
+
+template <int D, int MODE>
+hipError_t launch(const void* q, const void* k, const void* v, void* out, int T, int W, int Hq,
+                  int Hkv, float scale, hipStream_t stream) {
+  const int n_rowblocks = (T + kRowsPerBlock - 1) / kRowsPerBlock;
+  const long long nwg = (long long)n_rowblocks * Hq;
+  hipLaunchKernelGGL((prefill_f32_kernel<D, MODE>), dim3((unsigned)nwg),
+                     dim3(kRowsPerBlock * kLanesPerRow), 0,
+                     stream, static_cast<const float*>(q), static_cast<const float*>(k),
+                     static_cast<const float*>(v), static_cast<float*>(out), T, W, Hq, Hkv,
+                     scale, n_rowblocks);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_f32(const void* q, const void* k, const void* v, void* out, int T,
+                              int W, int Hq, int Hkv, int d, int mode, float scale,
+                              hipStream_t stream) {
+  if (mode == 0) {
+    if (d == 32) return launch<32, 0>(q, k, v, out, T, W, Hq, Hkv, scale, stream);
+    if (d == 64) return launch<64, 0>(q, k, v, out, T, W, Hq, Hkv, scale, stream);
+    return launch<128, 0>(q, k, v, out, T, W, Hq, Hkv, scale, stream);
+  }
+  if (d == 32) return launch<32, 1>(q, k, v, out, T, W, Hq, Hkv, scale, stream);
+  if (d == 64) return launch<64, 1>(q, k, v, out, T, W, Hq, Hkv, scale, stream);
+  return launch<128, 1>(q, k, v, out, T, W, Hq, Hkv, scale, stream);
+}
+
+}  // namespace swa

@@ -1,0 +1,354 @@
+// Ring-buffer KV cache (append) and split-K windowed decode on gfx950.
+//
+// Ring (Ultralytics glossary "Sliding Window Attention", ring-buffer paragraph
+// of "Come cresce la finestra con la profondita"; robocikowo glossary, rolling
+// KV buffer entry): each sequence keeps W slots per KV head, position i is
+// stored in slot i mod W and overwrites the oldest entry, so the cache never
+// grows past W rows ("Sliding-window and hybrid attention", "Check yourself").
+//
+// Decode ("Sliding-window and hybrid attention", "Walking through it"): the
+// query at position p reads only the window [max(0, p-W+1), p], i.e. the valid
+// slots [0, min(p+1, W)); softmax does not depend on the order of the keys,
+// so the slots are read in storage order.  The read of the ring dominates, so
+// the kernel is organised for HBM bandwidth:
+//   * grid = (sequence, KV head, query-head chunk, slot split); every K/V row
+//     of a KV head is read once for all the query heads of its group;
+//   * each row is read with 16-byte loads by d/8 (bf16) consecutive lanes, so
+//     a wave load covers whole rows and is fully coalesced; four loads of K
+//     and four of V are in flight per lane;
+//   * the dot product is finished with DPP row permutations (no LDS);
+//   * every lane-row group keeps its own running maximum / sum (rescaled only
+//     when the maximum grows by more than 2^8), merged once per workgroup
+//     through LDS; a small second kernel merges the splits with the usual
+//     log-sum-exp rule and writes the output.
+
+#include "swa_device.h"
+#include "swa_launch.h"
+
+namespace swa {
+namespace {
+
+constexpr float kRescaleThreshold = 8.0f;
+constexpr float kNegBig = -1.0e30f;
+constexpr int kDecodeThreads = 256;
+constexpr int kDecodeWaves = kDecodeThreads / 64;
+constexpr int kUnroll = 4;
+
+// ------------------------------------------------------------------ append
+
+__global__ __launch_bounds__(256) void append_kernel(uint4* __restrict__ k_ring,
+                                                     uint4* __restrict__ v_ring,
+                                                     const int32_t* __restrict__ pos,
+                                                     const uint4* __restrict__ k_new,
+                                                     const uint4* __restrict__ v_new, int Hkv,
+                                                     int W, int cpr, long long total) {
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const long long bh = idx / cpr;
+  const int c = (int)(idx % cpr);
+  const int b = (int)(bh / Hkv);
+  const int p = pos[b];
+  if (p < 0) return;
+  const long long dst = (bh * W + (p % W)) * cpr + c;
+  k_ring[dst] = k_new[idx];
+  v_ring[dst] = v_new[idx];
+}
+
+// --------------------------------------------------------------- helpers
+
+template <typename E>
+struct Elem;
+template <>
+struct Elem<__bf16> {
+  static constexpr int PER16 = 8;
+  __device__ static void widen(const uint4& raw, float* f) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = bf16lo(w[e]);
+      f[2 * e + 1] = bf16hi(w[e]);
+    }
+  }
+  __device__ static void store(__bf16* dst, float x) { *dst = (__bf16)x; }
+};
+template <>
+struct Elem<float> {
+  static constexpr int PER16 = 4;
+  __device__ static void widen(const uint4& raw, float* f) {
+    f[0] = __uint_as_float(raw.x);
+    f[1] = __uint_as_float(raw.y);
+    f[2] = __uint_as_float(raw.z);
+    f[3] = __uint_as_float(raw.w);
+  }
+  __device__ static void store(float* dst, float x) { *dst = x; }
+};
+
+// Sum over aligned groups of N lanes (N in {4, 8, 16, 32}); every lane of the
+// group receives the total.  DPP quad permutations and row mirrors stay on
+// the vector ALU.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));  // xor 1
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));  // xor 2
+  if (N >= 8)
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));  // mirror in 8
+  if (N >= 16)
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));  // mirror in 16
+  if (N >= 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
+// ------------------------------------------------------------ split pass
+
+template <typename E, int D, int NQ>
+__global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
+    const E* __restrict__ q, const E* __restrict__ k_ring, const E* __restrict__ v_ring,
+    const int32_t* __restrict__ pos, float* __restrict__ ws_acc, float* __restrict__ ws_m,
+    float* __restrict__ ws_l, int Hq, int Hkv, int W, float scale_log2, int S, int chunk,
+    int n_hchunks) {
+  constexpr int EPL = Elem<E>::PER16;  // elements per 16-byte load
+  constexpr int LPR = D / EPL;         // lanes per ring row
+  constexpr int RPW = 64 / LPR;        // rows per wave load
+  constexpr int NSTATE = kDecodeWaves * RPW;
+  constexpr int STEP = kDecodeWaves * RPW * kUnroll;  // rows per workgroup step
+
+  __shared__ float sm_acc[NQ][NSTATE][D];
+  __shared__ float sm_m[NQ][NSTATE];
+  __shared__ float sm_l[NQ][NSTATE];
+
+  int id = blockIdx.x;
+  const int split = id % S;
+  id /= S;
+  const int hc = id % n_hchunks;
+  id /= n_hchunks;
+  const int kvh = id % Hkv;
+  const int b = id / Hkv;
+  const int G = Hq / Hkv;
+  const int h0 = kvh * G + hc * NQ;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int rg = lane / LPR;
+  const int li = lane % LPR;
+
+  const int p = pos[b];
+  const int nvalid = p < 0 ? 0 : (p >= W ? W : p + 1);
+  const int s0 = split * chunk;
+  const int s1 = min(s0 + chunk, nvalid);
+
+  float qv[NQ][EPL];
+#pragma unroll
+  for (int hq = 0; hq < NQ; ++hq) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + h0 + hq) * D + li * EPL);
+    Elem<E>::widen(raw, qv[hq]);
+  }
+  float m[NQ], l[NQ], acc[NQ][EPL];
+#pragma unroll
+  for (int hq = 0; hq < NQ; ++hq) {
+    m[hq] = kNegBig;
+    l[hq] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[hq][e] = 0.f;
+  }
+
+  const size_t ring_off = ((size_t)b * Hkv + kvh) * (size_t)W * D + li * EPL;
+  const E* kb = k_ring + ring_off;
+  const E* vb = v_ring + ring_off;
+
+  for (int base = s0; base < s1; base += STEP) {
+    uint4 kraw[kUnroll], vraw[kUnroll];
+    bool valid[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int r = base + (u * kDecodeWaves + wave) * RPW + rg;
+      valid[u] = r < s1;
+      if (valid[u]) {
+        kraw[u] = *reinterpret_cast<const uint4*>(kb + (size_t)r * D);
+        vraw[u] = *reinterpret_cast<const uint4*>(vb + (size_t)r * D);
+      } else {
+        kraw[u] = make_uint4(0, 0, 0, 0);
+        vraw[u] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    float sc[kUnroll][NQ];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      float kf[EPL];
+      Elem<E>::widen(kraw[u], kf);
+#pragma unroll
+      for (int hq = 0; hq < NQ; ++hq) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) s = fmaf(qv[hq][e], kf[e], s);
+        sc[u][hq] = s;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+      for (int hq = 0; hq < NQ; ++hq) {
+        const float s = group_sum<LPR>(sc[u][hq]) * scale_log2;
+        sc[u][hq] = valid[u] ? s : -INFINITY;
+      }
+    }
+    float vf[kUnroll][EPL];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) Elem<E>::widen(vraw[u], vf[u]);
+#pragma unroll
+    for (int hq = 0; hq < NQ; ++hq) {
+      float mx = sc[0][hq];
+#pragma unroll
+      for (int u = 1; u < kUnroll; ++u) mx = fmaxf(mx, sc[u][hq]);
+      if (mx > m[hq] + kRescaleThreshold) {
+        const float alpha = __builtin_amdgcn_exp2f(m[hq] - mx);
+        m[hq] = mx;
+        l[hq] *= alpha;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[hq][e] *= alpha;
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const float pr = __builtin_amdgcn_exp2f(sc[u][hq] - m[hq]);
+        l[hq] += pr;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[hq][e] = fmaf(pr, vf[u][e], acc[hq][e]);
+      }
+    }
+  }
+
+  // ---- merge the NSTATE lane-row states of this workgroup
+  const int st = wave * RPW + rg;
+#pragma unroll
+  for (int hq = 0; hq < NQ; ++hq) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) sm_acc[hq][st][li * EPL + e] = acc[hq][e];
+    if (li == 0) {
+      sm_m[hq][st] = m[hq];
+      sm_l[hq][st] = l[hq];
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < NQ * D; idx += kDecodeThreads) {
+    const int hq = idx / D;
+    const int dim = idx % D;
+    float M = sm_m[hq][0];
+#pragma unroll
+    for (int s = 1; s < NSTATE; ++s) M = fmaxf(M, sm_m[hq][s]);
+    float a = 0.f, L = 0.f;
+#pragma unroll
+    for (int s = 0; s < NSTATE; ++s) {
+      const float w = __builtin_amdgcn_exp2f(sm_m[hq][s] - M);
+      a = fmaf(w, sm_acc[hq][s][dim], a);
+      L = fmaf(w, sm_l[hq][s], L);
+    }
+    const size_t slot = ((size_t)b * Hq + h0 + hq) * S + split;
+    ws_acc[slot * D + dim] = a;
+    if (dim == 0) {
+      ws_m[slot] = M;
+      ws_l[slot] = L;
+    }
+  }
+}
+
+// ------------------------------------------------------------ split merge
+
+template <typename E, int D>
+__global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restrict__ ws_acc,
+                                                           const float* __restrict__ ws_m,
+                                                           const float* __restrict__ ws_l,
+                                                           E* __restrict__ out, int S) {
+  const size_t row = blockIdx.x;  // b * Hq + h
+  const int dim = threadIdx.x;
+  const float* m = ws_m + row * S;
+  const float* l = ws_l + row * S;
+  float M = m[0];
+  for (int s = 1; s < S; ++s) M = fmaxf(M, m[s]);
+  float a = 0.f, L = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float w = __builtin_amdgcn_exp2f(m[s] - M);
+    L = fmaf(w, l[s], L);
+    a = fmaf(w, ws_acc[(row * S + s) * D + dim], a);
+  }
+  Elem<E>::store(out + row * D + dim, L > 0.f ? a / L : 0.f);
+}
+
+template <typename E, int D, int NQ>
+hipError_t launch_decode_t(const void* q, const void* k_ring, const void* v_ring,
+                           const int32_t* pos, void* out, int B, int Hq, int Hkv, int W,
+                           float scale, float* workspace, hipStream_t stream) {
+  const int S = decode_splits(B, Hq, W);
+  const int chunk = (W + S - 1) / S;
+  const int G = Hq / Hkv;
+  const int n_hchunks = G / NQ;
+  const size_t rows = (size_t)B * Hq * S;
+  float* ws_acc = workspace;
+  float* ws_m = ws_acc + rows * D;
+  float* ws_l = ws_m + rows;
+  const long long nwg = (long long)B * Hkv * n_hchunks * S;
+  hipLaunchKernelGGL((decode_split_kernel<E, D, NQ>), dim3((unsigned)nwg), dim3(kDecodeThreads), 0,
+                     stream, static_cast<const E*>(q), static_cast<const E*>(k_ring),
+                     static_cast<const E*>(v_ring), pos, ws_acc, ws_m, ws_l, Hq, Hkv, W,
+                     scale * kLog2e, S, chunk, n_hchunks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<E, D>), dim3((unsigned)((size_t)B * Hq)), dim3(D), 0,
+                     stream, ws_acc, ws_m, ws_l, static_cast<E*>(out), S);
+  return hipGetLastError();
+}
+
+template <typename E, int D>
+hipError_t launch_decode_d(const void* q, const void* k_ring, const void* v_ring,
+                           const int32_t* pos, void* out, int B, int Hq, int Hkv, int W,
+                           float scale, float* workspace, hipStream_t stream) {
+  const int G = Hq / Hkv;
+  if (G % 4 == 0)
+    return launch_decode_t<E, D, 4>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
+  if (G % 2 == 0)
+    return launch_decode_t<E, D, 2>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
+  return launch_decode_t<E, D, 1>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
+}
+
+template <typename E>
+hipError_t launch_decode_e(const void* q, const void* k_ring, const void* v_ring,
+                           const int32_t* pos, void* out, int B, int Hq, int Hkv, int W, int d,
+                           float scale, float* workspace, hipStream_t stream) {
+  if (d == 32) return launch_decode_d<E, 32>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
+  if (d == 64) return launch_decode_d<E, 64>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
+  return launch_decode_d<E, 128>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
+}
+
+}  // namespace
+
+hipError_t launch_append(void* k_ring, void* v_ring, const int32_t* pos, const void* k_new,
+                         const void* v_new, int B, int Hkv, int W, int row_bytes,
+                         hipStream_t stream) {
+  const int cpr = row_bytes / 16;
+  const long long total = (long long)B * Hkv * cpr;
+  const long long blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<uint4*>(k_ring), static_cast<uint4*>(v_ring), pos,
+                     static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new), Hkv, W,
+                     cpr, total);
+  return hipGetLastError();
+}
+
+int decode_splits(int B, int Hq, int W) {
+  // Aim for ~16K (sequence, query head, split) items so the split pass fills
+  // the 256 CUs several times over, but never split below 64 slots.
+  const long long heads = (long long)B * Hq;
+  long long want = (16384 + heads - 1) / heads;
+  if (want < 1) want = 1;
+  const long long cap = (W + 63) / 64;
+  return (int)(want < cap ? want : cap);
+}
+
+hipError_t launch_decode(const void* q, const void* k_ring, const void* v_ring,
+                         const int32_t* pos, void* out, int B, int Hq, int Hkv, int W, int d,
+                         float scale, int dtype, float* workspace, hipStream_t stream) {
+  if (dtype == 1)
+    return launch_decode_e<__bf16>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, d, scale, workspace, stream);
+  return launch_decode_e<float>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, d, scale, workspace, stream);
+}
+
+}  // namespace swa

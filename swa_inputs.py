@@ -49,9 +49,12 @@ def bf16_bits(x):
     Returns the uint16 bit patterns.  Inputs are finite normal draws, so no
     NaN/Inf handling is needed (and none is attempted).
     """
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return rounded.astype(np.uint16)
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> 16) & 1
+    lsb += 0x7FFF
+    lsb += u  # no wrap-around: finite values stay below 0xFF800000 + 0x8000
+    lsb >>= 16
+    return lsb.astype(np.uint16)
 
 
 def bf16_to_f32(bits):
@@ -127,3 +130,13 @@ def decode_inputs(workload=4, B=None, Hq=None, Hkv=None, W=None, d=None, dtype=N
     v_ring = normal(seed_for(workload, ROLE_V), (B, Hkv, W, d), dtype)
     pos = positions(seed_for(workload, ROLE_POS), B, lo, hi)
     return q, k_ring, v_ring, pos
+
+
+def to_torch(t, device="cuda"):
+    """Tensor -> torch tensor on `device` holding exactly the same bits."""
+    import torch
+    if t.dtype == BF16:
+        host = torch.from_numpy(np.ascontiguousarray(t.bits).view(np.int16)).view(torch.bfloat16)
+    else:
+        host = torch.from_numpy(np.ascontiguousarray(t.bits, dtype=np.float32))
+    return host.to(device)

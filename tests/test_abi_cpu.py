@@ -1,0 +1,128 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol,
+and rejects invalid arguments with the documented status before touching the
+device.  No valid call is ever made here (there is no GPU): every call below
+fails validation, so the fake pointer values are never dereferenced."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import sliding_window_attention_swa_amd as swa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swa.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+P = 0x10000  # aligned, never dereferenced
+MIS = P + 8  # misaligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(swa.LIB_PATH):
+        from sliding_window_attention_swa_amd import build
+        build.build(verbose=False)
+    return swa.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(swa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted([
+        "swa_prefill", "swa_cache_append", "swa_decode", "swa_decode_workspace_bytes",
+        "swa_status_string"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def prefill(lib, q=P, k=P, v=P, out=P, T=16, W=4, Hq=4, Hkv=2, d=64, mode=0, scale=0.125,
+            dtype=1):
+    return lib.swa_prefill(q, k, v, out, T, W, Hq, Hkv, d, mode, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID),
+    (dict(out=None), INVALID), (dict(q=MIS), INVALID), (dict(out=MIS), INVALID),
+    (dict(T=0), INVALID), (dict(T=-3), INVALID), (dict(W=0), INVALID), (dict(Hq=0), INVALID),
+    (dict(Hkv=0), INVALID), (dict(Hq=6, Hkv=4), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(d=48), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(mode=2), UNSUPPORTED),
+    (dict(dtype=2), UNSUPPORTED), (dict(dtype=-1), UNSUPPORTED),
+    (dict(T=2**30, Hq=2**10, Hkv=1), UNSUPPORTED),
+])
+def test_prefill_rejects(lib, kw, status):
+    assert prefill(lib, **kw) == status
+
+
+def append(lib, kr=P, vr=P, pos=P, kn=P, vn=P, B=2, Hkv=2, W=8, d=64, dtype=1):
+    return lib.swa_cache_append(kr, vr, pos, kn, vn, B, Hkv, W, d, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kr=None), INVALID), (dict(vr=None), INVALID), (dict(pos=None), INVALID),
+    (dict(kn=None), INVALID), (dict(vn=None), INVALID), (dict(kr=MIS), INVALID),
+    (dict(pos=MIS), INVALID), (dict(B=0), INVALID), (dict(Hkv=0), INVALID), (dict(W=0), INVALID),
+    (dict(d=16), UNSUPPORTED), (dict(dtype=5), UNSUPPORTED),
+])
+def test_append_rejects(lib, kw, status):
+    assert append(lib, **kw) == status
+
+
+def decode(lib, q=P, kr=P, vr=P, pos=P, out=P, B=2, Hq=8, Hkv=2, W=64, d=64, scale=0.125,
+           dtype=1, ws=P, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.swa_decode_workspace_bytes(B, Hq, W, d) if B > 0 and Hq > 0 and W > 0 else 0
+    return lib.swa_decode(q, kr, vr, pos, out, B, Hq, Hkv, W, d, scale, dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(kr=None), INVALID), (dict(vr=None), INVALID),
+    (dict(pos=None), INVALID), (dict(out=None), INVALID), (dict(vr=MIS), INVALID),
+    (dict(B=0), INVALID), (dict(Hq=0), INVALID), (dict(Hkv=0), INVALID), (dict(W=0), INVALID),
+    (dict(Hq=6, Hkv=4), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(dtype=3), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(ws=MIS), WORKSPACE), (dict(ws_bytes=0), WORKSPACE),
+])
+def test_decode_rejects(lib, kw, status):
+    assert decode(lib, **kw) == status
+
+
+def test_decode_rejects_one_byte_short_workspace(lib):
+    need = lib.swa_decode_workspace_bytes(2, 8, 64, 64)
+    assert need > 0
+    assert decode(lib, ws_bytes=need - 1) == WORKSPACE
+
+
+def test_workspace_bytes(lib):
+    f = lib.swa_decode_workspace_bytes
+    assert f(0, 8, 64, 64) == 0 and f(2, 0, 64, 64) == 0 and f(2, 8, 0, 64) == 0
+    assert f(2, 8, 64, 48) == 0
+    for B, Hq, W, d in [(64, 32, 4096, 128), (1, 1, 4, 64), (1, 32, 4096, 128), (3, 5, 100, 32)]:
+        n = f(B, Hq, W, d)
+        # whole fp32 partial records (d accumulators + max + sum) per split
+        assert n > 0 and n % (4 * (d + 2) * B * Hq) == 0
+        splits = n // (4 * (d + 2) * B * Hq)
+        assert 1 <= splits <= max(1, (W + 63) // 64)
+
+
+def test_status_strings(lib):
+    assert swa.status_string(0) == "ok"
+    texts = {swa.status_string(s) for s in (0, -1, -2, -3, -4)}
+    assert len(texts) == 5
+    assert swa.status_string(-99) == "unknown status"
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(swa, "_lib", None)
+    monkeypatch.setattr(swa, "LIB_PATH", "/nonexistent/libswa.so")
+    with pytest.raises(RuntimeError, match="libswa.so not found"):
+        swa.load()

@@ -1,0 +1,175 @@
+"""GPU parity of swa_prefill (through the C ABI) against the fp64 oracle.
+
+Small shapes span several 128-row query blocks and 64-key tiles with ragged
+tails; the full-size workloads run in the launch configuration the benchmark
+times and are checked on all rows (TinyMistral, Longformer) or on two whole
+heads plus sampled rows of every head (Mistral 7B).
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import swa_inputs as si
+from helpers import assert_parity, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def swa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sliding_window_attention_swa_amd as m
+    m.load()
+    return m
+
+
+def run(swa, q, k, v, W, mode, scale=None):
+    out = swa.prefill(to_device(q), to_device(k), to_device(v), W, mode=mode, scale=scale)
+    torch.cuda.synchronize()
+    return out
+
+
+def small_inputs(seed, B, Hq, Hkv, T, d, dtype):
+    q = si.normal(seed, (B, Hq, T, d), dtype)
+    k = si.normal(seed + 1, (B, Hkv, T, d), dtype)
+    v = si.normal(seed + 2, (B, Hkv, T, d), dtype)
+    return q, k, v
+
+
+SMALL = [
+    # (mode, T, W, B, Hq, Hkv, d)
+    (0, 1, 4, 1, 1, 1, 64),
+    (0, 5, 3, 2, 4, 2, 32),
+    (0, 63, 1, 1, 2, 1, 64),
+    (0, 64, 64, 1, 2, 2, 128),
+    (0, 65, 17, 2, 4, 1, 32),
+    (0, 130, 32, 1, 8, 2, 64),
+    (0, 300, 100, 2, 4, 2, 128),
+    (0, 333, 1000, 1, 2, 1, 64),
+    (0, 700, 129, 1, 4, 4, 128),
+    (0, 1000, 64, 1, 2, 1, 32),
+    (1, 1, 4, 1, 1, 1, 64),
+    (1, 37, 5, 1, 2, 1, 32),
+    (1, 128, 64, 2, 2, 2, 64),
+    (1, 200, 33, 1, 4, 2, 128),
+    (1, 513, 512, 1, 2, 2, 64),
+    (1, 300, 2000, 1, 2, 1, 128),
+    (1, 1000, 1, 1, 1, 1, 32),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mode,T,W,B,Hq,Hkv,d", SMALL)
+def test_prefill_small(swa, dtype, mode, T, W, B, Hq, Hkv, d):
+    print("prefill", dtype, dict(mode=mode, T=T, W=W, B=B, Hq=Hq, Hkv=Hkv, d=d), flush=True)
+    q, k, v = small_inputs(100 + T + W + d, B, Hq, Hkv, T, d, dtype)
+    scale = 1 / math.sqrt(d)
+    got = to_f64(run(swa, q, k, v, W, mode))
+    ref = oracle.attention_dense(q.values, k.values, v.values, W, mode, scale)
+    assert_parity(got, ref, dtype, "prefill %s mode=%d T=%d W=%d d=%d" % (dtype, mode, T, W, d))
+
+
+def test_toy_workload_fp32(swa):
+    """16 tokens, W=4 and W=16 (= full causal), d=64, fp32."""
+    cfg = si.WORKLOADS[1]
+    q, k, v = si.prefill_inputs(1)
+    scale = 1 / math.sqrt(cfg["d"])
+    for W in (4, 16):
+        got = to_f64(run(swa, q, k, v, W, si.CAUSAL))
+        ref = oracle.attention_dense(q.values, k.values, v.values, W, si.CAUSAL, scale)
+        assert_parity(got, ref, "f32", "toy W=%d" % W)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_window_one_is_exact_copy_of_v(swa, dtype):
+    for mode in (0, 1):
+        q, k, v = small_inputs(7, 2, 4, 2, 150, 64, dtype)
+        out = run(swa, q, k, v, 1, mode)
+        want = to_device(v).repeat_interleave(2, dim=1)
+        assert torch.equal(out, want)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_locality_bit_exact(swa, dtype):
+    """Changing K/V outside every window of rows [r0, r1) leaves those rows
+    bit-identical."""
+    T, W, d = 600, 70, 128
+    q, k, v = small_inputs(11, 1, 2, 1, T, d, dtype)
+    base = run(swa, q, k, v, W, 0)
+    kd, vd = to_device(k), to_device(v)
+    r0, r1 = 300, 340
+    outside = list(range(0, r0 - W + 1)) + list(range(r1, T))
+    kd[:, :, outside] += 3.0
+    vd[:, :, outside] -= 2.0
+    pert = swa.prefill(to_device(q), kd, vd, W)
+    torch.cuda.synchronize()
+    assert torch.equal(pert[:, :, r0:r1], base[:, :, r0:r1])
+    assert not torch.equal(pert[:, :, r1:], base[:, :, r1:])
+
+
+def test_deterministic(swa):
+    q, k, v = small_inputs(12, 1, 8, 2, 1000, 128, "bf16")
+    a = run(swa, q, k, v, 300, 0)
+    b = run(swa, q, k, v, 300, 0)
+    assert torch.equal(a, b)
+
+
+def test_scale_argument_and_negative_scale(swa):
+    q, k, v = small_inputs(13, 1, 2, 1, 200, 64, "bf16")
+    for scale in (0.5, -0.2, 0.0):
+        got = to_f64(run(swa, q, k, v, 50, 0, scale=scale))
+        ref = oracle.attention_dense(q.values, k.values, v.values, 50, 0, scale)
+        assert_parity(got, ref, "bf16", "scale=%g" % scale)
+
+
+# ------------------------------------------------------------ full sizes
+
+def test_tinymistral_full(swa):
+    """B=8, T=2048, W=32, 32/8 heads, d=32, bf16: every row of every head."""
+    cfg = si.WORKLOADS[2]
+    q, k, v = si.prefill_inputs(2)
+    got = to_f64(run(swa, q, k, v, cfg["W"], cfg["mode"]))
+    ref = oracle.attention_banded(q.values, k.values, v.values, cfg["W"], cfg["mode"],
+                                  1 / math.sqrt(cfg["d"]))
+    assert_parity(got, ref, "bf16", "TinyMistral")
+
+
+def test_longformer_full(swa):
+    """B=4, T=4096, W=512 symmetric, 12 heads, d=64, bf16: every row."""
+    cfg = si.WORKLOADS[5]
+    q, k, v = si.prefill_inputs(5)
+    got = to_f64(run(swa, q, k, v, cfg["W"], cfg["mode"]))
+    ref = oracle.attention_banded(q.values, k.values, v.values, cfg["W"], cfg["mode"],
+                                  1 / math.sqrt(cfg["d"]))
+    assert_parity(got, ref, "bf16", "Longformer")
+
+
+def test_mistral_full_sampled(swa):
+    """B=1, T=16384, W=4096, 32/8 heads, d=128, bf16: two whole heads (from
+    different KV groups) plus edge and random rows of every head."""
+    cfg = si.WORKLOADS[3]
+    T, W, d = cfg["T"], cfg["W"], cfg["d"]
+    scale = 1 / math.sqrt(d)
+    q, k, v = si.prefill_inputs(3)
+    got = to_f64(run(swa, q, k, v, W, cfg["mode"]))
+    heads = [(0, 0), (0, 21)]
+    ref = oracle.attention_banded(q.values, k.values, v.values, W, cfg["mode"], scale,
+                                  heads=heads)
+    for b, h in heads:
+        assert_parity(got[b, h], ref[b, h], "bf16", "Mistral head %d" % h)
+    rng = np.random.default_rng(3003)
+    edge = [0, 1, 63, 64, 127, 128, W - 2, W - 1, W, W + 1, T // 2, T - 129, T - 128, T - 1]
+    sampled_got, sampled_ref = [], []
+    for h in range(cfg["Hq"]):
+        rows = sorted(set(edge) | set(rng.integers(0, T, 24).tolist()))
+        sampled_ref.append(oracle.attention_rows(q.values, k.values, v.values, W, cfg["mode"],
+                                                 scale, 0, h, rows))
+        sampled_got.append(got[0, h, rows])
+    assert_parity(np.concatenate(sampled_got), np.concatenate(sampled_ref), "bf16",
+                  "Mistral sampled rows")
