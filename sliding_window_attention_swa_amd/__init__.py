@@ -22,7 +22,10 @@ SYMMETRIC = 1
 SWA_F32 = 0
 SWA_BF16 = 1
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswa.so")
+# SWA_LIBRARY may point at another build of the same library (e.g. a tuning
+# variant); by default the in-tree build is used.
+LIB_PATH = os.environ.get("SWA_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libswa.so")
 
 _lib = None
 

@@ -29,10 +29,10 @@ FLAGS = [
 SOURCES = ["swa_prefill_bf16.hip", "swa_prefill_f32.hip", "swa_ring.hip", "swa_api.cpp"]
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-c",
-                             os.path.join(CSRC, src), "-o", obj]
+def _compile(src, csrc=CSRC, build_dir=BUILD, defines=()):
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC] + FLAGS + ["-D" + d for d in defines] + [
+        "-I", os.path.join(ROOT, "include"), "-c", os.path.join(csrc, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the device-only feature flag: drop that note
     noise = "'-packed-fp32-ops' is not a recognized feature for this target"
@@ -44,19 +44,22 @@ def _compile(src):
     return obj
 
 
-def build(verbose=True):
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose=True, csrc=CSRC, out=LIB, defines=()):
+    """Compile every source in `csrc` and link `out` (default: the in-tree
+    libswa.so).  `defines` are extra -D macros."""
+    build_dir = os.path.join(BUILD, os.path.basename(out) + ".d")
+    os.makedirs(build_dir, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, csrc, build_dir, defines), SOURCES))
+    tmp = out + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", out)
+    return out
 
 
 if __name__ == "__main__":

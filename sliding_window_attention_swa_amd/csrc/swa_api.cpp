@@ -7,7 +7,7 @@
 
 #include <hip/hip_runtime.h>
 
-#include "../../include/swa.h"
+#include "swa.h"
 #include "swa_launch.h"
 
 namespace {

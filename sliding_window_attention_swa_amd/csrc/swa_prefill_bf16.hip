@@ -6,27 +6,38 @@
 // scale * q_i . k_j, applied to the v_j.  Causal window 0 <= i-j <= W-1,
 // symmetric window |i-j| <= floor(W/2), both clipped to [0, T).
 //
-// Structure (one workgroup = 128 query rows of one query head, 4 waves of 32
-// rows each; key tiles of 64 rows):
-//   * only the key tiles that intersect the union of the block's windows are
-//     visited, so the work is O(T * W * d) and no [T, T] matrix exists;
-//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (K tile from LDS as the A
-//     operand, the wave's Q rows held in registers as the B operand), so each
-//     lane owns one query row of the score tile and the row statistics need
-//     only one cross-lane exchange (lane l with lane l^32);
-//   * the out-of-window mask is applied only on tiles that cross a window
-//     edge or the end of the sequence;
-//   * online softmax in fp32 with a lazily updated reference maximum: the
-//     accumulators are rescaled only when a row's maximum grows by more than
-//     2^8, which keeps every exponent <= 2^8 and changes only rounding;
-//   * P is rounded to bf16 and used straight from the score registers as the
-//     B operand of O^T += V^T P^T; V^T comes from the natural [key][dim] LDS
-//     tile through the gfx950 transposing LDS read (ds_read_b64_tr_b16);
-//   * K/V tiles are double-buffered: the next tile's global loads are in
-//     flight while the current one is consumed, one barrier per tile;
-//   * grouped-query heads: query head h reads KV head h / (Hq / Hkv); the
-//     workgroup order keeps the heads of one group and neighbouring query
-//     blocks on the same XCD so their K/V tiles are shared through its L2.
+// Work decomposition: one workgroup = 128 query rows of one query head, four
+// waves of 32 rows; two workgroups per CU (two waves per SIMD, so one wave's
+// softmax can overlap the other's matrix products).  Key/value tiles of 64
+// rows are visited only where they intersect the union of the block's
+// windows, so the work is O(T * W * d) and no [T, T] matrix exists.
+//
+// Per tile:
+//   S^T = K Q^T   v_mfma_f32_32x32x16_bf16 with the K tile (LDS) as the A
+//                 operand and the wave's Q rows (registers) as the B operand,
+//                 so each lane owns one query row and row statistics need one
+//                 exchange between lanes l and l^32.
+//   softmax       fp32, scores kept raw: p = exp2(s*c - m*c) with
+//                 c = scale*log2(e) folded into one FMA.  The reference
+//                 maximum m is raised lazily, only when a row maximum grows by
+//                 more than 2^8, so the accumulators are rarely rescaled
+//                 (exponents stay <= 2^8; only rounding changes).  The row sum
+//                 adds the bf16-rounded probabilities the product uses (packed
+//                 dot2).  The mask is applied only on tiles crossing a window
+//                 edge or the end of the sequence.
+//   O^T += V^T P^T  P (bf16, straight from the score registers) is the B
+//                 operand; V^T comes from the natural [key][dim] LDS tile
+//                 through the transposing LDS read (ds_read_b64_tr_b16).
+// Tiles are double-buffered in LDS: the next tile's buffer loads are in
+// flight while the current one is consumed; one barrier per tile.  Buffer
+// descriptors start at each tile and end at the sequence end, so rows past T
+// read as zeros without any per-lane bounds arithmetic.  LDS rows are
+// unpadded; their 16-byte chunks are XOR-swizzled by row so that the K reads,
+// the transposing V reads and the tile stores are all free of bank conflicts.
+//
+// Grouped-query heads: query head h reads KV head h / (Hq / Hkv); workgroups
+// are ordered so that the heads of one group and neighbouring query blocks
+// land on the same XCD and share K/V through its L2.
 
 #include "swa_device.h"
 #include "swa_launch.h"
@@ -34,39 +45,59 @@
 namespace swa {
 namespace {
 
-constexpr int kBM = 128;  // query rows per workgroup
-constexpr int kBN = 64;   // key rows per tile
-constexpr int kThreads = 256;
-constexpr float kRescaleThreshold = 8.0f;  // log2 units
-constexpr float kNegBig = -1.0e30f;        // finite "no maximum yet"
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32 * kWaves;   // query rows per workgroup
+constexpr int kBN = 64;            // key rows per tile
+constexpr float kGrowLog2 = 8.0f;  // rescale when a row maximum grows by > 2^8
+constexpr float kNoMax = -1.0e30f;
+constexpr int kBufferFlags = 0x00020000;  // raw 32-bit buffer access
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct Geo {
-  static constexpr int PITCH = D + 8;           // LDS row pitch (elements): 16 B pad
-  static constexpr int TILE = kBN * PITCH;      // elements in one K or V tile
-  static constexpr int KS = D / 16;             // k-steps of the QK^T contraction
-  static constexpr int MD = D / 32;             // 32-dim blocks of the output
-  static constexpr int TPR = D / 8;             // copy threads per row (16 B each)
-  static constexpr int RPI = kThreads / TPR;    // rows per copy instruction
-  static constexpr int NLD = kBN / RPI;         // copy instructions per tile
-  static constexpr int LDS_BYTES = 2 * 2 * TILE * 2;
+  static constexpr int ROWB = D * 2;              // bytes per K/V row in LDS
+  static constexpr int CHUNKS = D / 8;            // 16-byte chunks per row
+  static constexpr int TILEB = kBN * ROWB;        // bytes per tile
+  static constexpr int KS = D / 16;               // k-steps of S = K Q^T
+  static constexpr int MD = D / 32;               // 32-dim output blocks
+  static constexpr int RPI = kThreads / CHUNKS;   // rows per copy instruction
+  static constexpr int NLD = kBN / RPI;           // copy instructions per tile
+  static constexpr int LDS_BYTES = 2 * 2 * TILEB; // [stage][K|V]
 };
 
+// XOR swizzle of a row's 16-byte chunks (LDS: 64 banks of 4 bytes, i.e. 16
+// chunk slots per 256 bytes).  Chosen per row length so that
+//   * the K operand read (16 lanes, 16 consecutive rows, one logical chunk),
+//   * the transposing V read (32 lanes, 4 consecutive rows x two 32-byte
+//     chunk pairs) and
+//   * the tile stores (16 lanes, consecutive chunks)
+// each touch every bank slot at most once.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  if (D == 64) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  return (row >> 2) & 3;
+}
+
 template <int D, int MODE>
-__global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    __bf16* __restrict__ out, int T, int W, int Hq, int Hkv, float scale_log2, int n_qtiles) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                         const __bf16* __restrict__ v, __bf16* __restrict__ out, int T, int W,
+                         int Hq, int Hkv, float c, uint32_t qsign, int n_qtiles) {
   using Gm = Geo<D>;
-  constexpr int PITCH = Gm::PITCH, TILE = Gm::TILE, KS = Gm::KS, MD = Gm::MD;
-  constexpr int TPR = Gm::TPR, RPI = Gm::RPI, NLD = Gm::NLD;
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * 2 * TILE];  // [stage][K|V][kBN][PITCH]
+  constexpr int ROWB = Gm::ROWB, CHUNKS = Gm::CHUNKS, TILEB = Gm::TILEB, KS = Gm::KS;
+  constexpr int MD = Gm::MD, RPI = Gm::RPI, NLD = Gm::NLD;
+  __shared__ __attribute__((aligned(1024))) char smem[Gm::LDS_BYTES];
 
   // ---- which (query head, query block) this workgroup owns
   const int G = Hq / Hkv;
   int id = blockIdx.x;
   const int nwg = gridDim.x;
-  // Consecutive workgroup ids are dealt round-robin to the 8 XCDs; regroup
-  // them so that each XCD receives a contiguous range of logical ids.
+  // consecutive ids go round-robin to the 8 XCDs: give each XCD a contiguous range
   if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
   const int hg = id % G;
   const int rest = id / G;
@@ -77,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int half = lane >> 5;  // which 8 of the 16 contraction elements this lane holds
+  const int half = lane >> 5;
   const int q0 = qt * kBM;
   const int qw0 = q0 + wave * 32;
   const int qi = qw0 + (lane & 31);  // the query row this lane owns
@@ -103,57 +134,86 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
   const int wlo = (MODE == 0) ? max(0, qw0 - W + 1) : max(0, qw0 - hw);
   const int whi = (MODE == 0) ? qlast : min(T - 1, qlast + hw);
 
-  // ---- Q rows as B operands (one per k-step), zero beyond the sequence
+  // ---- Q rows as B operands, zero beyond the sequence; a negative scale is
+  // folded into Q's sign bits (exact) so that c > 0 below.
   bf16x8 qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    if (qi < T) {
-      qf[ks] = *reinterpret_cast<const bf16x8*>(qh + (size_t)qi * D + ks * 16 + half * 8);
-    } else {
-      qf[ks] = bf16x8{};
-    }
+    uint4 r = make_uint4(0, 0, 0, 0);
+    if (qi < T) r = *reinterpret_cast<const uint4*>(qh + (size_t)qi * D + ks * 16 + half * 8);
+    r.x ^= qsign;
+    r.y ^= qsign;
+    r.z ^= qsign;
+    r.w ^= qsign;
+    qf[ks] = __builtin_bit_cast(bf16x8, r);
   }
 
-  // ---- global -> register -> LDS tile copy
-  uint4 kreg[NLD], vreg[NLD];
-  const int crow = tid / TPR;
-  const int ccol = (tid % TPR) * 8;
+  // ---- global -> register -> LDS tile copy.  Copy slot i of this thread is
+  // row i*RPI + tid/CHUNKS, chunk tid%CHUNKS; in LDS the chunk goes to its
+  // swizzled position.
+  const int crow = tid / CHUNKS;
+  const int cchunk = tid % CHUNKS;
+  int src_off[NLD], dst_off[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int row = i * RPI + crow;
+    src_off[i] = row * ROWB + cchunk * 16;
+    dst_off[i] = row * ROWB + ((cchunk ^ (swz<D>(row))) * 16);
+  }
+  i32x4 kreg[NLD], vreg[NLD];
   auto load_tile = [&](int kt) {
     const int kbase = kt * kBN;
+    const int bytes = (T - kbase) * ROWB;  // rows past T read as zeros
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kh + (size_t)kbase * D), 0, bytes, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vh + (size_t)kbase * D), 0, bytes, kBufferFlags);
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const int key = kbase + i * RPI + crow;
-      if (key < T) {
-        kreg[i] = *reinterpret_cast<const uint4*>(kh + (size_t)key * D + ccol);
-        vreg[i] = *reinterpret_cast<const uint4*>(vh + (size_t)key * D + ccol);
-      } else {
-        kreg[i] = make_uint4(0, 0, 0, 0);
-        vreg[i] = make_uint4(0, 0, 0, 0);
-      }
+      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, src_off[i], 0, 0);
+      vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, src_off[i], 0, 0);
     }
   };
   auto store_tile = [&](int stage) {
-    __bf16* Ks = smem + stage * 2 * TILE;
-    __bf16* Vs = Ks + TILE;
+    char* Ks = smem + stage * 2 * TILEB;
+    char* Vs = Ks + TILEB;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const int r = i * RPI + crow;
-      *reinterpret_cast<uint4*>(Ks + r * PITCH + ccol) = kreg[i];
-      *reinterpret_cast<uint4*>(Vs + r * PITCH + ccol) = vreg[i];
+      *reinterpret_cast<i32x4*>(Ks + dst_off[i]) = kreg[i];
+      *reinterpret_cast<i32x4*>(Vs + dst_off[i]) = vreg[i];
     }
   };
+
+  // ---- per-lane LDS read offsets.
+  // K (A operand of S^T): row mb*32 + lane%32, logical chunk 2*ks + half,
+  // stored at chunk (2*ks + half) ^ f.
+  const int kr = lane & 31;
+  const int kf = swz<D>(kr);
+  int koff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = kr * ROWB + (((2 * ks + half) ^ kf) * 16);
+  // V (transposing read): source lane s of 16-lane group g addresses key row
+  // 16*kk + 4*(g/2) + s/4 (plus 8 for the upper half) and dims
+  // 32*md + 16*(g%2) + 4*(s%4), i.e. logical chunk 4*md + c0.  The two halves
+  // sit 8 rows apart, which changes the swizzle, so each has its own offsets.
+  const int tr_s = lane & 15, tr_g = lane >> 4;
+  const int tr_row = 4 * (tr_g >> 1) + (tr_s >> 2);
+  const int tr_c0 = 2 * (tr_g & 1) + ((tr_s & 3) >> 1);
+  const int tr_flo = swz<D>(tr_row), tr_fhi = swz<D>(tr_row + 8);
+  int voff_lo[MD], voff_hi[MD];
+#pragma unroll
+  for (int md = 0; md < MD; ++md) {
+    voff_lo[md] = tr_row * ROWB + (((4 * md + tr_c0) ^ tr_flo) * 16) + (tr_s & 1) * 8;
+    voff_hi[md] = (tr_row + 8) * ROWB + (((4 * md + tr_c0) ^ tr_fhi) * 16) + (tr_s & 1) * 8;
+  }
 
   f32x16 o[MD];
 #pragma unroll
   for (int md = 0; md < MD; ++md) o[md] = f32x16{};
-  float m_ref = kNegBig;  // reference maximum (log2 domain) of this lane's row
-  float l_part = 0.f;     // this lane's share of the row's exponential sum
-
-  // source-lane addressing of the transposing V read (see the PV step)
-  const int tr_s = lane & 15;
-  const int tr_g = lane >> 4;
-  const int tr_row = 4 * (tr_g >> 1) + (tr_s >> 2);
-  const int tr_col = 16 * (tr_g & 1) + 4 * (tr_s & 3);
+  float m_ref = kNoMax;  // raw-score reference maximum of this lane's row
+  float l_part = 0.f;    // this lane's share of the row sum
+  const float grow_raw = kGrowLog2 / c;
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   load_tile(kt0);
   store_tile(0);
@@ -165,33 +225,27 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
     const int k0 = kt * kBN;
     const bool relevant = wave_active && k0 <= whi && k0 + kBN - 1 >= wlo;
     if (relevant) {
-      const __bf16* Ks = smem + stage * 2 * TILE;
-      const __bf16* Vs = Ks + TILE;
+      const char* Ks = smem + stage * 2 * TILEB;
+      const char* Vs = Ks + TILEB;
 
       // ---- S^T tile: 64 keys x 32 queries, two 32-key blocks
       f32x16 s[2];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         s[mb] = f32x16{};
-        const __bf16* krow = Ks + (mb * 32 + (lane & 31)) * PITCH + half * 8;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + ks * 16);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + mb * 32 * ROWB + koff[ks]);
           s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[mb], 0, 0, 0);
         }
       }
 
-      // ---- scale into the log2 domain; mask tiles that cross an edge
+      // ---- mask the tiles that cross a window edge or the sequence end
       bool full;
       if (MODE == 0) {
         full = (k0 + kBN - 1 <= qw0) && (k0 >= qlast - W + 1) && (k0 + kBN <= T);
       } else {
         full = (k0 >= qlast - hw) && (k0 + kBN - 1 <= qw0 + hw) && (k0 + kBN <= T);
-      }
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[mb][r] *= scale_log2;
       }
       if (!full) {
 #pragma unroll
@@ -212,17 +266,17 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
       }
 
       // ---- row maximum (this lane's 32 scores, then the partner lane's)
-      float mx = s[0][0];
+      float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+      for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-      mx = wave_max_xor32(mx);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
 
-      const bool grow = mx > m_ref + kRescaleThreshold;
+      const bool grow = mx > m_ref + grow_raw;
       if (__ballot(grow)) {
         const float m_new = grow ? mx : m_ref;
-        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+        const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * c);
         m_ref = m_new;
         l_part *= alpha;
 #pragma unroll
@@ -232,45 +286,42 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
         }
       }
 
-      // ---- probabilities, row sum, bf16 B operands of the PV product
-      bf16x8 pb[2][2];
+      // ---- probabilities (bf16 B operands of the PV product) and row sum
+      const float mc = -m_ref * c;
+      bf16x8 pb[4];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(s[mb][r] - m_ref);
-          s[mb][r] = p;
-          l_part += p;
-        }
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
           uint32_t w[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(s[mb][8 * k2 + 2 * e], s[mb][8 * k2 + 2 * e + 1]);
-          pb[mb][k2] = __builtin_bit_cast(bf16x8, w);
+          for (int e = 0; e < 4; ++e) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[mb][8 * k2 + 2 * e], c, mc));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[mb][8 * k2 + 2 * e + 1], c, mc));
+            w[e] = pack_bf16x2(p0, p1);
+            l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[e]), ones,
+                                                     l_part, false);
+          }
+          pb[2 * mb + k2] = __builtin_bit_cast(bf16x8, w);
         }
       }
 
-      // ---- O^T += V^T P^T.  Element j of pb[mb][k2] in lane l holds key
-      // mb*32 + 16*k2 + 8*(j/4) + 4*(l/32) + j%4.  The A operand must hold
-      // V at those keys for dim 32*md + l%32; two transposing reads give
-      // exactly that: within each 16-lane group, lane i receives component
-      // i%4 of the 8 bytes addressed by lane 4*j + i/4, and each source lane
-      // addresses 4 consecutive dims of one key row.
+      // ---- O^T += V^T P^T.  Element j of pb[kk] in lane l holds key
+      // 16*kk + 8*(j/4) + 4*(l/32) + j%4.  The A operand must hold V at those
+      // keys for dim 32*md + l%32; two transposing reads give exactly that:
+      // within each 16-lane group, lane i receives component i%4 of the 8
+      // bytes addressed by lane 4*j + i/4, and each source lane addresses 4
+      // consecutive dims of one key row.
 #pragma unroll
       for (int md = 0; md < MD; ++md) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-          for (int k2 = 0; k2 < 2; ++k2) {
-            const __bf16* src = Vs + (mb * 32 + 16 * k2 + tr_row) * PITCH + 32 * md + tr_col;
-            const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src));
-            const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + 8 * PITCH));
-            typedef short i16x8 __attribute__((ext_vector_type(8)));
-            const i16x8 a16 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-            const bf16x8 a = __builtin_bit_cast(bf16x8, a16);
-            o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[mb][k2], o[md], 0, 0, 0);
-          }
+        for (int kk = 0; kk < 4; ++kk) {
+          const char* src = Vs + kk * 16 * ROWB;
+          const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + voff_lo[md]));
+          const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + voff_hi[md]));
+          const i16x8 a16 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+          o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a16), pb[kk],
+                                                          o[md], 0, 0, 0);
         }
       }
     }
@@ -278,9 +329,10 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
     __syncthreads();
   }
 
-  // ---- epilogue: divide by the row sum, round to bf16, store
+  // ---- epilogue: divide by the row sum, round to bf16, store.  The
+  // row-sum exchange involves both wave halves, so it precedes the guard.
+  const float l_tot = l_part + __shfl_xor(l_part, 32);
   if (qi < T) {
-    const float l_tot = l_part + __shfl_xor(l_part, 32);
     const float inv = 1.0f / l_tot;
     __bf16* orow = out + ((size_t)h * T + qi) * D;
 #pragma unroll
@@ -302,10 +354,17 @@ hipError_t launch(const void* q, const void* k, const void* v, void* out, int T,
                   int Hkv, float scale, hipStream_t stream) {
   const int n_qtiles = (T + kBM - 1) / kBM;
   const long long nwg = (long long)n_qtiles * Hq;
+  float c = scale * kLog2e;
+  uint32_t qsign = 0;
+  if (c < 0.f) {  // fold the sign into Q (bf16 negation is exact)
+    c = -c;
+    qsign = 0x80008000u;
+  }
+  if (c == 0.f) c = 1.0e-30f;  // all weights equal; masked logits stay at -inf
   hipLaunchKernelGGL((prefill_bf16_kernel<D, MODE>), dim3((unsigned)nwg), dim3(kThreads), 0,
                      stream, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
-                     static_cast<const __bf16*>(v), static_cast<__bf16*>(out), T, W, Hq, Hkv,
-                     scale * kLog2e, n_qtiles);
+                     static_cast<const __bf16*>(v), static_cast<__bf16*>(out), T, W, Hq, Hkv, c,
+                     qsign, n_qtiles);
   return hipGetLastError();
 }
 
