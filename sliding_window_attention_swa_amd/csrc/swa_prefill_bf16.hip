@@ -28,10 +28,9 @@
 //   O^T += V^T P^T  P (bf16, straight from the score registers) is the B
 //                 operand; V^T comes from the natural [key][dim] LDS tile
 //                 through the transposing LDS read (ds_read_b64_tr_b16).
-// Tiles are double-buffered in LDS: the next tile's buffer loads are in
-// flight while the current one is consumed; one barrier per tile.  Buffer
-// descriptors start at each tile and end at the sequence end, so rows past T
-// read as zeros without any per-lane bounds arithmetic.  LDS rows are
+// Tiles are double-buffered in LDS and filled by direct buffer-to-LDS loads
+// (no register staging): the next tile's loads are in flight while the
+// current one is consumed; one barrier per tile.  LDS rows are
 // unpadded; their 16-byte chunks are XOR-swizzled by row so that the K reads,
 // the transposing V reads and the tile stores are all free of bank conflicts.
 //
@@ -56,6 +55,7 @@ constexpr int kBufferFlags = 0x00020000;  // raw 32-bit buffer access
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 template <int D>
 struct Geo {
@@ -64,9 +64,7 @@ struct Geo {
   static constexpr int TILEB = kBN * ROWB;        // bytes per tile
   static constexpr int KS = D / 16;               // k-steps of S = K Q^T
   static constexpr int MD = D / 32;               // 32-dim output blocks
-  static constexpr int RPI = kThreads / CHUNKS;   // rows per copy instruction
-  static constexpr int NLD = kBN / RPI;           // copy instructions per tile
-  static constexpr int LDS_BYTES = 2 * 2 * TILEB; // [stage][K|V]
+  static constexpr int NLD = TILEB / (kThreads * 16);  // direct loads per thread per tile
 };
 
 // XOR swizzle of a row's 16-byte chunks (LDS: 64 banks of 4 bytes, i.e. 16
@@ -90,8 +88,13 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
                          int Hq, int Hkv, float c, uint32_t qsign, int n_qtiles) {
   using Gm = Geo<D>;
   constexpr int ROWB = Gm::ROWB, CHUNKS = Gm::CHUNKS, TILEB = Gm::TILEB, KS = Gm::KS;
-  constexpr int MD = Gm::MD, RPI = Gm::RPI, NLD = Gm::NLD;
-  __shared__ __attribute__((aligned(1024))) char smem[Gm::LDS_BYTES];
+  constexpr int MD = Gm::MD, NLD = Gm::NLD;
+  // two stages of K and V tiles, as separate objects so the compiler can tell
+  // the stage being filled by direct loads from the stage being read
+  __shared__ __attribute__((aligned(1024))) char lds_k0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char lds_v0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char lds_k1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char lds_v1[TILEB];
 
   // ---- which (query head, query block) this workgroup owns
   const int G = Hq / Hkv;
@@ -148,39 +151,36 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     qf[ks] = __builtin_bit_cast(bf16x8, r);
   }
 
-  // ---- global -> register -> LDS tile copy.  Copy slot i of this thread is
-  // row i*RPI + tid/CHUNKS, chunk tid%CHUNKS; in LDS the chunk goes to its
-  // swizzled position.
-  const int crow = tid / CHUNKS;
-  const int cchunk = tid % CHUNKS;
-  int src_off[NLD], dst_off[NLD];
+  // ---- global -> LDS tile copy with direct (buffer -> LDS) loads.  Load j
+  // of this thread fills the 16 bytes at LDS offset (j*kThreads + tid)*16 of
+  // the tile (each wave writes 1 KB contiguously) and fetches the logical
+  // chunk the swizzle keeps there.  In the last, partial tile the rows past T
+  // re-read row T-1, so every LDS row holds finite data (their scores are
+  // masked to zero weight, and 0 * finite = 0 in the product).
+  int src_off[NLD], src_row[NLD];
 #pragma unroll
-  for (int i = 0; i < NLD; ++i) {
-    const int row = i * RPI + crow;
-    src_off[i] = row * ROWB + cchunk * 16;
-    dst_off[i] = row * ROWB + ((cchunk ^ (swz<D>(row))) * 16);
+  for (int j = 0; j < NLD; ++j) {
+    const int o = (j * kThreads + tid) * 16;
+    const int row = o / ROWB;
+    src_row[j] = row;
+    src_off[j] = (((o % ROWB) / 16) ^ swz<D>(row)) * 16;
   }
-  i32x4 kreg[NLD], vreg[NLD];
-  auto load_tile = [&](int kt) {
+  auto load_tile = [&](char* Kdst, char* Vdst, int kt) __attribute__((always_inline)) {
     const int kbase = kt * kBN;
-    const int bytes = (T - kbase) * ROWB;  // rows past T read as zeros
+    const int last = T - 1 - kbase;  // last valid row of this tile
+    const int bytes = (last + 1) * ROWB;
     const __amdgpu_buffer_rsrc_t rk =
         __builtin_amdgcn_make_buffer_rsrc((void*)(kh + (size_t)kbase * D), 0, bytes, kBufferFlags);
     const __amdgpu_buffer_rsrc_t rv =
         __builtin_amdgcn_make_buffer_rsrc((void*)(vh + (size_t)kbase * D), 0, bytes, kBufferFlags);
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, src_off[i], 0, 0);
-      vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, src_off[i], 0, 0);
-    }
-  };
-  auto store_tile = [&](int stage) {
-    char* Ks = smem + stage * 2 * TILEB;
-    char* Vs = Ks + TILEB;
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      *reinterpret_cast<i32x4*>(Ks + dst_off[i]) = kreg[i];
-      *reinterpret_cast<i32x4*>(Vs + dst_off[i]) = vreg[i];
+    for (int j = 0; j < NLD; ++j) {
+      const int wbase = (j * kThreads + wave * 64) * 16;
+      const int off = min(src_row[j], last) * ROWB + src_off[j];
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass mishandles this builtin
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(Kdst + wbase), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(Vdst + wbase), 16, off, 0, 0, 0);
+#endif
     }
   };
 
@@ -215,118 +215,213 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   const float grow_raw = kGrowLog2 / c;
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  load_tile(kt0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int kt = kt0; kt <= kt1; ++kt) {
-    const int stage = (kt - kt0) & 1;
-    if (kt < kt1) load_tile(kt + 1);
-    const int k0 = kt * kBN;
-    const bool relevant = wave_active && k0 <= whi && k0 + kBN - 1 >= wlo;
-    if (relevant) {
-      const char* Ks = smem + stage * 2 * TILEB;
-      const char* Vs = Ks + TILEB;
-
-      // ---- S^T tile: 64 keys x 32 queries, two 32-key blocks
-      f32x16 s[2];
+  // ---- tile building blocks
+  auto kread = [&](const char* Ks, int mb, int ks) __attribute__((always_inline)) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(Ks + mb * 32 * ROWB + koff[ks]);
+  };
+  // O^T += V^T P^T for 16 keys (kk).  Element j of the P operand in lane l
+  // holds key 16*kk + 8*(j/4) + 4*(l/32) + j%4.  The A operand must hold V at
+  // those keys for dim 32*md + l%32; two transposing reads give exactly that:
+  // within each 16-lane group, lane i receives component i%4 of the 8 bytes
+  // addressed by lane 4*j + i/4, and each source lane addresses 4 consecutive
+  // dims of one key row.
+  auto vread = [&](const char* Vs, int md, int kk) __attribute__((always_inline)) -> bf16x8 {
+    const char* src = Vs + kk * 16 * ROWB;
+    const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + voff_lo[md]));
+    const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + voff_hi[md]));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // probabilities of one 32-key half against the current reference maximum,
+  // packed as two bf16 B operands, with their (rounded) sum and the raw max
+  auto probs = [&](const f32x16& s, float mc, bf16x8* p, float& lsum, float& mx) __attribute__((always_inline)) {
+    mx = fmaxf(s[0], s[1]);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        s[mb] = f32x16{};
+    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    lsum = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + mb * 32 * ROWB + koff[ks]);
-          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[mb], 0, 0, 0);
-        }
+    for (int k2 = 0; k2 < 2; ++k2) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * k2 + 2 * e], c, mc));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * k2 + 2 * e + 1], c, mc));
+        w[e] = pack_bf16x2(p0, p1);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[e]), ones, lsum, false);
       }
+      p[k2] = __builtin_bit_cast(bf16x8, w);
+    }
+  };
+  // raise the reference maximum where a row grew by more than 2^8; rescale
+  // the accumulators and return true when any row of the wave did
+  auto raise_max = [&](float mx) __attribute__((always_inline)) -> bool {
+    mx = fmaxf(mx, __shfl_xor(mx, 32));  // lanes l and l^32 hold the same row
+    const bool grow = mx > m_ref + grow_raw;
+    if (!__ballot(grow)) return false;
+    const float m_new = grow ? mx : m_ref;
+    const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * c);
+    m_ref = m_new;
+    l_part *= alpha;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[md][r] *= alpha;
+    }
+    return true;
+  };
 
-      // ---- mask the tiles that cross a window edge or the sequence end
-      bool full;
-      if (MODE == 0) {
-        full = (k0 + kBN - 1 <= qw0) && (k0 >= qlast - W + 1) && (k0 + kBN <= T);
-      } else {
-        full = (k0 >= qlast - hw) && (k0 + kBN - 1 <= qw0 + hw) && (k0 + kBN <= T);
-      }
-      if (!full) {
+  // opaque use: makes the speculative probabilities exist at this point, so
+  // they are computed inside the overlap region rather than sunk into a branch
+  auto pin = [&](bf16x8* p, float& l, float& m) __attribute__((always_inline)) {
+    uint4 w0 = __builtin_bit_cast(uint4, p[0]), w1 = __builtin_bit_cast(uint4, p[1]);
+#if defined(__HIP_DEVICE_COMPILE__)  // register constraints exist only for the GPU pass
+    __asm__ volatile("" : "+v"(w0.x), "+v"(w0.y), "+v"(w0.z), "+v"(w0.w));
+    __asm__ volatile("" : "+v"(w1.x), "+v"(w1.y), "+v"(w1.z), "+v"(w1.w), "+v"(l), "+v"(m));
+#endif
+    p[0] = __builtin_bit_cast(bf16x8, w0);
+    p[1] = __builtin_bit_cast(bf16x8, w1);
+  };
+
+  // A tile inside every row's window.  Three regions, each mixing matrix and
+  // vector work so that one wave keeps both busy:
+  //   A: S of keys 32..63        | probabilities of keys 0..31
+  //   B: O += V P for keys 0..31 | probabilities of keys 32..63
+  //   C: O += V P for keys 32..63
+  // Probabilities are computed against the current reference maximum; the
+  // rare tile that raises it recomputes them after the rescale.
+  auto interior_tile = [&](const char* Ks, const char* Vs) __attribute__((always_inline)) {
+    // S for keys 0..31: all K operands requested up front
+    bf16x8 ka[KS];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+    for (int ks = 0; ks < KS; ++ks) ka[ks] = kread(Ks, 0, ks);
+    f32x16 s0 = f32x16{};
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            const int diff = qi - key;
-            bool ok = key < T;
-            if (MODE == 0) {
-              ok = ok && diff >= 0 && diff < W;
-            } else {
-              ok = ok && diff >= -hw && diff <= hw;
-            }
-            if (!ok) s[mb][r] = -INFINITY;
-          }
+    for (int ks = 0; ks < KS; ++ks) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], s0, 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // region A: S for keys 32..63 | probabilities of keys 0..31
+    bf16x8 p0[2], p1[2];
+    float l0, l1, mx0, mx1;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) ka[ks] = kread(Ks, 1, ks);
+    f32x16 s1 = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], s1, 0, 0, 0);
+    probs(s0, -m_ref * c, p0, l0, mx0);
+    pin(p0, l0, mx0);
+    __builtin_amdgcn_sched_group_barrier(0x100, KS / 2, 0);
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 56 / KS, 0);
+      if (i < KS / 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (raise_max(mx0)) probs(s0, -m_ref * c, p0, l0, mx0);
+    l_part += l0;
+
+    // region B: O += V P for keys 0..31 | probabilities of keys 32..63
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(Vs, md, kk), p0[kk], o[md], 0, 0, 0);
+    }
+    probs(s1, -m_ref * c, p1, l1, mx1);
+    pin(p1, l1, mx1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * MD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 56 / (2 * MD), 0);
+      if (i < 2 * MD - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (raise_max(mx1)) probs(s1, -m_ref * c, p1, l1, mx1);
+    l_part += l1;
+
+    // region C: O += V P for keys 32..63
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(Vs, md, 2 + kk), p1[kk], o[md], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * MD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < 2 * MD - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // A tile that crosses a window edge or the sequence end: mask, then the
+  // same steps without overlap.
+  auto edge_tile = [&](const char* Ks, const char* Vs, int k0) __attribute__((always_inline)) {
+    f32x16 s[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      s[mb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(Ks, mb, ks), qf[ks], s[mb], 0, 0, 0);
+    }
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        const int diff = qi - key;
+        bool ok = key < T;
+        if (MODE == 0) {
+          ok = ok && diff >= 0 && diff < W;
+        } else {
+          ok = ok && diff >= -hw && diff <= hw;
         }
-      }
-
-      // ---- row maximum (this lane's 32 scores, then the partner lane's)
-      float mx = fmaxf(s[0][0], s[0][1]);
-#pragma unroll
-      for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-
-      const bool grow = mx > m_ref + grow_raw;
-      if (__ballot(grow)) {
-        const float m_new = grow ? mx : m_ref;
-        const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * c);
-        m_ref = m_new;
-        l_part *= alpha;
-#pragma unroll
-        for (int md = 0; md < MD; ++md) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[md][r] *= alpha;
-        }
-      }
-
-      // ---- probabilities (bf16 B operands of the PV product) and row sum
-      const float mc = -m_ref * c;
-      bf16x8 pb[4];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          uint32_t w[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[mb][8 * k2 + 2 * e], c, mc));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[mb][8 * k2 + 2 * e + 1], c, mc));
-            w[e] = pack_bf16x2(p0, p1);
-            l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[e]), ones,
-                                                     l_part, false);
-          }
-          pb[2 * mb + k2] = __builtin_bit_cast(bf16x8, w);
-        }
-      }
-
-      // ---- O^T += V^T P^T.  Element j of pb[kk] in lane l holds key
-      // 16*kk + 8*(j/4) + 4*(l/32) + j%4.  The A operand must hold V at those
-      // keys for dim 32*md + l%32; two transposing reads give exactly that:
-      // within each 16-lane group, lane i receives component i%4 of the 8
-      // bytes addressed by lane 4*j + i/4, and each source lane addresses 4
-      // consecutive dims of one key row.
-#pragma unroll
-      for (int md = 0; md < MD; ++md) {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const char* src = Vs + kk * 16 * ROWB;
-          const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + voff_lo[md]));
-          const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + voff_hi[md]));
-          const i16x8 a16 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a16), pb[kk],
-                                                          o[md], 0, 0, 0);
-        }
+        if (!ok) s[mb][r] = -INFINITY;
       }
     }
-    if (kt < kt1) store_tile(stage ^ 1);
+    bf16x8 p[4];
+    float l0, l1, mx0, mx1;
+    probs(s[0], -m_ref * c, p, l0, mx0);
+    probs(s[1], -m_ref * c, p + 2, l1, mx1);
+    if (raise_max(fmaxf(mx0, mx1))) {
+      probs(s[0], -m_ref * c, p, l0, mx0);
+      probs(s[1], -m_ref * c, p + 2, l1, mx1);
+    }
+    l_part += l0 + l1;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(Vs, md, kk), p[kk], o[md], 0, 0, 0);
+    }
+  };
+
+  // One tile: wait for its loads (issued during the previous tile) and for
+  // every wave to be done with the other stage, refill that stage with the
+  // next tile, then consume this one.
+  auto step = [&](const char* Ks, const char* Vs, char* Kn, char* Vn, int kt) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
+    if (kt < kt1) load_tile(Kn, Vn, kt + 1);
+    const int k0 = kt * kBN;
+    if (!(wave_active && k0 <= whi && k0 + kBN - 1 >= wlo)) return;
+    bool full;
+    if (MODE == 0) {
+      full = (k0 + kBN - 1 <= qw0) && (k0 >= qlast - W + 1) && (k0 + kBN <= T);
+    } else {
+      full = (k0 >= qlast - hw) && (k0 + kBN - 1 <= qw0 + hw) && (k0 + kBN <= T);
+    }
+    if (full) {
+      interior_tile(Ks, Vs);
+    } else {
+      edge_tile(Ks, Vs, k0);
+    }
+  };
+  load_tile(lds_k0, lds_v0, kt0);
+  for (int kt = kt0; kt <= kt1; kt += 2) {
+    step(lds_k0, lds_v0, lds_k1, lds_v1, kt);
+    if (kt + 1 > kt1) break;
+    step(lds_k1, lds_v1, lds_k0, lds_v0, kt + 1);
   }
 
   // ---- epilogue: divide by the row sum, round to bf16, store.  The
