@@ -37,6 +37,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
 METRIC = "SWA prefill in-window TFLOP/s + decode KV-read GB/s, % of MI355X peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_mistral7b_traffic.md")
+COPY_BYTES = 256 << 20  # calibration copy: reads and writes this many bytes
 
 
 def band_pairs_causal(T, W):
@@ -64,28 +65,83 @@ def decode_work(pos):
     return flops, kv_bytes, qo_bytes
 
 
-def read_traffic(kernel_hash):
-    """HBM bytes per launch of the prefill kernel from the committed counter
-    summary, if it was taken on the current kernel source."""
+def read_traffic(prefix, source):
+    """HBM bytes per launch recorded in the committed counter summary under
+    `<prefix>traffic_bytes_per_launch`, if it was taken on the current source
+    of the kernel (`<prefix>traffic_kernel_sha256`)."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     fields = {}
     for line in open(TRAFFIC_FILE):
-        if line.startswith("traffic_") and ":" in line:
+        if ":" in line and not line.startswith(" "):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("traffic_kernel_sha256") != kernel_hash:
+    if fields.get(prefix + "traffic_kernel_sha256") != source_hash(source):
         return None
     try:
-        return int(fields["traffic_bytes_per_launch"])
+        return int(fields[prefix + "traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
 
 
-def kernel_source_hash():
+def source_hash(name):
     import hashlib
-    p = os.path.join(ROOT, "sliding_window_attention_swa_amd", "csrc", "swa_prefill_bf16.hip")
+    p = os.path.join(ROOT, "sliding_window_attention_swa_amd", "csrc", name)
     return hashlib.sha256(open(p, "rb").read()).hexdigest()
+
+
+PREFILL_SOURCE = "swa_prefill_bf16.hip"
+DECODE_SOURCE = "swa_ring.hip"
+
+
+def summarize_pmc(paths):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the calibration copy and
+    of the step's kernels -> HBM bytes per launch.  Each counter is scaled by
+    (known copy bytes) / (what that counter reads for the copy).  The copy is
+    the largest runtime buffer copy (__amd_rocclr_copyBuffer) in the run."""
+    import csv
+    kinds = {"prefill_bf16_kernel": "prefill", "decode_split_kernel": "decode",
+             "decode_combine_kernel": "decode_combine"}
+    per = {}  # (kind, counter) -> value
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            name, ctr, val = r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
+            if "copyBuffer" in name:
+                per[("copy", ctr)] = max(per.get(("copy", ctr), 0.0), val)
+                continue
+            for pat, kind in kinds.items():
+                if pat in name:
+                    per[(kind, ctr)] = per.get((kind, ctr), 0.0) + val
+    factors = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        copy_kib = per.get(("copy", ctr))
+        if not copy_kib:
+            print("no calibration copy for %s" % ctr, file=sys.stderr)
+            return 1
+        factors[ctr] = COPY_BYTES / (copy_kib * 1024.0)
+        print("%s: the %d MiB copy reads %.0f KiB -> factor %.4f"
+              % (ctr, COPY_BYTES >> 20, copy_kib, factors[ctr]))
+    totals = {}
+    for kind in ("prefill", "decode", "decode_combine"):
+        parts = []
+        for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+            kib = per.get((kind, ctr))
+            if kib is None:
+                continue
+            b = kib * 1024.0 * factors[ctr]
+            parts.append(b)
+            print("%s %s: %.0f KiB -> %.0f bytes" % (kind, ctr, kib, b))
+        if len(parts) == 2:
+            totals[kind] = int(sum(parts))
+    if "prefill" not in totals:
+        print("no prefill counters", file=sys.stderr)
+        return 1
+    print("traffic_bytes_per_launch: %d" % totals["prefill"])
+    print("traffic_kernel_sha256: %s" % source_hash(PREFILL_SOURCE))
+    if "decode" in totals:
+        print("decode_traffic_bytes_per_launch: %d" % totals["decode"])
+        print("decode_traffic_kernel_sha256: %s" % source_hash(DECODE_SOURCE))
+    return 0
 
 
 def cpu_baseline(pos_np, q_dec, kr, vr, qkv_pre):
@@ -131,7 +187,15 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-workload", action="store_true",
+                    help="run one plain copy of %d MiB, then one step, for counter collection"
+                    % (COPY_BYTES >> 20))
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="CSV",
+                    help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs of a "
+                         "--pmc-workload run into the prefill traffic summary")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        return summarize_pmc(args.summarize_pmc)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -160,8 +224,7 @@ def main():
     new_k = si.to_torch(si.normal(si.seed_for(4, 4), (c4["B"], c4["Hkv"], c4["d"]), si.BF16), dev)
     new_v = si.to_torch(si.normal(si.seed_for(4, 5), (c4["B"], c4["Hkv"], c4["d"]), si.BF16), dev)
     out_dec = torch.empty_like(q_dec)
-    ws = torch.empty(swa.decode_workspace_bytes(c4["B"], c4["Hq"], c4["W"], c4["d"]),
-                     dtype=torch.uint8, device=dev)
+    ws = swa.decode_workspace(c4["B"], c4["Hq"], c4["W"], c4["d"], dev)
     s_pre = 1.0 / math.sqrt(c3["d"])
     s_dec = 1.0 / math.sqrt(c4["d"])
 
@@ -177,6 +240,18 @@ def main():
         swa.decode(q_dec, k_ring, v_ring, pos, scale=s_dec, out=out_dec, workspace=ws)
         if ev is not None:
             ev[3].record()
+
+    if args.pmc_workload:
+        # a plain copy kernel of known size calibrates the byte counters
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        step()
+        torch.cuda.synchronize()
+        print("pmc workload done", flush=True)
+        return 0
 
     for _ in range(args.warmup):
         step()
@@ -205,7 +280,8 @@ def main():
     pre_tflops = pre_flops / (ms_pre * 1e-3) / 1e12
     dec_gbs = dec_kv_bytes / (ms_dec * 1e-3) / 1e9
 
-    traffic = read_traffic(kernel_source_hash())
+    traffic = read_traffic("", PREFILL_SOURCE)
+    dec_traffic = read_traffic("decode_", DECODE_SOURCE)
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -253,6 +329,8 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+            "traffic": dec_traffic,
+            "kernel": "decode_split_kernel<bf16, 128, 4>",
             "algorithmic_bytes_per_launch": dec_kv_bytes + dec_qo_bytes,
         },
         "wall_s_timed": round(wall, 3),

@@ -143,6 +143,12 @@ def decode_workspace_bytes(B, Hq, W, d):
     return int(load().swa_decode_workspace_bytes(int(B), int(Hq), int(W), int(d)))
 
 
+def decode_workspace(B, Hq, W, d, device="cuda"):
+    """A zero-filled decode workspace (reusable across calls without clearing)."""
+    import torch
+    return torch.zeros(max(decode_workspace_bytes(B, Hq, W, d), 16), dtype=torch.uint8, device=device)
+
+
 def decode(q, k_ring, v_ring, pos, scale=None, out=None, workspace=None, stream=None):
     """One query token per sequence against its ring; returns out [B, Hq, d]."""
     import torch
@@ -162,7 +168,7 @@ def decode(q, k_ring, v_ring, pos, scale=None, out=None, workspace=None, stream=
         scale = 1.0 / math.sqrt(d)
     need = decode_workspace_bytes(B, Hq, W, d)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = decode_workspace(B, Hq, W, d, q.device)
     st = load().swa_decode(q.data_ptr(), k_ring.data_ptr(), v_ring.data_ptr(), pos.data_ptr(),
                            out.data_ptr(), B, Hq, Hkv, W, d, float(scale), _dtype_code(q),
                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),

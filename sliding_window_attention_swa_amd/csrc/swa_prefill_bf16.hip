@@ -87,7 +87,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
                          const __bf16* __restrict__ v, __bf16* __restrict__ out, int T, int W,
                          int Hq, int Hkv, float c, uint32_t qsign, int n_qtiles) {
   using Gm = Geo<D>;
-  constexpr int ROWB = Gm::ROWB, CHUNKS = Gm::CHUNKS, TILEB = Gm::TILEB, KS = Gm::KS;
+  constexpr int ROWB = Gm::ROWB, TILEB = Gm::TILEB, KS = Gm::KS;
   constexpr int MD = Gm::MD, NLD = Gm::NLD;
   // two stages of K and V tiles, as separate objects so the compiler can tell
   // the stage being filled by direct loads from the stage being read
@@ -180,6 +180,8 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass mishandles this builtin
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(Kdst + wbase), 16, off, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(Vdst + wbase), 16, off, 0, 0, 0);
+#else
+      (void)rk, (void)rv, (void)wbase, (void)off;
 #endif
     }
   };

@@ -13,10 +13,13 @@
 // the kernel is organised for HBM bandwidth:
 //   * grid = (sequence, KV head, query-head chunk, slot split); every K/V row
 //     of a KV head is read once for all the query heads of its group;
-//   * each row is read with 16-byte loads by d/8 (bf16) consecutive lanes, so
-//     a wave load covers whole rows and is fully coalesced; four loads of K
-//     and four of V are in flight per lane;
-//   * the dot product is finished with DPP row permutations (no LDS);
+//   * each row is read with 16-byte non-temporal loads by d/8 (bf16)
+//     consecutive lanes, so a wave load covers whole rows and is fully
+//     coalesced; eight loads of K and eight of V are in flight per lane;
+//   * the ring is split into slot chunks only as far as needed to fill the
+//     GPU; with one chunk the pass writes the output itself;
+//   * q.k uses packed bf16 dot products; the sum over the lanes of a row is
+//     finished with DPP row permutations (no LDS);
 //   * every lane-row group keeps its own running maximum / sum (rescaled only
 //     when the maximum grows by more than 2^8), merged once per workgroup
 //     through LDS; a small second kernel merges the splits with the usual
@@ -32,7 +35,13 @@ constexpr float kRescaleThreshold = 8.0f;
 constexpr float kNegBig = -1.0e30f;
 constexpr int kDecodeThreads = 256;
 constexpr int kDecodeWaves = kDecodeThreads / 64;
-constexpr int kUnroll = 4;
+#ifndef SWA_DECODE_UNROLL
+#define SWA_DECODE_UNROLL 8
+#endif
+#ifndef SWA_DECODE_ITEMS
+#define SWA_DECODE_ITEMS 2048
+#endif
+constexpr int kUnroll = SWA_DECODE_UNROLL;  // K and V rows in flight per lane
 
 // ------------------------------------------------------------------ append
 
@@ -70,6 +79,14 @@ struct Elem<__bf16> {
     }
   }
   __device__ static void store(__bf16* dst, float x) { *dst = (__bf16)x; }
+  // acc + sum of the 8 products of two 16-byte rows (packed bf16 dot2)
+  __device__ static float dot(const uint4& a, const uint4& b, float acc) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, a.x), __builtin_bit_cast(b2, b.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, a.y), __builtin_bit_cast(b2, b.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, a.z), __builtin_bit_cast(b2, b.z), acc, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, a.w), __builtin_bit_cast(b2, b.w), acc, false);
+  }
 };
 template <>
 struct Elem<float> {
@@ -81,6 +98,12 @@ struct Elem<float> {
     f[3] = __uint_as_float(raw.w);
   }
   __device__ static void store(float* dst, float x) { *dst = x; }
+  __device__ static float dot(const uint4& a, const uint4& b, float acc) {
+    acc = fmaf(__uint_as_float(a.x), __uint_as_float(b.x), acc);
+    acc = fmaf(__uint_as_float(a.y), __uint_as_float(b.y), acc);
+    acc = fmaf(__uint_as_float(a.z), __uint_as_float(b.z), acc);
+    return fmaf(__uint_as_float(a.w), __uint_as_float(b.w), acc);
+  }
 };
 
 // Sum over aligned groups of N lanes (N in {4, 8, 16, 32}); every lane of the
@@ -98,14 +121,23 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// 16-byte load marked non-temporal: each ring row is read exactly once per
+// decode, so it should not displace reusable lines from the caches.
+template <typename E>
+__device__ __forceinline__ uint4 stream_load(const E* p) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
 // ------------------------------------------------------------ split pass
 
 template <typename E, int D, int NQ>
 __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     const E* __restrict__ q, const E* __restrict__ k_ring, const E* __restrict__ v_ring,
-    const int32_t* __restrict__ pos, float* __restrict__ ws_acc, float* __restrict__ ws_m,
-    float* __restrict__ ws_l, int Hq, int Hkv, int W, float scale_log2, int S, int chunk,
-    int n_hchunks) {
+    const int32_t* __restrict__ pos, E* __restrict__ out, float* __restrict__ ws_acc,
+    float* __restrict__ ws_m, float* __restrict__ ws_l, int Hq, int Hkv, int W, float scale_log2,
+    int S, int chunk, int n_hchunks) {
   constexpr int EPL = Elem<E>::PER16;  // elements per 16-byte load
   constexpr int LPR = D / EPL;         // lanes per ring row
   constexpr int RPW = 64 / LPR;        // rows per wave load
@@ -137,12 +169,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
   const int s0 = split * chunk;
   const int s1 = min(s0 + chunk, nvalid);
 
-  float qv[NQ][EPL];
+  uint4 qraw[NQ];  // this lane's EPL query elements of each head, as stored
 #pragma unroll
-  for (int hq = 0; hq < NQ; ++hq) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + h0 + hq) * D + li * EPL);
-    Elem<E>::widen(raw, qv[hq]);
-  }
+  for (int hq = 0; hq < NQ; ++hq)
+    qraw[hq] = *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + h0 + hq) * D + li * EPL);
   float m[NQ], l[NQ], acc[NQ][EPL];
 #pragma unroll
   for (int hq = 0; hq < NQ; ++hq) {
@@ -164,8 +194,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
       const int r = base + (u * kDecodeWaves + wave) * RPW + rg;
       valid[u] = r < s1;
       if (valid[u]) {
-        kraw[u] = *reinterpret_cast<const uint4*>(kb + (size_t)r * D);
-        vraw[u] = *reinterpret_cast<const uint4*>(vb + (size_t)r * D);
+        kraw[u] = stream_load(kb + (size_t)r * D);
+        vraw[u] = stream_load(vb + (size_t)r * D);
       } else {
         kraw[u] = make_uint4(0, 0, 0, 0);
         vraw[u] = make_uint4(0, 0, 0, 0);
@@ -174,15 +204,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     float sc[kUnroll][NQ];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      float kf[EPL];
-      Elem<E>::widen(kraw[u], kf);
 #pragma unroll
-      for (int hq = 0; hq < NQ; ++hq) {
-        float s = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) s = fmaf(qv[hq][e], kf[e], s);
-        sc[u][hq] = s;
-      }
+      for (int hq = 0; hq < NQ; ++hq) sc[u][hq] = Elem<E>::dot(kraw[u], qraw[hq], 0.f);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -242,6 +265,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
       a = fmaf(w, sm_acc[hq][s][dim], a);
       L = fmaf(w, sm_l[hq][s], L);
     }
+    if (S == 1) {  // no other split to merge with: finish here
+      Elem<E>::store(out + ((size_t)b * Hq + h0 + hq) * D + dim, L > 0.f ? a / L : 0.f);
+      continue;
+    }
     const size_t slot = ((size_t)b * Hq + h0 + hq) * S + split;
     ws_acc[slot * D + dim] = a;
     if (dim == 0) {
@@ -288,10 +315,10 @@ hipError_t launch_decode_t(const void* q, const void* k_ring, const void* v_ring
   const long long nwg = (long long)B * Hkv * n_hchunks * S;
   hipLaunchKernelGGL((decode_split_kernel<E, D, NQ>), dim3((unsigned)nwg), dim3(kDecodeThreads), 0,
                      stream, static_cast<const E*>(q), static_cast<const E*>(k_ring),
-                     static_cast<const E*>(v_ring), pos, ws_acc, ws_m, ws_l, Hq, Hkv, W,
-                     scale * kLog2e, S, chunk, n_hchunks);
+                     static_cast<const E*>(v_ring), pos, static_cast<E*>(out), ws_acc, ws_m, ws_l,
+                     Hq, Hkv, W, scale * kLog2e, S, chunk, n_hchunks);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || S == 1) return e;
   hipLaunchKernelGGL((decode_combine_kernel<E, D>), dim3((unsigned)((size_t)B * Hq)), dim3(D), 0,
                      stream, ws_acc, ws_m, ws_l, static_cast<E*>(out), S);
   return hipGetLastError();
@@ -334,10 +361,11 @@ hipError_t launch_append(void* k_ring, void* v_ring, const int32_t* pos, const v
 }
 
 int decode_splits(int B, int Hq, int W) {
-  // Aim for ~16K (sequence, query head, split) items so the split pass fills
-  // the 256 CUs several times over, but never split below 64 slots.
+  // Split each ring only as far as needed for ~SWA_DECODE_ITEMS (sequence,
+  // query head, split) items, enough work to fill the 256 CUs; a single
+  // split needs no merge pass.  Never split below 64 slots.
   const long long heads = (long long)B * Hq;
-  long long want = (16384 + heads - 1) / heads;
+  long long want = (SWA_DECODE_ITEMS + heads - 1) / heads;
   if (want < 1) want = 1;
   const long long cap = (W + 63) / 64;
   return (int)(want < cap ? want : cap);

@@ -152,3 +152,18 @@ def test_decode_deterministic(swa):
     b = swa.decode(*args)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_workspace_reused_across_calls_and_shapes(swa):
+    """One zero-filled workspace serves consecutive calls of different sizes
+    (the arrival counters return to zero after every call)."""
+    ws = swa.decode_workspace(8, 32, 4096, 128)
+    for B, W in [(8, 4096), (3, 1000), (8, 4096), (1, 64)]:
+        q, kr, vr, pos = si.decode_inputs(4, B=B, W=W, pos_lo=W // 2, pos_hi=3 * W)
+        args = (to_device(q), to_device(kr), to_device(vr), torch.from_numpy(pos).cuda())
+        reused = swa.decode(*args, workspace=ws)
+        fresh = swa.decode(*args)
+        torch.cuda.synchronize()
+        assert torch.equal(reused, fresh), (B, W)
+        ref = oracle.decode(q.values, kr.values, vr.values, pos, 1 / math.sqrt(128))
+        assert_parity(to_f64(reused), ref, "bf16", "reused workspace B=%d W=%d" % (B, W))
