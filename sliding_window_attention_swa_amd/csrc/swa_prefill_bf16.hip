@@ -256,7 +256,14 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   // raise the reference maximum where a row grew by more than 2^8; rescale
   // the accumulators and return true when any row of the wave did
   auto raise_max = [&](float mx) __attribute__((always_inline)) -> bool {
-    mx = fmaxf(mx, __shfl_xor(mx, 32));  // lanes l and l^32 hold the same row
+    {  // lanes l and l^32 hold the same row; exchange without an LDS round trip
+      uint32_t a = __float_as_uint(mx), b = a;
+#if defined(__HIP_DEVICE_COMPILE__)
+      __asm__ volatile("" : "+v"(b));  // opaque copy: the swap must not be folded
+#endif
+      const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+      mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
     const bool grow = mx > m_ref + grow_raw;
     if (!__ballot(grow)) return false;
     const float m_new = grow ? mx : m_ref;
