@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import swa_inputs as si
-from helpers import assert_parity, to_device, to_f64
+from helpers import FP32_MAX_ABS, assert_parity, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -61,6 +61,16 @@ SMALL = [
     (1, 513, 512, 1, 2, 2, 64),
     (1, 300, 2000, 1, 2, 1, 128),
     (1, 1000, 1, 1, 1, 1, 32),
+    # window and sequence edges on tile boundaries (64-key tiles, 128-row
+    # blocks): W = one tile and one tile + 1, symmetric half-windows of
+    # exactly 32 and 64 keys, T a multiple of the block and one past it; rows
+    # whose first visited tile is fully masked (causal W = 8)
+    (0, 256, 64, 1, 2, 1, 128),
+    (0, 257, 65, 1, 2, 2, 64),
+    (0, 256, 8, 1, 2, 1, 32),
+    (1, 256, 64, 1, 2, 1, 128),
+    (1, 129, 128, 1, 2, 2, 64),
+    (1, 384, 129, 1, 2, 1, 32),
 ]
 
 
@@ -111,6 +121,22 @@ def test_locality_bit_exact(swa, dtype):
     torch.cuda.synchronize()
     assert torch.equal(pert[:, :, r0:r1], base[:, :, r0:r1])
     assert not torch.equal(pert[:, :, r1:], base[:, :, r1:])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mode,T,W,d", [(0, 300, 100, 128), (1, 200, 33, 64), (0, 130, 5, 32)])
+def test_constant_values_give_constant_output(swa, dtype, mode, T, W, d):
+    """Weights sum to one: if every V row is the same vector c, every output
+    row is c: within one bf16 unit in the last place for bf16 output, within
+    the fp32 parity tolerance (accumulation order) for fp32."""
+    q, k, _ = small_inputs(700 + T, 1, 4, 2, T, d, dtype)
+    c = si.normal(777, (d,), dtype)
+    v = si.Tensor(np.broadcast_to(c.values, (1, 2, T, d)).copy(),
+                  np.broadcast_to(c.bits, (1, 2, T, d)).copy(), c.dtype)
+    got = to_f64(run(swa, q, k, v, W, mode))
+    want = np.broadcast_to(c.values.astype(np.float64), got.shape)
+    tol = 2.0 ** -8 * np.abs(want) + 1e-30 if dtype == "bf16" else FP32_MAX_ABS
+    assert np.all(np.abs(got - want) <= tol), float(np.max(np.abs(got - want)))
 
 
 def test_deterministic(swa):
