@@ -17,6 +17,8 @@ HIP events around its own launches; `roofline` describes the dominant kernel
 bounded sample of the same work.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+       python bench.py --all-configs   (every configuration vs its roofline, warm and
+                                        flushed; not the benchmark line)
 """
 
 import argparse
@@ -181,6 +183,79 @@ def cpu_baseline(pos_np, q_dec, kr, vr, qkv_pre):
     }
 
 
+def band_pairs(T, W, mode):
+    """(query, key) pairs inside the windows of one head, either mode."""
+    if mode == 0:
+        return band_pairs_causal(T, W)
+    h = W // 2
+    i = np.arange(T, dtype=np.int64)
+    return int((np.minimum(T - 1, i + h) - np.maximum(0, i - h) + 1).sum())
+
+
+def all_configs(reps):
+    """Every configuration's kernel time, cache-warm (same inputs every
+    repetition) and flushed (a 1 GiB write between repetitions evicts the L2s
+    and the Infinity Cache), against its binding roofline.  One JSON line per
+    configuration."""
+    import torch
+    import sliding_window_attention_swa_amd as swa
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    swa.load()
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+
+    def timed(fn, flushed):
+        times = []
+        for r in range(reps + 3):
+            if flushed:
+                flush.fill_(float(r))
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            if r >= 3:
+                times.append(a.elapsed_time(b))
+        return float(np.median(times))
+
+    for wl in (2, 3, 5):
+        c = si.WORKLOADS[wl]
+        q, k, v = (si.to_torch(t, dev) for t in si.prefill_inputs(wl))
+        out = torch.empty_like(q)
+        scale = 1.0 / math.sqrt(c["d"])
+        fn = lambda: swa.prefill(q, k, v, c["W"], mode=c["mode"], scale=scale, out=out)  # noqa: E731
+        flops = 4 * c["d"] * band_pairs(c["T"], c["W"], c["mode"]) * c["Hq"] * c["B"]
+        bytes_ = 2 * c["T"] * c["d"] * c["B"] * (2 * c["Hq"] + 2 * c["Hkv"])
+        t_roof = max(flops / (PEAK_BF16_TFLOPS * 1e12), bytes_ / (PEAK_HBM_GBS * 1e9)) * 1e3
+        bound = "mfma" if flops / PEAK_BF16_TFLOPS / 1e12 >= bytes_ / PEAK_HBM_GBS / 1e9 else "hbm"
+        row = {"config": c["name"], "kernel": "prefill", "bound": bound,
+               "roofline_ms": round(t_roof, 5)}
+        for tag, fl in (("warm", False), ("flushed", True)):
+            ms = timed(fn, fl)
+            row[tag] = {"ms": round(ms, 5), "tflops": round(flops / ms / 1e9, 1),
+                        "gbs": round(bytes_ / ms / 1e6, 1), "frac_roofline": round(t_roof / ms, 3)}
+        print(json.dumps(row), flush=True)
+        del q, k, v, out
+
+    c = si.WORKLOADS[4]
+    q_np, kr_np, vr_np, pos_np = si.decode_inputs(4)
+    q, kr, vr = (si.to_torch(t, dev) for t in (q_np, kr_np, vr_np))
+    pos = torch.from_numpy(pos_np).to(dev)
+    out = torch.empty_like(q)
+    ws = swa.decode_workspace(c["B"], c["Hq"], c["W"], c["d"], dev)
+    fn = lambda: swa.decode(q, kr, vr, pos, scale=1.0 / math.sqrt(c["d"]), out=out, workspace=ws)  # noqa: E731
+    _, kv_bytes, qo_bytes = decode_work(pos_np)
+    t_roof = (kv_bytes + qo_bytes) / (PEAK_HBM_GBS * 1e9) * 1e3
+    row = {"config": c["name"], "kernel": "decode", "bound": "hbm", "roofline_ms": round(t_roof, 5)}
+    for tag, fl in (("warm", False), ("flushed", True)):
+        ms = timed(fn, fl)
+        row[tag] = {"ms": round(ms, 5), "kv_gbs": round(kv_bytes / ms / 1e6, 1),
+                    "frac_roofline": round(t_roof / ms, 3)}
+    print(json.dumps(row), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,9 +268,14 @@ def main():
     ap.add_argument("--summarize-pmc", nargs="+", metavar="CSV",
                     help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs of a "
                          "--pmc-workload run into the prefill traffic summary")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="instead of the benchmark line: every configuration, cache-warm and "
+                         "flushed, against its roofline (one JSON line each)")
     args = ap.parse_args()
     if args.summarize_pmc:
         return summarize_pmc(args.summarize_pmc)
+    if args.all_configs:
+        return all_configs(max(args.steps, 20))
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -7,10 +7,13 @@
 // symmetric window |i-j| <= floor(W/2), both clipped to [0, T).
 //
 // Work decomposition: one workgroup = 128 query rows of one query head, four
-// waves of 32 rows; two workgroups per CU (two waves per SIMD, so one wave's
-// softmax can overlap the other's matrix products).  Key/value tiles of 64
-// rows are visited only where they intersect the union of the block's
-// windows, so the work is O(T * W * d) and no [T, T] matrix exists.
+// waves of 32 rows; two workgroups per CU at d = 128 (register-bound), three
+// at d = 64, five at d = 32, so that the tile loads and barriers of one
+// workgroup hide behind the work of the others.  (Softmax and matrix
+// products overlap only within a wave, hence the mixed regions below.)
+// Key/value tiles of 64 rows are visited only where they intersect the union
+// of the block's windows, so the work is O(T * W * d) and no [T, T] matrix
+// exists.
 //
 // Per tile:
 //   S^T = K Q^T   v_mfma_f32_32x32x16_bf16 with the K tile (LDS) as the A
@@ -81,8 +84,15 @@ __device__ __forceinline__ int swz(int row) {
   return (row >> 2) & 3;
 }
 
+// Occupancy target (waves per SIMD): d = 128 needs the registers of two
+// waves; smaller heads fit more, which hides the tile-load latency of short
+// windows.
+template <int D>
+constexpr int kWavesPerSimd = D == 128 ? 2 : (D == 64 ? 3 : 5);
+
 template <int D, int MODE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>, kWavesPerSimd<D>)))
 void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                          const __bf16* __restrict__ v, __bf16* __restrict__ out, int T, int W,
                          int Hq, int Hkv, float c, uint32_t qsign, int n_qtiles) {
