@@ -463,6 +463,206 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   }
 }
 
+// ---------------------------------------------------------------------------
+// Short windows.  When every window of 32 consecutive rows fits the 64 keys
+// starting kOff keys before the first of them (causal W <= 33: kOff = 32;
+// symmetric floor(W/2) <= 16: kOff = 16), one wave computes its 32 rows from
+// one key block of its own: a workgroup is a single wave (no barriers, no
+// idle waves), the softmax is exact in two passes over the block (maximum,
+// then exponentials), and there is no online rescaling.  Same score layout,
+// operand reads and LDS swizzle as the tiled kernel above.
+template <int MODE>
+constexpr int kShortOff = MODE == 0 ? 32 : 16;
+
+bool short_window(int W, int mode) { return mode == 0 ? W <= 33 : (W >> 1) <= 16; }
+
+template <int D, int MODE>
+__global__ __launch_bounds__(64) void prefill_short_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    __bf16* __restrict__ out, int T, int W, int Hq, int Hkv, float c, uint32_t qsign,
+    int n_wtiles) {
+  using Gm = Geo<D>;
+  constexpr int ROWB = Gm::ROWB, KS = Gm::KS, MD = Gm::MD;
+  constexpr int BLOCKB = 64 * ROWB;      // 64 key rows
+  constexpr int NL = BLOCKB / (64 * 16);  // direct loads per lane per block
+  __shared__ __attribute__((aligned(1024))) char lds_k[BLOCKB];
+  __shared__ __attribute__((aligned(1024))) char lds_v[BLOCKB];
+
+  const int G = Hq / Hkv;
+  int id = blockIdx.x;
+  const int nwg = gridDim.x;
+  if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
+  const int hg = id % G;
+  const int rest = id / G;
+  const int wt = rest % n_wtiles;
+  const int kvh = rest / n_wtiles;
+  const int h = kvh * G + hg;
+
+  const int lane = threadIdx.x;
+  const int half = lane >> 5;
+  const int qw0 = wt * 32;
+  const int qi = qw0 + (lane & 31);
+  const int kb0 = qw0 - kShortOff<MODE>;  // key of LDS row 0 (may be negative)
+
+  const __bf16* qh = q + (size_t)h * T * D;
+  const __bf16* kh = k + (size_t)kvh * T * D;
+  const __bf16* vh = v + (size_t)kvh * T * D;
+
+  // ---- the key block, rows clamped into [0, T) (out-of-range rows hold
+  // finite data and are masked below); load j of a lane fills LDS bytes
+  // [(64*j + lane)*16, +16)
+  {
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)kh, 0, T * ROWB, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)vh, 0, T * ROWB, kBufferFlags);
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int o = (64 * j + lane) * 16;
+      const int row = o / ROWB;
+      const int src = min(max(kb0 + row, 0), T - 1);
+      const int off = src * ROWB + ((((o % ROWB) / 16) ^ swz<D>(row)) * 16);
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass mishandles this builtin
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(lds_k + 64 * j * 16), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(lds_v + 64 * j * 16), 16, off, 0, 0, 0);
+#else
+      (void)rk, (void)rv, (void)off;
+#endif
+    }
+  }
+  // ---- Q rows as B operands (sign of a negative scale folded in)
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    uint4 r = make_uint4(0, 0, 0, 0);
+    if (qi < T) r = *reinterpret_cast<const uint4*>(qh + (size_t)qi * D + ks * 16 + half * 8);
+    r.x ^= qsign;
+    r.y ^= qsign;
+    r.z ^= qsign;
+    r.w ^= qsign;
+    qf[ks] = __builtin_bit_cast(bf16x8, r);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the block is in LDS (one wave: no barrier)
+
+  // ---- S^T = K Q^T for the 64 keys (two 32-key blocks), masked
+  const int kr = lane & 31;
+  const int kf = swz<D>(kr);
+  f32x16 s[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    s[mb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+          lds_k + (mb * 32 + kr) * ROWB + (((2 * ks + half) ^ kf) * 16));
+      s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[mb], 0, 0, 0);
+    }
+  }
+  const int hw = W >> 1;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kb0 + mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+      const int diff = qi - key;
+      bool ok = key >= 0 && key < T;
+      if (MODE == 0) {
+        ok = ok && diff >= 0 && diff < W;
+      } else {
+        ok = ok && diff >= -hw && diff <= hw;
+      }
+      if (!ok) s[mb][r] = -INFINITY;
+      mx = fmaxf(mx, s[mb][r]);
+    }
+  }
+  // lanes l and l^32 hold the same row: exchange without an LDS round trip
+  auto pair_max = [](float x) __attribute__((always_inline)) -> float {
+    uint32_t a = __float_as_uint(x), b = a;
+#if defined(__HIP_DEVICE_COMPILE__)
+    __asm__ volatile("" : "+v"(b));  // opaque copy: the swap must not be folded
+#endif
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  };
+  mx = pair_max(mx);
+  // a row past T has no valid key: keep its (unstored) arithmetic finite
+  if (mx == -INFINITY) mx = 0.f;
+
+  // ---- probabilities (bf16, as the product uses them) and their sum
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  const float mc = -mx * c;
+  bf16x8 p[4];
+  float l = 0.f;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[mb][8 * k2 + 2 * e], c, mc));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[mb][8 * k2 + 2 * e + 1], c, mc));
+        w[e] = pack_bf16x2(p0, p1);
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[e]), ones, l, false);
+      }
+      p[2 * mb + k2] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+  l += __shfl_xor(l, 32);
+
+  // ---- O^T = V^T P^T over the 64 keys (transposing LDS reads, as above)
+  const int tr_s = lane & 15, tr_g = lane >> 4;
+  const int tr_row = 4 * (tr_g >> 1) + (tr_s >> 2);
+  const int tr_c0 = 2 * (tr_g & 1) + ((tr_s & 3) >> 1);
+  const int tr_flo = swz<D>(tr_row), tr_fhi = swz<D>(tr_row + 8);
+  f32x16 o[MD];
+#pragma unroll
+  for (int md = 0; md < MD; ++md) {
+    o[md] = f32x16{};
+    const int vlo = tr_row * ROWB + (((4 * md + tr_c0) ^ tr_flo) * 16) + (tr_s & 1) * 8;
+    const int vhi = (tr_row + 8) * ROWB + (((4 * md + tr_c0) ^ tr_fhi) * 16) + (tr_s & 1) * 8;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const char* src = lds_v + kk * 16 * ROWB;
+      const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + vlo));
+      const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + vhi));
+      const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+      o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[kk], o[md], 0, 0, 0);
+    }
+  }
+
+  // ---- divide by the row sum, round to bf16, store
+  if (qi < T) {
+    const float inv = 1.0f / l;
+    __bf16* orow = out + ((size_t)h * T + qi) * D;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int dim = 32 * md + 8 * rq + 4 * half;
+        uint2 w;
+        w.x = pack_bf16x2(o[md][4 * rq + 0] * inv, o[md][4 * rq + 1] * inv);
+        w.y = pack_bf16x2(o[md][4 * rq + 2] * inv, o[md][4 * rq + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + dim) = w;
+      }
+    }
+  }
+}
+
+template <int D, int MODE>
+hipError_t launch_short(const void* q, const void* k, const void* v, void* out, int T, int W,
+                        int Hq, int Hkv, float c, uint32_t qsign, hipStream_t stream) {
+  const int n_wtiles = (T + 31) / 32;
+  const long long nwg = (long long)n_wtiles * Hq;
+  hipLaunchKernelGGL((prefill_short_kernel<D, MODE>), dim3((unsigned)nwg), dim3(64), 0, stream,
+                     static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+                     static_cast<const __bf16*>(v), static_cast<__bf16*>(out), T, W, Hq, Hkv, c,
+                     qsign, n_wtiles);
+  return hipGetLastError();
+}
+
 template <int D, int MODE>
 hipError_t launch(const void* q, const void* k, const void* v, void* out, int T, int W, int Hq,
                   int Hkv, float scale, hipStream_t stream) {
@@ -475,6 +675,7 @@ hipError_t launch(const void* q, const void* k, const void* v, void* out, int T,
     qsign = 0x80008000u;
   }
   if (c == 0.f) c = 1.0e-30f;  // all weights equal; masked logits stay at -inf
+  if (short_window(W, MODE)) return launch_short<D, MODE>(q, k, v, out, T, W, Hq, Hkv, c, qsign, stream);
   hipLaunchKernelGGL((prefill_bf16_kernel<D, MODE>), dim3((unsigned)nwg), dim3(kThreads), 0,
                      stream, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                      static_cast<const __bf16*>(v), static_cast<__bf16*>(out), T, W, Hq, Hkv, c,
