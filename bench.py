@@ -206,18 +206,18 @@ def all_configs(reps):
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
 
     def timed(fn, flushed):
-        times = []
-        for r in range(reps + 3):
+        # every repetition is enqueued before the one host synchronisation, so
+        # the device never idles between them; events bracket the kernel alone
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps + 3)]
+        for r, (a, b) in enumerate(ev):
             if flushed:
                 flush.fill_(float(r))
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             fn()
             b.record()
-            torch.cuda.synchronize()
-            if r >= 3:
-                times.append(a.elapsed_time(b))
-        return float(np.median(times))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev[3:]]))
 
     for wl in (2, 3, 5):
         c = si.WORKLOADS[wl]

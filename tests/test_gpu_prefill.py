@@ -71,6 +71,14 @@ SMALL = [
     (1, 256, 64, 1, 2, 1, 128),
     (1, 129, 128, 1, 2, 2, 64),
     (1, 384, 129, 1, 2, 1, 32),
+    # either side of the short-window kernel's range (causal W <= 33,
+    # symmetric floor(W/2) <= 16: one 64-key block per 32 rows)
+    (0, 300, 33, 2, 4, 2, 64),
+    (0, 300, 34, 1, 2, 1, 32),
+    (0, 33, 33, 1, 2, 1, 128),
+    (1, 97, 33, 1, 2, 2, 32),
+    (1, 300, 34, 1, 2, 1, 128),
+    (1, 300, 35, 1, 4, 2, 64),
 ]
 
 
