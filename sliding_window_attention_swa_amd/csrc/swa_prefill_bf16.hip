@@ -22,12 +22,15 @@
 //                 exchange between lanes l and l^32.
 //   softmax       fp32, scores kept raw: p = exp2(s*c - m*c) with
 //                 c = scale*log2(e) folded into one FMA.  The reference
-//                 maximum m is raised lazily, only when a row maximum grows by
-//                 more than 2^8, so the accumulators are rarely rescaled
-//                 (exponents stay <= 2^8; only rounding changes).  The row sum
-//                 adds the bf16-rounded probabilities the product uses (packed
-//                 dot2).  The mask is applied only on tiles crossing a window
-//                 edge or the end of the sequence.
+//                 maximum m is raised lazily, only when a probability against
+//                 it reaches 2^28 (detected from the block's partial sums, so
+//                 no per-score maximum is needed on the common path); the
+//                 accumulators are then rescaled and the block recomputed.
+//                 Larger-than-one probabilities cost no precision (bf16 and
+//                 fp32 are relative-precision formats) and stay far from
+//                 overflow.  The row sum adds the bf16-rounded probabilities
+//                 the product uses (packed dot2).  The mask is applied only on
+//                 tiles crossing a window edge or the end of the sequence.
 //   O^T += V^T P^T  P (bf16, straight from the score registers) is the B
 //                 operand; V^T comes from the natural [key][dim] LDS tile
 //                 through the transposing LDS read (ds_read_b64_tr_b16).
@@ -51,7 +54,12 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;   // query rows per workgroup
 constexpr int kBN = 64;            // key rows per tile
-constexpr float kGrowLog2 = 8.0f;  // rescale when a row maximum grows by > 2^8
+// A row's accumulators are rescaled only when one of its probabilities
+// against the current reference maximum reaches 2^28 (a lane's partial block
+// sum reaches 2^32): until then every product term stays far from overflow
+// and the exponent headroom costs no precision (bf16 and fp32 keep their
+// relative precision at any scale).
+constexpr float kBigSum = 4294967296.0f;
 constexpr float kNoMax = -1.0e30f;
 constexpr int kBufferFlags = 0x00020000;  // raw 32-bit buffer access
 
@@ -224,7 +232,6 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   for (int md = 0; md < MD; ++md) o[md] = f32x16{};
   float m_ref = kNoMax;  // raw-score reference maximum of this lane's row
   float l_part = 0.f;    // this lane's share of the row sum
-  const float grow_raw = kGrowLog2 / c;
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // ---- tile building blocks
@@ -244,11 +251,8 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   // probabilities of one 32-key half against the current reference maximum,
-  // packed as two bf16 B operands, with their (rounded) sum and the raw max
-  auto probs = [&](const f32x16& s, float mc, bf16x8* p, float& lsum, float& mx) __attribute__((always_inline)) {
-    mx = fmaxf(s[0], s[1]);
-#pragma unroll
-    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
+  // packed as two bf16 B operands, with their (rounded) sum
+  auto probs = [&](const f32x16& s, float mc, bf16x8* p, float& lsum) __attribute__((always_inline)) {
     lsum = 0.f;
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
@@ -263,9 +267,17 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
       p[k2] = __builtin_bit_cast(bf16x8, w);
     }
   };
-  // raise the reference maximum where a row grew by more than 2^8; rescale
-  // the accumulators and return true when any row of the wave did
-  auto raise_max = [&](float mx) __attribute__((always_inline)) -> bool {
+  // When a block's probabilities grew too large for some row (partial sum
+  // >= 2^32; also the first visited block, whose reference maximum is
+  // -1e30), raise the reference maximum of every row whose block maximum
+  // exceeds it and rescale the accumulators; the caller recomputes the block.
+  // Returns true when anything was rescaled.
+  auto raise_max = [&](const f32x16* sb, int nb, float lsum) __attribute__((always_inline)) -> bool {
+    if (!__ballot(lsum >= kBigSum)) return false;
+    float mx = -INFINITY;
+    for (int b = 0; b < nb; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sb[b][r]);
     {  // lanes l and l^32 hold the same row; exchange without an LDS round trip
       uint32_t a = __float_as_uint(mx), b = a;
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -274,8 +286,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
       const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
       mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
     }
-    const bool grow = mx > m_ref + grow_raw;
-    if (!__ballot(grow)) return false;
+    const bool grow = mx > m_ref;
     const float m_new = grow ? mx : m_ref;
     const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * c);
     m_ref = m_new;
@@ -290,11 +301,11 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
 
   // opaque use: makes the speculative probabilities exist at this point, so
   // they are computed inside the overlap region rather than sunk into a branch
-  auto pin = [&](bf16x8* p, float& l, float& m) __attribute__((always_inline)) {
+  auto pin = [&](bf16x8* p, float& l) __attribute__((always_inline)) {
     uint4 w0 = __builtin_bit_cast(uint4, p[0]), w1 = __builtin_bit_cast(uint4, p[1]);
 #if defined(__HIP_DEVICE_COMPILE__)  // register constraints exist only for the GPU pass
     __asm__ volatile("" : "+v"(w0.x), "+v"(w0.y), "+v"(w0.z), "+v"(w0.w));
-    __asm__ volatile("" : "+v"(w1.x), "+v"(w1.y), "+v"(w1.z), "+v"(w1.w), "+v"(l), "+v"(m));
+    __asm__ volatile("" : "+v"(w1.x), "+v"(w1.y), "+v"(w1.z), "+v"(w1.w), "+v"(l));
 #endif
     p[0] = __builtin_bit_cast(bf16x8, w0);
     p[1] = __builtin_bit_cast(bf16x8, w1);
@@ -321,14 +332,14 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
 
     // region A: S for keys 32..63 | probabilities of keys 0..31
     bf16x8 p0[2], p1[2];
-    float l0, l1, mx0, mx1;
+    float l0, l1;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) ka[ks] = kread(Ks, 1, ks);
     f32x16 s1 = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], s1, 0, 0, 0);
-    probs(s0, -m_ref * c, p0, l0, mx0);
-    pin(p0, l0, mx0);
+    probs(s0, -m_ref * c, p0, l0);
+    pin(p0, l0);
     __builtin_amdgcn_sched_group_barrier(0x100, KS / 2, 0);
 #pragma unroll
     for (int i = 0; i < KS; ++i) {
@@ -337,7 +348,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
       if (i < KS / 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (raise_max(mx0)) probs(s0, -m_ref * c, p0, l0, mx0);
+    if (raise_max(&s0, 1, l0)) probs(s0, -m_ref * c, p0, l0);
     l_part += l0;
 
     // region B: O += V P for keys 0..31 | probabilities of keys 32..63
@@ -346,8 +357,8 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(Vs, md, kk), p0[kk], o[md], 0, 0, 0);
     }
-    probs(s1, -m_ref * c, p1, l1, mx1);
-    pin(p1, l1, mx1);
+    probs(s1, -m_ref * c, p1, l1);
+    pin(p1, l1);
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int i = 0; i < 2 * MD; ++i) {
@@ -356,7 +367,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
       if (i < 2 * MD - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (raise_max(mx1)) probs(s1, -m_ref * c, p1, l1, mx1);
+    if (raise_max(&s1, 1, l1)) probs(s1, -m_ref * c, p1, l1);
     l_part += l1;
 
     // region C: O += V P for keys 32..63
@@ -400,12 +411,12 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
       }
     }
     bf16x8 p[4];
-    float l0, l1, mx0, mx1;
-    probs(s[0], -m_ref * c, p, l0, mx0);
-    probs(s[1], -m_ref * c, p + 2, l1, mx1);
-    if (raise_max(fmaxf(mx0, mx1))) {
-      probs(s[0], -m_ref * c, p, l0, mx0);
-      probs(s[1], -m_ref * c, p + 2, l1, mx1);
+    float l0, l1;
+    probs(s[0], -m_ref * c, p, l0);
+    probs(s[1], -m_ref * c, p + 2, l1);
+    if (raise_max(s, 2, fmaxf(l0, l1))) {
+      probs(s[0], -m_ref * c, p, l0);
+      probs(s[1], -m_ref * c, p + 2, l1);
     }
     l_part += l0 + l1;
 #pragma unroll

@@ -147,6 +147,33 @@ def test_constant_values_give_constant_output(swa, dtype, mode, T, W, d):
     assert np.all(np.abs(got - want) <= tol), float(np.max(np.abs(got - want)))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("scale", [3.0, -4.0])
+@pytest.mark.parametrize("mode,T,W,d", [(0, 700, 600, 128), (1, 600, 500, 64), (0, 400, 250, 32)])
+def test_large_scores_force_rescaling(swa, dtype, scale, mode, T, W, d):
+    """Scores with a standard deviation of 3-4 sqrt(d) (near one-hot softmax):
+    row maxima keep growing by far more than the accumulators' headroom from
+    tile to tile, so the rescaling path runs again and again."""
+    print("large scores", dtype, scale, mode, T, W, d, flush=True)
+    q, k, v = small_inputs(900 + T + d, 1, 2, 1, T, d, dtype)
+    got = to_f64(run(swa, q, k, v, W, mode, scale=scale))
+    ref = oracle.attention_dense(q.values, k.values, v.values, W, mode, scale)
+    if dtype == "bf16":
+        assert_parity(got, ref, dtype, "large scores scale=%g mode=%d d=%d" % (scale, mode, d))
+        return
+    # fp32: the exponent s*c - m*c (c = scale*log2 e) is formed in fp32 from
+    # terms as large as max|s*c|, so each probability carries a relative error
+    # up to about max|s*c| * 2^-23; the output error is bounded by that times
+    # max|v| (first order, both signs of the difference)
+    sc = np.abs(np.einsum("bhid,bhjd->bhij", q.values.astype(np.float64),
+                          np.repeat(k.values, 2, axis=1).astype(np.float64))).max()
+    sc *= abs(scale) / np.log(2.0)
+    tol = max(FP32_MAX_ABS, 2.0 * sc * 2.0 ** -23 * np.abs(v.values).max())
+    assert np.all(np.isfinite(got))
+    err = float(np.max(np.abs(got - ref)))
+    assert err <= tol, "large scores fp32: max-abs %.3g > derived bound %.3g" % (err, tol)
+
+
 def test_deterministic(swa):
     q, k, v = small_inputs(12, 1, 8, 2, 1000, 128, "bf16")
     a = run(swa, q, k, v, 300, 0)
