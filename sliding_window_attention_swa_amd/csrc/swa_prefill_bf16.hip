@@ -65,13 +65,11 @@ constexpr int kBufferFlags = 0x00020000;  // raw 32-bit buffer access
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 template <int D>
 struct Geo {
   static constexpr int ROWB = D * 2;              // bytes per K/V row in LDS
-  static constexpr int CHUNKS = D / 8;            // 16-byte chunks per row
   static constexpr int TILEB = kBN * ROWB;        // bytes per tile
   static constexpr int KS = D / 16;               // k-steps of S = K Q^T
   static constexpr int MD = D / 32;               // 32-dim output blocks
@@ -278,14 +276,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     for (int b = 0; b < nb; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sb[b][r]);
-    {  // lanes l and l^32 hold the same row; exchange without an LDS round trip
-      uint32_t a = __float_as_uint(mx), b = a;
-#if defined(__HIP_DEVICE_COMPILE__)
-      __asm__ volatile("" : "+v"(b));  // opaque copy: the swap must not be folded
-#endif
-      const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
-      mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-    }
+    mx = max_lane_pair(mx);  // lanes l and l^32 hold the same row
     const bool grow = mx > m_ref;
     const float m_new = grow ? mx : m_ref;
     const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * c);
@@ -587,16 +578,7 @@ __global__ __launch_bounds__(64) void prefill_short_kernel(
       mx = fmaxf(mx, s[mb][r]);
     }
   }
-  // lanes l and l^32 hold the same row: exchange without an LDS round trip
-  auto pair_max = [](float x) __attribute__((always_inline)) -> float {
-    uint32_t a = __float_as_uint(x), b = a;
-#if defined(__HIP_DEVICE_COMPILE__)
-    __asm__ volatile("" : "+v"(b));  // opaque copy: the swap must not be folded
-#endif
-    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  };
-  mx = pair_max(mx);
+  mx = max_lane_pair(mx);  // lanes l and l^32 hold the same row
   // a row past T has no valid key: keep its (unstored) arithmetic finite
   if (mx == -INFINITY) mx = 0.f;
 
