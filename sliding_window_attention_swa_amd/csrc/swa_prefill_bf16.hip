@@ -308,7 +308,11 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   //   B: O += V P for keys 0..31 | probabilities of keys 32..63
   //   C: O += V P for keys 32..63
   // Probabilities are computed against the current reference maximum; the
-  // rare tile that raises it recomputes them after the rescale.
+  // rare tile that raises it recomputes them after the rescale.  A wave in
+  // regions A and B issues at raised priority, so on a SIMD shared by two
+  // waves the one with vector work to interleave goes first and the other's
+  // matrix-only work fills the gaps (measured about 1% faster than equal
+  // priority).
   auto interior_tile = [&](const char* Ks, const char* Vs) __attribute__((always_inline)) {
     // S for keys 0..31: all K operands requested up front
     bf16x8 ka[KS];
@@ -322,6 +326,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     __builtin_amdgcn_sched_barrier(0);
 
     // region A: S for keys 32..63 | probabilities of keys 0..31
+    __builtin_amdgcn_s_setprio(3);
     bf16x8 p0[2], p1[2];
     float l0, l1;
 #pragma unroll
@@ -362,6 +367,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     l_part += l1;
 
     // region C: O += V P for keys 32..63
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int md = 0; md < MD; ++md) {
 #pragma unroll
