@@ -29,4 +29,6 @@ from .swa_ref import (  # noqa: F401
     attention_rows,
     ring_append,
     decode,
+    ring_append_chunk,
+    prefill_chunk,
 )

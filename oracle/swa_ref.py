@@ -37,7 +37,12 @@ Readings of points the pages leave open (each also listed in the design doc):
   * scale is an argument (the workloads use 1/sqrt(d));
   * decode: the query at position p is appended first, then sees positions
     [max(0, p-W+1), p]; a sequence with p < 0 holds no tokens and its output
-    is defined as zeros.
+    is defined as zeros;
+  * chunked prefill: n new tokens at positions [p, p+n) attend the ring
+    (positions before p) and the chunk itself, read before the chunk is
+    appended; each output row equals the causal-prefill row of the same
+    position over the whole sequence.  Appending n tokens is n single appends
+    in order, so when n > W only the last W of them remain.
 """
 
 import math
@@ -293,4 +298,69 @@ def decode(q, k_ring, v_ring, pos, scale):
             s = scale * (kk @ q[b, h])
             e = np.exp(s - s.max())
             out[b, h] = (e / e.sum()) @ vv
+    return out
+
+
+# --------------------------------------------------------------------------
+# Chunked prefill into an existing ring
+# --------------------------------------------------------------------------
+
+def ring_append_chunk(k_ring, v_ring, pos, k_new, v_new):
+    """Append n consecutive tokens per sequence, in place: token i of
+    sequence b has position pos[b] + i and goes to slot (pos[b] + i) mod W,
+    one token after the other, so a later token overwrites an earlier one
+    that maps to the same slot (Ultralytics ring-buffer paragraph; robocikowo
+    rolling buffer, FIFO).  k_new [B, Hkv, n, d].  A negative pos[b] writes
+    nothing for that sequence.
+    """
+    n = k_new.shape[2]
+    for b, p in enumerate(np.asarray(pos).tolist()):
+        if p < 0:
+            continue
+        for i in range(n):
+            ring_append(k_ring[b:b + 1], v_ring[b:b + 1], [p + i], k_new[b:b + 1, :, i],
+                        v_new[b:b + 1, :, i])
+
+
+def prefill_chunk(q, k, v, k_ring, v_ring, pos, W, scale, heads=None, rows=None):
+    """Causal windowed attention for a chunk of n new tokens per sequence.
+
+    Token i of sequence b sits at position P = pos[b] + i and sees the causal
+    window [max(0, P-W+1), P] (robocikowo definition paragraph; Ultralytics
+    mask 0 <= i-j < w).  Positions before pos[b] are read from the ring,
+    where position p' lives in slot p' mod W (Ultralytics ring-buffer
+    paragraph); positions from pos[b] on are the chunk's own rows k[b, g, p'-pos[b]].
+    The ring is read before the chunk is appended to it.
+
+    q [B, Hq, n, d]; k, v [B, Hkv, n, d]; rings [B, Hkv, W, d]; pos [B].
+    Returns float64 [B, Hq, n, d]; a sequence with pos[b] < 0 gives zeros.
+    `heads` (list of (b, h)) and `rows` (list of chunk rows) restrict the
+    computation; entries left out are NaN.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, n, d = q.shape
+    Hkv = k.shape[1]
+    restricted = heads is not None or rows is not None
+    out = np.full((B, Hq, n, d), np.nan) if restricted else np.zeros((B, Hq, n, d))
+    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
+    row_list = list(range(n)) if rows is None else [int(i) for i in rows]
+    pos = np.asarray(pos).tolist()
+    for b, h in pairs:
+        p = pos[b]
+        if p < 0:
+            out[b, h, row_list] = 0.0
+            continue
+        g = kv_head(h, Hq, Hkv)
+        for i in row_list:
+            P = p + i
+            window = np.arange(max(0, P - W + 1), P + 1)
+            old = window[window < p]
+            new = window[window >= p] - p
+            kk = np.concatenate([np.asarray(k_ring[b, g, old % W], dtype=np.float64),
+                                 np.asarray(k[b, g, new], dtype=np.float64)])
+            vv = np.concatenate([np.asarray(v_ring[b, g, old % W], dtype=np.float64),
+                                 np.asarray(v[b, g, new], dtype=np.float64)])
+            sc = scale * (kk @ q[b, h, i])
+            e = np.exp(sc - sc.max())
+            out[b, h, i] = (e / e.sum()) @ vv
     return out

@@ -322,3 +322,99 @@ def test_mutant_symmetric_as_causal_is_caught():
     q, k, v = rand((1, 1, T, d), 33), rand((1, 1, T, d), 34), rand((1, 1, T, d), 35)
     want = sdpa(q, k, v, 0.5, mask=torch_band(T, W, SYMMETRIC))
     assert np.abs(oracle.attention_dense(q, k, v, W, CAUSAL, 0.5) - want).max() > 1e-3
+
+
+# ------------------------------------------------ chunked prefill into a ring
+
+@pytest.mark.parametrize("W,p,n", [(4, 0, 16), (4, 5, 7), (4, 9, 3), (6, 2, 11), (1, 7, 5),
+                                   (16, 3, 13), (5, 10, 1), (3, 12, 4)])
+def test_chunk_equals_prefill_rows(W, p, n):
+    """A chunk at positions [p, p+n) after the ring took positions [0, p) (in
+    two chunks) gives the library's masked-softmax rows p..p+n-1 of the whole
+    sequence."""
+    B, Hq, Hkv, d = 2, 4, 2, 8
+    T = p + n
+    q, k, v = rand((B, Hq, T, d), 60), rand((B, Hkv, T, d), 61), rand((B, Hkv, T, d), 62)
+    scale = 1 / math.sqrt(d)
+    want = sdpa(q, k, v, scale, mask=torch_band(T, W, CAUSAL))[:, :, p:]  # library, not the oracle
+    kr = np.full((B, Hkv, W, d), np.nan)
+    vr = np.full((B, Hkv, W, d), np.nan)
+    cut = p // 2
+    oracle.ring_append_chunk(kr, vr, np.zeros(B, dtype=int), k[:, :, :cut], v[:, :, :cut])
+    oracle.ring_append_chunk(kr, vr, np.full(B, cut), k[:, :, cut:p], v[:, :, cut:p])
+    got = oracle.prefill_chunk(q[:, :, p:], k[:, :, p:], v[:, :, p:], kr, vr, np.full(B, p), W, scale)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_chunk_of_one_token_equals_decode():
+    B, Hq, Hkv, W, d = 3, 4, 2, 5, 6
+    rng = np.random.default_rng(63)
+    q = rng.standard_normal((B, Hq, 1, d))
+    k1, v1 = rng.standard_normal((B, Hkv, 1, d)), rng.standard_normal((B, Hkv, 1, d))
+    kr, vr = rng.standard_normal((B, Hkv, W, d)), rng.standard_normal((B, Hkv, W, d))
+    pos = np.array([0, 3, 11])
+    got = oracle.prefill_chunk(q, k1, v1, kr, vr, pos, W, 0.7)
+    oracle.ring_append(kr, vr, pos, k1[:, :, 0], v1[:, :, 0])
+    want = oracle.decode(q[:, :, 0], kr, vr, pos, 0.7)
+    np.testing.assert_allclose(got[:, :, 0], want, rtol=0, atol=1e-13)
+
+
+def test_chunk_negative_position_gives_zeros_and_writes_nothing():
+    rng = np.random.default_rng(64)
+    q = rng.standard_normal((2, 2, 3, 4))
+    k, v = rng.standard_normal((2, 1, 3, 4)), rng.standard_normal((2, 1, 3, 4))
+    kr, vr = rng.standard_normal((2, 1, 5, 4)), rng.standard_normal((2, 1, 5, 4))
+    out = oracle.prefill_chunk(q, k, v, kr, vr, np.array([-1, 2]), 5, 0.5)
+    assert np.all(out[0] == 0.0) and np.all(np.isfinite(out[1]))
+    kr0, vr0 = kr.copy(), vr.copy()
+    oracle.ring_append_chunk(kr, vr, np.array([-3, 2]), k, v)
+    assert np.array_equal(kr[0], kr0[0]) and np.array_equal(vr[0], vr0[0])
+    assert not np.array_equal(kr[1], kr0[1])
+
+
+@pytest.mark.parametrize("W,p,n", [(5, 0, 3), (5, 3, 4), (5, 7, 12), (1, 4, 3), (8, 13, 8),
+                                   (6, 2, 6)])
+def test_append_chunk_closed_form(W, p, n):
+    """Slot s ends up holding chunk token i* = n-1 - ((p+n-1-s) mod W) (the
+    last token whose position is s mod W) when i* >= 0; the other slots keep
+    their previous contents."""
+    B, Hkv, d = 2, 3, 4
+    rng = np.random.default_rng(65)
+    k, v = rng.standard_normal((B, Hkv, n, d)), rng.standard_normal((B, Hkv, n, d))
+    kr, vr = np.full((B, Hkv, W, d), -9.0), np.full((B, Hkv, W, d), -9.0)
+    oracle.ring_append_chunk(kr, vr, np.full(B, p), k, v)
+    for s in range(W):
+        i_star = n - 1 - ((p + n - 1 - s) % W)
+        if i_star >= 0:
+            assert np.array_equal(kr[:, :, s], k[:, :, i_star]), s
+            assert np.array_equal(vr[:, :, s], v[:, :, i_star]), s
+        else:
+            assert np.all(kr[:, :, s] == -9.0) and np.all(vr[:, :, s] == -9.0), s
+
+
+def test_mutant_chunk_appended_before_it_is_read_is_caught():
+    """Reading the ring after the chunk was written into it (the wrong order)
+    loses keys the early rows of the chunk need."""
+    B, Hq, Hkv, d, W, p, n = 1, 2, 1, 8, 4, 9, 3
+    T = p + n
+    q, k, v = rand((B, Hq, T, d), 66), rand((B, Hkv, T, d), 67), rand((B, Hkv, T, d), 68)
+    want = sdpa(q, k, v, 0.5, mask=torch_band(T, W, CAUSAL))[:, :, p:]
+    kr, vr = np.zeros((B, Hkv, W, d)), np.zeros((B, Hkv, W, d))
+    oracle.ring_append_chunk(kr, vr, np.zeros(B, dtype=int), k, v)  # positions 0..T-1, too far
+    got = oracle.prefill_chunk(q[:, :, p:], k[:, :, p:], v[:, :, p:], kr, vr, np.full(B, p), W, 0.5)
+    assert np.abs(got - want).max() > 1e-3
+
+
+def test_mutant_chunk_ring_slot_is_caught():
+    """A ring filled one slot off (position p' in slot (p'+1) mod W) gives
+    different chunk rows."""
+    B, Hq, Hkv, d, W, p, n = 1, 2, 1, 8, 4, 9, 3
+    T = p + n
+    q, k, v = rand((B, Hq, T, d), 69), rand((B, Hkv, T, d), 70), rand((B, Hkv, T, d), 71)
+    want = sdpa(q, k, v, 0.5, mask=torch_band(T, W, CAUSAL))[:, :, p:]
+    kr, vr = np.zeros((B, Hkv, W, d)), np.zeros((B, Hkv, W, d))
+    for t in range(p):
+        kr[:, :, (t + 1) % W] = k[:, :, t]
+        vr[:, :, (t + 1) % W] = v[:, :, t]
+    got = oracle.prefill_chunk(q[:, :, p:], k[:, :, p:], v[:, :, p:], kr, vr, np.full(B, p), W, 0.5)
+    assert np.abs(got - want).max() > 1e-3
