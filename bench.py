@@ -253,7 +253,53 @@ def all_configs(reps):
         row[tag] = {"ms": round(ms, 5), "kv_gbs": round(kv_bytes / ms / 1e6, 1),
                     "frac_roofline": round(t_roof / ms, 3)}
     print(json.dumps(row), flush=True)
+    del q, kr, vr, out, ws
+
+    # chunked prefill into full rings, then the chunk's append
+    c = si.WORKLOADS[6]
+    tensors = si.chunk_inputs(6)
+    q, k, v, kr, vr = (si.to_torch(t, dev) for t in tensors[:5])
+    pos_np = tensors[5]
+    pos = torch.from_numpy(pos_np).to(dev)
+    out = torch.empty_like(q)
+    fn = lambda: swa.prefill_chunk(q, k, v, kr, vr, pos, scale=1.0 / math.sqrt(c["d"]), out=out)  # noqa: E731
+    flops, bytes_ = chunk_work(c, pos_np)
+    t_roof = max(flops / (PEAK_BF16_TFLOPS * 1e12), bytes_ / (PEAK_HBM_GBS * 1e9)) * 1e3
+    bound = "mfma" if flops / PEAK_BF16_TFLOPS / 1e12 >= bytes_ / PEAK_HBM_GBS / 1e9 else "hbm"
+    row = {"config": c["name"], "kernel": "prefill_chunk", "bound": bound,
+           "roofline_ms": round(t_roof, 5)}
+    for tag, fl in (("warm", False), ("flushed", True)):
+        ms = timed(fn, fl)
+        row[tag] = {"ms": round(ms, 5), "tflops": round(flops / ms / 1e9, 1),
+                    "gbs": round(bytes_ / ms / 1e6, 1), "frac_roofline": round(t_roof / ms, 3)}
+    print(json.dumps(row), flush=True)
+    # the append rewrites the same slots every repetition (same positions)
+    fn = lambda: swa.cache_append_chunk(kr, vr, pos, k, v)  # noqa: E731
+    rows = c["B"] * c["Hkv"] * min(c["n"], c["W"])
+    bytes_ = 2 * rows * c["d"] * 2 * 2  # K and V rows, read once and written once
+    t_roof = bytes_ / (PEAK_HBM_GBS * 1e9) * 1e3
+    row = {"config": c["name"] + " append", "kernel": "append_chunk", "bound": "hbm",
+           "roofline_ms": round(t_roof, 5)}
+    for tag, fl in (("warm", False), ("flushed", True)):
+        ms = timed(fn, fl)
+        row[tag] = {"ms": round(ms, 5), "gbs": round(bytes_ / ms / 1e6, 1),
+                    "frac_roofline": round(t_roof / ms, 3)}
+    print(json.dumps(row), flush=True)
     return 0
+
+
+def chunk_work(c, pos):
+    """In-window FLOPs and algorithmic bytes of a chunked prefill: row i of a
+    chunk at position p sees min(p + i + 1, W) keys; the bytes are Q, O, the
+    chunk's K and V, and the ring rows some window reads (min(p, W - 1) per
+    KV head, K and V), bf16."""
+    n, W, d = c["n"], c["W"], c["d"]
+    i = np.arange(n, dtype=np.int64)
+    keys = sum(int(np.minimum(int(p) + i + 1, W).sum()) for p in pos if p >= 0)
+    flops = 4 * d * keys * c["Hq"]
+    ring_rows = sum(min(int(p), W - 1) for p in pos if p >= 0)
+    bytes_ = 2 * d * (c["B"] * n * (2 * c["Hq"] + 2 * c["Hkv"]) + 2 * c["Hkv"] * ring_rows)
+    return flops, bytes_
 
 
 def main():

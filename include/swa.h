@@ -22,6 +22,8 @@
  *       k_ring, v_ring[B, Hkv, W, d]
  *       k_new, v_new  [B, Hkv, d]
  *       pos           [B] int32
+ *     and for a chunk of n tokens per sequence (chunked prefill)
+ *       q, out        [B, Hq, n, d]    k, v  [B, Hkv, n, d]
  *     Element type is selected by `dtype` (swa_dtype): IEEE fp32 or bfloat16.
  *   - Query head h reads KV head h / (Hq / Hkv) (contiguous GQA groups); Hq
  *     must be a multiple of Hkv.
@@ -133,6 +135,60 @@ int swa_cache_append(void* k_ring, void* v_ring, const int32_t* pos, const void*
 int swa_decode(const void* q, const void* k_ring, const void* v_ring, const int32_t* pos,
                void* out, int B, int Hq, int Hkv, int W, int d, float scale, int dtype,
                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * swa_cache_append_chunk - append n consecutive tokens per sequence to the
+ * ring cache.
+ *
+ *   token i of sequence b has position pos[b] + i and is written to slot
+ *   (pos[b] + i) mod W:  k_ring[b, :, (pos[b]+i) mod W, :] = k[b, :, i, :]
+ *   (and the same for v).
+ *
+ * The result equals n single appends in order (Ultralytics ring-buffer
+ * paragraph: slot i mod w, the oldest entry is overwritten), so when n > W
+ * only the last W tokens of the chunk remain; the earlier ones are not
+ * written at all.  A bit-exact copy.  A sequence with pos[b] < 0 is left
+ * untouched.  Positions pos[b] + n - 1 must stay below 2^31; a larger value
+ * lands in some slot of its own sequence, never outside the ring.
+ *
+ *   k_ring, v_ring  in/out [B, Hkv, W, d].
+ *   pos             device int32 [B], the position of each chunk's first token.
+ *   k, v            input [B, Hkv, n, d].
+ *   B, n, Hkv, W >= 1, d in {32, 64, 128}, dtype in swa_dtype.
+ */
+int swa_cache_append_chunk(void* k_ring, void* v_ring, const int32_t* pos, const void* k,
+                           const void* v, int B, int n, int Hkv, int W, int d, int dtype,
+                           void* stream);
+
+/*
+ * swa_prefill_chunk - causal windowed attention for a chunk of n new tokens
+ * per sequence that continues a sequence whose earlier tokens are in the ring
+ * cache (chunked prefill).
+ *
+ * Token i of sequence b sits at position P = pos[b] + i and attends the
+ * positions [max(0, P-W+1), P] (robocikowo definition paragraph; Ultralytics
+ * mask 0 <= i-j < w): the positions before pos[b] from ring slot p' mod W
+ * (Ultralytics ring-buffer paragraph), the others from the chunk's own rows.
+ * The output equals rows pos[b] .. pos[b]+n-1 of swa_prefill (causal, same W)
+ * over the whole sequence, provided every earlier position was appended.
+ * The ring is only read: append the chunk with swa_cache_append_chunk after
+ * this call (same stream), because its tokens overwrite slots that the
+ * chunk's early rows still read.  A sequence with pos[b] < 0 gets all-zero
+ * output rows.  Positions must stay below 2^31.
+ *
+ *   q               input [B, Hq, n, d].
+ *   k, v            input [B, Hkv, n, d], the chunk's own keys and values.
+ *   k_ring, v_ring  input [B, Hkv, W, d], holding positions
+ *                   [max(0, pos[b]-W), pos[b]-1].
+ *   pos             device int32 [B], the position of each chunk's first token
+ *                   (the number of tokens appended before it).
+ *   out             output [B, Hq, n, d] (may not alias any input).
+ *   B, n, W, Hq, Hkv >= 1, Hq % Hkv == 0, d in {32, 64, 128}, scale finite,
+ *   dtype in swa_dtype, W * d * element size < 2^31.
+ */
+int swa_prefill_chunk(const void* q, const void* k, const void* v, const void* k_ring,
+                      const void* v_ring, const int32_t* pos, void* out, int B, int n, int W,
+                      int Hq, int Hkv, int d, float scale, int dtype, void* stream);
 
 /* Workspace bytes swa_decode needs for these sizes (0 for invalid sizes). */
 size_t swa_decode_workspace_bytes(int B, int Hq, int W, int d);

@@ -10,6 +10,7 @@ Layouts (contiguous, head-major):
   prefill  q, out [B, Hq, T, d]   k, v [B, Hkv, T, d]
   ring     k_ring, v_ring [B, Hkv, W, d]   k_new, v_new [B, Hkv, d]   pos [B] int32
   decode   q, out [B, Hq, d]
+  chunk    q, out [B, Hq, n, d]   k, v [B, Hkv, n, d]   (n new tokens per sequence)
 """
 
 import ctypes
@@ -54,6 +55,10 @@ def load():
     lib.swa_cache_append.restype = i
     lib.swa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     lib.swa_decode.restype = i
+    lib.swa_cache_append_chunk.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+    lib.swa_cache_append_chunk.restype = i
+    lib.swa_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    lib.swa_prefill_chunk.restype = i
     lib.swa_decode_workspace_bytes.argtypes = [i, i, i, i]
     lib.swa_decode_workspace_bytes.restype = sz
     lib.swa_status_string.argtypes = [i]
@@ -174,4 +179,56 @@ def decode(q, k_ring, v_ring, pos, scale=None, out=None, workspace=None, stream=
                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                            _stream(stream))
     _raise("swa_decode", st)
+    return out
+
+
+def cache_append_chunk(k_ring, v_ring, pos, k, v, stream=None):
+    """Append n tokens per sequence: k/v [B, Hkv, n, d], token i to slot
+    (pos[b] + i) mod W of the rings."""
+    import torch
+    _check(k_ring, "k_ring", 4)
+    _check(v_ring, "v_ring", 4, k_ring.dtype)
+    _check(pos, "pos", 1, torch.int32)
+    _check(k, "k", 4, k_ring.dtype)
+    _check(v, "v", 4, k_ring.dtype)
+    B, Hkv, W, d = k_ring.shape
+    n = k.shape[2]
+    if tuple(v_ring.shape) != tuple(k_ring.shape) or tuple(k.shape) != (B, Hkv, n, d) \
+            or tuple(v.shape) != tuple(k.shape) or pos.shape[0] != B:
+        raise ValueError("shape mismatch")
+    st = load().swa_cache_append_chunk(k_ring.data_ptr(), v_ring.data_ptr(), pos.data_ptr(),
+                                       k.data_ptr(), v.data_ptr(), B, n, Hkv, W, d,
+                                       _dtype_code(k_ring), _stream(stream))
+    _raise("swa_cache_append_chunk", st)
+
+
+def prefill_chunk(q, k, v, k_ring, v_ring, pos, scale=None, out=None, stream=None):
+    """Causal attention of a chunk of n new tokens per sequence (positions
+    pos[b] .. pos[b]+n-1) over the ring plus the chunk itself; returns out
+    [B, Hq, n, d].  Append the chunk to the rings afterwards."""
+    import torch
+    _check(q, "q", 4)
+    _check(k, "k", 4, q.dtype)
+    _check(v, "v", 4, q.dtype)
+    _check(k_ring, "k_ring", 4, q.dtype)
+    _check(v_ring, "v_ring", 4, q.dtype)
+    _check(pos, "pos", 1, torch.int32)
+    B, Hq, n, d = q.shape
+    Hkv, W = k_ring.shape[1], k_ring.shape[2]
+    if tuple(k.shape) != (B, Hkv, n, d) or tuple(v.shape) != tuple(k.shape) \
+            or tuple(k_ring.shape) != (B, Hkv, W, d) or tuple(v_ring.shape) != tuple(k_ring.shape) \
+            or pos.shape[0] != B:
+        raise ValueError("shape mismatch q%s k%s ring%s" % (tuple(q.shape), tuple(k.shape),
+                                                          tuple(k_ring.shape)))
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", 4, q.dtype)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = load().swa_prefill_chunk(q.data_ptr(), k.data_ptr(), v.data_ptr(), k_ring.data_ptr(),
+                                  v_ring.data_ptr(), pos.data_ptr(), out.data_ptr(), B, n, W, Hq,
+                                  Hkv, d, float(scale), _dtype_code(q), _stream(stream))
+    _raise("swa_prefill_chunk", st)
     return out

@@ -59,6 +59,49 @@ int swa_cache_append(void* k_ring, void* v_ring, const int32_t* pos, const void*
   return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH;
 }
 
+int swa_cache_append_chunk(void* k_ring, void* v_ring, const int32_t* pos, const void* k,
+                           const void* v, int B, int n, int Hkv, int W, int d, int dtype,
+                           void* stream) {
+  if (!k_ring || !v_ring || !pos || !k || !v) return SWA_ERR_INVALID_ARG;
+  if (!aligned16(k_ring) || !aligned16(v_ring) || !aligned16(pos) || !aligned16(k) ||
+      !aligned16(v))
+    return SWA_ERR_INVALID_ARG;
+  if (B <= 0 || n <= 0 || Hkv <= 0 || W <= 0) return SWA_ERR_INVALID_ARG;
+  if (!supported_d(d) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
+  const long long row_bytes = (long long)d * elem_bytes(dtype);
+  const long long written = n < W ? n : W;
+  if ((long long)B * Hkv * written * (row_bytes / 16) / 256 + 1 > kMaxGrid) return SWA_ERR_UNSUPPORTED;
+  hipError_t e = swa::launch_append_chunk(k_ring, v_ring, pos, k, v, B, n, Hkv, W, (int)row_bytes,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH;
+}
+
+int swa_prefill_chunk(const void* q, const void* k, const void* v, const void* k_ring,
+                      const void* v_ring, const int32_t* pos, void* out, int B, int n, int W,
+                      int Hq, int Hkv, int d, float scale, int dtype, void* stream) {
+  if (!q || !k || !v || !k_ring || !v_ring || !pos || !out) return SWA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_ring) ||
+      !aligned16(v_ring) || !aligned16(pos) || !aligned16(out))
+    return SWA_ERR_INVALID_ARG;
+  if (B <= 0 || n <= 0 || W <= 0 || Hq <= 0 || Hkv <= 0) return SWA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return SWA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return SWA_ERR_INVALID_ARG;
+  if (!supported_d(d) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
+  // ring rows are addressed with 32-bit byte offsets
+  if ((long long)W * d * elem_bytes(dtype) > 2147483647LL) return SWA_ERR_UNSUPPORTED;
+  // folded head counts and the workgroup count (16-row blocks for fp32) fit int32
+  if ((long long)B * Hq > kMaxGrid) return SWA_ERR_UNSUPPORTED;
+  if ((long long)((n + 15) / 16) * Hq * B > kMaxGrid) return SWA_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e =
+      (dtype == SWA_BF16)
+          ? swa::launch_prefill_chunk_bf16(q, k, v, k_ring, v_ring, pos, out, B, n, W, Hq, Hkv, d,
+                                           scale, s)
+          : swa::launch_prefill_chunk_f32(q, k, v, k_ring, v_ring, pos, out, B, n, W, Hq, Hkv, d,
+                                          scale, s);
+  return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH;
+}
+
 size_t swa_decode_workspace_bytes(int B, int Hq, int W, int d) {
   if (B <= 0 || Hq <= 0 || W <= 0 || !supported_d(d)) return 0;
   const int S = swa::decode_splits(B, Hq, W);

@@ -17,6 +17,21 @@ hipError_t launch_prefill_f32(const void* q, const void* k, const void* v, void*
                               int W, int Hq, int Hkv, int d, int mode, float scale,
                               hipStream_t stream);
 
+// Chunk of n tokens per sequence against its ring plus itself (causal).
+hipError_t launch_prefill_chunk_bf16(const void* q, const void* k, const void* v,
+                                     const void* k_ring, const void* v_ring, const int32_t* pos,
+                                     void* out, int B, int n, int W, int Hq, int Hkv, int d,
+                                     float scale, hipStream_t stream);
+
+hipError_t launch_prefill_chunk_f32(const void* q, const void* k, const void* v,
+                                    const void* k_ring, const void* v_ring, const int32_t* pos,
+                                    void* out, int B, int n, int W, int Hq, int Hkv, int d,
+                                    float scale, hipStream_t stream);
+
+hipError_t launch_append_chunk(void* k_ring, void* v_ring, const int32_t* pos, const void* k,
+                               const void* v, int B, int n, int Hkv, int W, int row_bytes,
+                               hipStream_t stream);
+
 hipError_t launch_append(void* k_ring, void* v_ring, const int32_t* pos, const void* k_new,
                          const void* v_new, int B, int Hkv, int W, int row_bytes,
                          hipStream_t stream);

@@ -43,6 +43,12 @@
 // Grouped-query heads: query head h reads KV head h / (Hq / Hkv); workgroups
 // are ordered so that the heads of one group and neighbouring query blocks
 // land on the same XCD and share K/V through its L2.
+//
+// Chunked prefill (MODE 2) is the causal kernel in key coordinates relative
+// to the chunk's first token at position p: key r >= 0 is chunk row r, key
+// r < 0 is position p + r, read from ring slot (p + r) mod W (Ultralytics
+// ring-buffer paragraph).  Tiles are aligned to the chunk start, so a tile is
+// wholly ring or wholly chunk; the window mask adds p + r >= 0.
 
 #include "swa_device.h"
 #include "swa_launch.h"
@@ -96,12 +102,18 @@ __device__ __forceinline__ int swz(int row) {
 template <int D>
 constexpr int kWavesPerSimd = D == 128 ? 2 : (D == 64 ? 3 : 5);
 
+// MODE: 0 causal, 1 symmetric, 2 causal chunk continuing a ring cache (T is
+// then the chunk length; kring/vring/pos/hkv_seq are used by MODE 2 only).
 template <int D, int MODE>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>, kWavesPerSimd<D>)))
 void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                          const __bf16* __restrict__ v, __bf16* __restrict__ out, int T, int W,
-                         int Hq, int Hkv, float c, uint32_t qsign, int n_qtiles) {
+                         int Hq, int Hkv, float c, uint32_t qsign, int n_qtiles,
+                         const __bf16* __restrict__ kring, const __bf16* __restrict__ vring,
+                         const int32_t* __restrict__ pos, int hkv_seq) {
+  constexpr bool kCausal = MODE != 1;
+  constexpr bool kChunk = MODE == 2;
   using Gm = Geo<D>;
   constexpr int ROWB = Gm::ROWB, TILEB = Gm::TILEB, KS = Gm::KS;
   constexpr int MD = Gm::MD, NLD = Gm::NLD;
@@ -136,22 +148,45 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   const __bf16* kh = k + (size_t)kvh * T * D;
   const __bf16* vh = v + (size_t)kvh * T * D;
 
+  // chunk mode: position of the chunk's first token; the lowest key is -pstart
+  int pstart = 0;
+  if constexpr (kChunk) {
+    pstart = pos[kvh / hkv_seq];
+    if (pstart < 0) {  // inactive sequence: zero rows (uniform over the workgroup)
+      if (qi < T) {
+        __bf16* orow = out + ((size_t)h * T + qi) * D;
+#pragma unroll
+        for (int md = 0; md < Gm::MD; ++md)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq)
+            *reinterpret_cast<uint2*>(orow + 32 * md + 8 * rq + 4 * half) = make_uint2(0, 0);
+      }
+      return;
+    }
+  }
+
   const int hw = W >> 1;
   int lo, hi;
-  if (MODE == 0) {
-    lo = max(0, q0 - W + 1);
+  if (kCausal) {
+    lo = max(-pstart, q0 - W + 1);
     hi = min(T - 1, q0 + kBM - 1);
   } else {
     lo = max(0, q0 - hw);
     hi = min(T - 1, q0 + kBM - 1 + hw);
   }
-  const int kt0 = lo / kBN, kt1 = hi / kBN;
+  int kt0;
+  if constexpr (kChunk) {
+    kt0 = lo >= 0 ? lo / kBN : -((kBN - 1 - lo) / kBN);  // floor division
+  } else {
+    kt0 = lo / kBN;
+  }
+  const int kt1 = hi / kBN;
 
   // this wave's rows and key range
   const bool wave_active = qw0 < T;
   const int qlast = min(qw0 + 31, T - 1);
-  const int wlo = (MODE == 0) ? max(0, qw0 - W + 1) : max(0, qw0 - hw);
-  const int whi = (MODE == 0) ? qlast : min(T - 1, qlast + hw);
+  const int wlo = kCausal ? max(-pstart, qw0 - W + 1) : max(0, qw0 - hw);
+  const int whi = kCausal ? qlast : min(T - 1, qlast + hw);
 
   // ---- Q rows as B operands, zero beyond the sequence; a negative scale is
   // folded into Q's sign bits (exact) so that c > 0 below.
@@ -183,6 +218,30 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   }
   auto load_tile = [&](char* Kdst, char* Vdst, int kt) __attribute__((always_inline)) {
     const int kbase = kt * kBN;
+    if constexpr (kChunk) {
+      if (kbase < 0) {
+        // a ring tile: key r = kbase + row is position pstart + r < pstart, in
+        // slot (pstart + r) mod W.  Rows before position 0 (never in a window)
+        // re-read position 0, which every sequence with pstart >= 1 has written.
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(kring + (size_t)kvh * W * D), 0, W * ROWB, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(vring + (size_t)kvh * W * D), 0, W * ROWB, kBufferFlags);
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) {
+          const int wbase = (j * kThreads + wave * 64) * 16;
+          const unsigned slot = (unsigned)max(pstart + kbase + src_row[j], 0) % (unsigned)W;
+          const int off = (int)slot * ROWB + src_off[j];
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass mishandles this builtin
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(Kdst + wbase), 16, off, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(Vdst + wbase), 16, off, 0, 0, 0);
+#else
+          (void)rk, (void)rv, (void)wbase, (void)off;
+#endif
+        }
+        return;
+      }
+    }
     const int last = T - 1 - kbase;  // last valid row of this tile
     const int bytes = (last + 1) * ROWB;
     const __amdgpu_buffer_rsrc_t rk =
@@ -399,27 +458,28 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
         const int key = k0 + mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
         const int diff = qi - key;
         bool ok = key < T;
-        if (MODE == 0) {
+        if (kCausal) {
           ok = ok && diff >= 0 && diff < W;
+          if (kChunk) ok = ok && key >= -pstart;
         } else {
           ok = ok && diff >= -hw && diff <= hw;
         }
         if (!ok) s[mb][r] = -INFINITY;
       }
     }
-    bf16x8 p[4];
+    bf16x8 pb[4];
     float l0, l1;
-    probs(s[0], -m_ref * c, p, l0);
-    probs(s[1], -m_ref * c, p + 2, l1);
+    probs(s[0], -m_ref * c, pb, l0);
+    probs(s[1], -m_ref * c, pb + 2, l1);
     if (raise_max(s, 2, fmaxf(l0, l1))) {
-      probs(s[0], -m_ref * c, p, l0);
-      probs(s[1], -m_ref * c, p + 2, l1);
+      probs(s[0], -m_ref * c, pb, l0);
+      probs(s[1], -m_ref * c, pb + 2, l1);
     }
     l_part += l0 + l1;
 #pragma unroll
     for (int md = 0; md < MD; ++md) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(Vs, md, kk), p[kk], o[md], 0, 0, 0);
+      for (int kk = 0; kk < 4; ++kk) o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(Vs, md, kk), pb[kk], o[md], 0, 0, 0);
     }
   };
 
@@ -433,8 +493,9 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     const int k0 = kt * kBN;
     if (!(wave_active && k0 <= whi && k0 + kBN - 1 >= wlo)) return;
     bool full;
-    if (MODE == 0) {
+    if (kCausal) {
       full = (k0 + kBN - 1 <= qw0) && (k0 >= qlast - W + 1) && (k0 + kBN <= T);
+      if (kChunk) full = full && k0 >= -pstart;
     } else {
       full = (k0 >= qlast - hw) && (k0 + kBN - 1 <= qw0 + hw) && (k0 + kBN <= T);
     }
@@ -678,11 +739,45 @@ hipError_t launch(const void* q, const void* k, const void* v, void* out, int T,
   hipLaunchKernelGGL((prefill_bf16_kernel<D, MODE>), dim3((unsigned)nwg), dim3(kThreads), 0,
                      stream, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                      static_cast<const __bf16*>(v), static_cast<__bf16*>(out), T, W, Hq, Hkv, c,
-                     qsign, n_qtiles);
+                     qsign, n_qtiles, static_cast<const __bf16*>(nullptr),
+                     static_cast<const __bf16*>(nullptr), static_cast<const int32_t*>(nullptr), 1);
+  return hipGetLastError();
+}
+
+// Chunked prefill: B sequences of n new tokens; heads are folded with the
+// batch (B*Hq query heads, B*Hkv KV heads, ring heads likewise), and the
+// kernel recovers the sequence of KV head kvh as kvh / Hkv.
+template <int D>
+hipError_t launch_chunk(const void* q, const void* k, const void* v, const void* k_ring,
+                        const void* v_ring, const int32_t* pos, void* out, int B, int n, int W,
+                        int Hq, int Hkv, float scale, hipStream_t stream) {
+  const int n_qtiles = (n + kBM - 1) / kBM;
+  const long long nwg = (long long)n_qtiles * Hq * B;
+  float c = scale * kLog2e;
+  uint32_t qsign = 0;
+  if (c < 0.f) {
+    c = -c;
+    qsign = 0x80008000u;
+  }
+  if (c == 0.f) c = 1.0e-30f;
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, 2>), dim3((unsigned)nwg), dim3(kThreads), 0, stream,
+                     static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+                     static_cast<const __bf16*>(v), static_cast<__bf16*>(out), n, W, Hq * B,
+                     Hkv * B, c, qsign, n_qtiles, static_cast<const __bf16*>(k_ring),
+                     static_cast<const __bf16*>(v_ring), pos, Hkv);
   return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_prefill_chunk_bf16(const void* q, const void* k, const void* v,
+                                     const void* k_ring, const void* v_ring, const int32_t* pos,
+                                     void* out, int B, int n, int W, int Hq, int Hkv, int d,
+                                     float scale, hipStream_t stream) {
+  if (d == 32) return launch_chunk<32>(q, k, v, k_ring, v_ring, pos, out, B, n, W, Hq, Hkv, scale, stream);
+  if (d == 64) return launch_chunk<64>(q, k, v, k_ring, v_ring, pos, out, B, n, W, Hq, Hkv, scale, stream);
+  return launch_chunk<128>(q, k, v, k_ring, v_ring, pos, out, B, n, W, Hq, Hkv, scale, stream);
+}
 
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* out, int T,
                                int W, int Hq, int Hkv, int d, int mode, float scale,

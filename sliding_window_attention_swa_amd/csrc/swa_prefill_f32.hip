@@ -7,6 +7,11 @@
 // in-window logits only.  16 lanes share one query row, each holding d/16
 // dims; a row walks exactly the keys of its own window, one key at a time,
 // with a running maximum and sum.
+//
+// Chunked prefill (MODE 2): T is the chunk length and row i is position
+// p + i of its sequence; its keys r = j - p in [max(-p, i-W+1), i] come from
+// ring slot (p + r) mod W when r < 0 (Ultralytics ring-buffer paragraph) and
+// from chunk row r otherwise.
 
 #include "swa_device.h"
 #include "swa_launch.h"
@@ -17,13 +22,14 @@ namespace {
 constexpr int kRowsPerBlock = 16;
 constexpr int kLanesPerRow = 16;
 
+// MODE: 0 causal, 1 symmetric, 2 causal chunk continuing a ring cache
+// (kring/vring/pos/hkv_seq are used by MODE 2 only).
 template <int D, int MODE>
-__global__ __launch_bounds__(256) void prefill_f32_kernel(const float* __restrict__ q,
-                                                          const float* __restrict__ k,
-                                                          const float* __restrict__ v,
-                                                          float* __restrict__ out, int T,
-                                                          int W, int Hq, int Hkv, float scale,
-                                                          int n_rowblocks) {
+__global__ __launch_bounds__(256) void prefill_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    float* __restrict__ out, int T, int W, int Hq, int Hkv, float scale, int n_rowblocks,
+    const float* __restrict__ kring, const float* __restrict__ vring,
+    const int32_t* __restrict__ pos, int hkv_seq) {
   constexpr int DPL = D / kLanesPerRow;
   const int h = blockIdx.x / n_rowblocks;
   const int i = (blockIdx.x % n_rowblocks) * kRowsPerBlock + threadIdx.x / kLanesPerRow;
@@ -34,6 +40,17 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(const float* __restric
   const float* kh = k + (size_t)kvh * T * D + c * DPL;
   const float* vh = v + (size_t)kvh * T * D + c * DPL;
 
+  float* orow = out + ((size_t)h * T + i) * D + c * DPL;
+  int pstart = 0;  // chunk mode: position of the chunk's first token
+  if constexpr (MODE == 2) {
+    pstart = pos[kvh / hkv_seq];
+    if (pstart < 0) {  // inactive sequence: zero rows
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) orow[e] = 0.f;
+      return;
+    }
+  }
+
   float qv[DPL], acc[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) {
@@ -41,16 +58,34 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(const float* __restric
     acc[e] = 0.f;
   }
   int lo, hi;
-  if (MODE == 0) {
-    lo = max(0, i - W + 1);
+  if (MODE != 1) {
+    lo = max(-pstart, i - W + 1);
     hi = i;
   } else {
     lo = max(0, i - W / 2);
     hi = min(T - 1, i + W / 2);
   }
+  // chunk mode: ring slot of key lo (pstart + lo >= 0), advanced with the key
+  unsigned slot = 0;
+  const float* krh = nullptr;
+  const float* vrh = nullptr;
+  if constexpr (MODE == 2) {
+    slot = (unsigned)(pstart + lo) % (unsigned)W;
+    krh = kring + (size_t)kvh * W * D + c * DPL;
+    vrh = vring + (size_t)kvh * W * D + c * DPL;
+  }
   float m = -INFINITY, l = 0.f;
   for (int j = lo; j <= hi; ++j) {
-    const float* kr = kh + (size_t)j * D;
+    const float* kr;
+    const float* vr;
+    if (MODE == 2 && j < 0) {  // a ring position
+      kr = krh + (size_t)slot * D;
+      vr = vrh + (size_t)slot * D;
+      slot = slot + 1 == (unsigned)W ? 0u : slot + 1;
+    } else {
+      kr = kh + (size_t)j * D;
+      vr = vh + (size_t)j * D;
+    }
     float s = 0.f;
 #pragma unroll
     for (int e = 0; e < DPL; ++e) s = fmaf(qv[e], kr[e], s);
@@ -61,12 +96,10 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(const float* __restric
     const float alpha = expf(m - m_new);  // m = -inf on the first key: 0
     const float p = expf(s - m_new);
     l = l * alpha + p;
-    const float* vr = vh + (size_t)j * D;
 #pragma unroll
     for (int e = 0; e < DPL; ++e) acc[e] = fmaf(p, vr[e], acc[e] * alpha);
     m = m_new;
   }
-  float* orow = out + ((size_t)h * T + i) * D + c * DPL;
   const float inv = 1.0f / l;
 #pragma unroll
   for (int e = 0; e < DPL; ++e) orow[e] = acc[e] * inv;
@@ -81,11 +114,36 @@ hipError_t launch(const void* q, const void* k, const void* v, void* out, int T,
                      dim3(kRowsPerBlock * kLanesPerRow), 0,
                      stream, static_cast<const float*>(q), static_cast<const float*>(k),
                      static_cast<const float*>(v), static_cast<float*>(out), T, W, Hq, Hkv,
-                     scale, n_rowblocks);
+                     scale, n_rowblocks, static_cast<const float*>(nullptr),
+                     static_cast<const float*>(nullptr), static_cast<const int32_t*>(nullptr), 1);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_chunk(const void* q, const void* k, const void* v, const void* k_ring,
+                        const void* v_ring, const int32_t* pos, void* out, int B, int n, int W,
+                        int Hq, int Hkv, float scale, hipStream_t stream) {
+  const int n_rowblocks = (n + kRowsPerBlock - 1) / kRowsPerBlock;
+  const long long nwg = (long long)n_rowblocks * Hq * B;
+  hipLaunchKernelGGL((prefill_f32_kernel<D, 2>), dim3((unsigned)nwg),
+                     dim3(kRowsPerBlock * kLanesPerRow), 0, stream, static_cast<const float*>(q),
+                     static_cast<const float*>(k), static_cast<const float*>(v),
+                     static_cast<float*>(out), n, W, Hq * B, Hkv * B, scale, n_rowblocks,
+                     static_cast<const float*>(k_ring), static_cast<const float*>(v_ring), pos,
+                     Hkv);
   return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_prefill_chunk_f32(const void* q, const void* k, const void* v,
+                                    const void* k_ring, const void* v_ring, const int32_t* pos,
+                                    void* out, int B, int n, int W, int Hq, int Hkv, int d,
+                                    float scale, hipStream_t stream) {
+  if (d == 32) return launch_chunk<32>(q, k, v, k_ring, v_ring, pos, out, B, n, W, Hq, Hkv, scale, stream);
+  if (d == 64) return launch_chunk<64>(q, k, v, k_ring, v_ring, pos, out, B, n, W, Hq, Hkv, scale, stream);
+  return launch_chunk<128>(q, k, v, k_ring, v_ring, pos, out, B, n, W, Hq, Hkv, scale, stream);
+}
 
 hipError_t launch_prefill_f32(const void* q, const void* k, const void* v, void* out, int T,
                               int W, int Hq, int Hkv, int d, int mode, float scale,

@@ -63,6 +63,29 @@ __global__ __launch_bounds__(256) void append_kernel(uint4* __restrict__ k_ring,
   v_ring[dst] = v_new[idx];
 }
 
+// Append n consecutive tokens per sequence: token i goes to slot
+// (pos + i) mod W.  Only the last min(n, W) tokens are written (n single
+// appends in order would overwrite the earlier ones); they map to distinct
+// slots, so no two threads write the same row.  One thread per 16 bytes.
+__global__ __launch_bounds__(256) void append_chunk_kernel(
+    uint4* __restrict__ k_ring, uint4* __restrict__ v_ring, const int32_t* __restrict__ pos,
+    const uint4* __restrict__ k, const uint4* __restrict__ v, int Hkv, int n, int n0, int W,
+    int cpr, long long total) {
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int c = (int)(idx % cpr);
+  const long long t = idx / cpr;
+  const int i = n0 + (int)(t % (n - n0));
+  const long long bh = t / (n - n0);
+  const int p = pos[bh / Hkv];
+  if (p < 0) return;
+  const unsigned slot = ((unsigned)p + (unsigned)i) % (unsigned)W;
+  const long long dst = (bh * W + slot) * cpr + c;
+  const long long src = (bh * n + i) * cpr + c;
+  k_ring[dst] = k[src];
+  v_ring[dst] = v[src];
+}
+
 // --------------------------------------------------------------- helpers
 
 template <typename E>
@@ -356,6 +379,20 @@ hipError_t launch_append(void* k_ring, void* v_ring, const int32_t* pos, const v
   hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      static_cast<uint4*>(k_ring), static_cast<uint4*>(v_ring), pos,
                      static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new), Hkv, W,
+                     cpr, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_chunk(void* k_ring, void* v_ring, const int32_t* pos, const void* k,
+                               const void* v, int B, int n, int Hkv, int W, int row_bytes,
+                               hipStream_t stream) {
+  const int cpr = row_bytes / 16;
+  const int n0 = n > W ? n - W : 0;
+  const long long total = (long long)B * Hkv * (n - n0) * cpr;
+  const long long blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(append_chunk_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<uint4*>(k_ring), static_cast<uint4*>(v_ring), pos,
+                     static_cast<const uint4*>(k), static_cast<const uint4*>(v), Hkv, n, n0, W,
                      cpr, total);
   return hipGetLastError();
 }

@@ -7,12 +7,13 @@ bits produced here.
 
 Recipe: ``numpy.random.default_rng(seed).standard_normal(shape, float32)``,
 then round-to-nearest-even to bfloat16 for bf16 workloads.  Seeds are
-``1000 * workload + role`` with role Q=0, K=1, V=2, positions=3.
+``1000 * workload + role`` with role Q=0, K=1, V=2, positions=3, and for
+chunked prefill ring K=4, ring V=5.
 """
 
 import numpy as np
 
-ROLE_Q, ROLE_K, ROLE_V, ROLE_POS = 0, 1, 2, 3
+ROLE_Q, ROLE_K, ROLE_V, ROLE_POS, ROLE_K_RING, ROLE_V_RING = 0, 1, 2, 3, 4, 5
 
 F32 = "f32"
 BF16 = "bf16"
@@ -36,6 +37,10 @@ WORKLOADS = {
             W=4096, d=128, dtype=BF16, mode=CAUSAL, pos_lo=4096, pos_hi=32768),
     5: dict(name="Longformer symmetric prefill", kind="prefill", B=4, Hq=12, Hkv=12,
             T=4096, W=512, d=64, dtype=BF16, mode=SYMMETRIC),
+    # serving-style chunked prefill: 4 sequences, each continuing with a
+    # 2048-token chunk after at least W tokens are already in its ring
+    6: dict(name="Mistral-7B chunked prefill", kind="chunk", B=4, Hq=32, Hkv=8, n=2048,
+            W=4096, d=128, dtype=BF16, mode=CAUSAL, pos_lo=4096, pos_hi=32768),
 }
 
 
@@ -130,6 +135,31 @@ def decode_inputs(workload=4, B=None, Hq=None, Hkv=None, W=None, d=None, dtype=N
     v_ring = normal(seed_for(workload, ROLE_V), (B, Hkv, W, d), dtype)
     pos = positions(seed_for(workload, ROLE_POS), B, lo, hi)
     return q, k_ring, v_ring, pos
+
+
+def chunk_inputs(workload=6, B=None, Hq=None, Hkv=None, n=None, W=None, d=None, dtype=None,
+                 pos_lo=None, pos_hi=None):
+    """Chunk queries/keys/values, rings and chunk start positions for a
+    chunked-prefill workload.  Every ring slot is filled with a random row
+    (positions >= W by default), which is what a ring holds after at least W
+    appends."""
+    cfg = WORKLOADS[workload]
+    B = cfg["B"] if B is None else B
+    Hq = cfg["Hq"] if Hq is None else Hq
+    Hkv = cfg["Hkv"] if Hkv is None else Hkv
+    n = cfg["n"] if n is None else n
+    W = cfg["W"] if W is None else W
+    d = cfg["d"] if d is None else d
+    dtype = cfg["dtype"] if dtype is None else dtype
+    lo = cfg.get("pos_lo", W) if pos_lo is None else pos_lo
+    hi = cfg.get("pos_hi", 8 * W) if pos_hi is None else pos_hi
+    q = normal(seed_for(workload, ROLE_Q), (B, Hq, n, d), dtype)
+    k = normal(seed_for(workload, ROLE_K), (B, Hkv, n, d), dtype)
+    v = normal(seed_for(workload, ROLE_V), (B, Hkv, n, d), dtype)
+    k_ring = normal(seed_for(workload, ROLE_K_RING), (B, Hkv, W, d), dtype)
+    v_ring = normal(seed_for(workload, ROLE_V_RING), (B, Hkv, W, d), dtype)
+    pos = positions(seed_for(workload, ROLE_POS), B, lo, hi)
+    return q, k, v, k_ring, v_ring, pos
 
 
 def to_torch(t, device="cuda"):

@@ -36,7 +36,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "swa_prefill", "swa_cache_append", "swa_decode", "swa_decode_workspace_bytes",
-        "swa_status_string"])
+        "swa_status_string", "swa_cache_append_chunk", "swa_prefill_chunk"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -75,6 +75,42 @@ def append(lib, kr=P, vr=P, pos=P, kn=P, vn=P, B=2, Hkv=2, W=8, d=64, dtype=1):
 ])
 def test_append_rejects(lib, kw, status):
     assert append(lib, **kw) == status
+
+
+def append_chunk(lib, kr=P, vr=P, pos=P, k=P, v=P, B=2, n=5, Hkv=2, W=8, d=64, dtype=1):
+    return lib.swa_cache_append_chunk(kr, vr, pos, k, v, B, n, Hkv, W, d, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kr=None), INVALID), (dict(vr=None), INVALID), (dict(pos=None), INVALID),
+    (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(vr=MIS), INVALID),
+    (dict(k=MIS), INVALID), (dict(B=0), INVALID), (dict(n=0), INVALID), (dict(n=-1), INVALID),
+    (dict(Hkv=0), INVALID), (dict(W=0), INVALID), (dict(d=8), UNSUPPORTED),
+    (dict(dtype=2), UNSUPPORTED),
+])
+def test_append_chunk_rejects(lib, kw, status):
+    assert append_chunk(lib, **kw) == status
+
+
+def prefill_chunk(lib, q=P, k=P, v=P, kr=P, vr=P, pos=P, out=P, B=2, n=16, W=8, Hq=4, Hkv=2,
+                  d=64, scale=0.125, dtype=1):
+    return lib.swa_prefill_chunk(q, k, v, kr, vr, pos, out, B, n, W, Hq, Hkv, d, scale, dtype,
+                                 None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID),
+    (dict(kr=None), INVALID), (dict(vr=None), INVALID), (dict(pos=None), INVALID),
+    (dict(out=None), INVALID), (dict(q=MIS), INVALID), (dict(kr=MIS), INVALID),
+    (dict(pos=MIS), INVALID), (dict(out=MIS), INVALID), (dict(B=0), INVALID),
+    (dict(n=0), INVALID), (dict(W=-2), INVALID), (dict(Hq=0), INVALID), (dict(Hkv=0), INVALID),
+    (dict(Hq=6, Hkv=4), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(d=16), UNSUPPORTED), (dict(dtype=7), UNSUPPORTED),
+    (dict(W=2**24, d=128), UNSUPPORTED),  # ring rows beyond 32-bit byte offsets
+    (dict(B=2**16, n=2**20, Hq=2**10, Hkv=1), UNSUPPORTED),
+])
+def test_prefill_chunk_rejects(lib, kw, status):
+    assert prefill_chunk(lib, **kw) == status
 
 
 def decode(lib, q=P, kr=P, vr=P, pos=P, out=P, B=2, Hq=8, Hkv=2, W=64, d=64, scale=0.125,
