@@ -31,4 +31,7 @@ from .swa_ref import (  # noqa: F401
     decode,
     ring_append_chunk,
     prefill_chunk,
+    dilated_mask,
+    attention_dilated_dense,
+    attention_dilated_rows,
 )

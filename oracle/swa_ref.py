@@ -42,7 +42,11 @@ Readings of points the pages leave open (each also listed in the design doc):
     (positions before p) and the chunk itself, read before the chunk is
     appended; each output row equals the causal-prefill row of the same
     position over the whole sequence.  Appending n tokens is n single appends
-    in order, so when n > W only the last W of them remain.
+    in order, so when n > W only the last W of them remain;
+  * dilated window (aivaro section 4.2, whose example numbers disagree with
+    each other under the other reading): the window keeps its number of keys
+    and spaces them d apart, so key j is allowed when (i - j) / d is a whole
+    number inside the undilated window.
 """
 
 import math
@@ -364,3 +368,71 @@ def prefill_chunk(q, k, v, k_ring, v_ring, pos, W, scale, heads=None, rows=None)
             e = np.exp(sc - sc.max())
             out[b, h, i] = (e / e.sum()) @ vv
     return out
+
+
+# --------------------------------------------------------------------------
+# Dilated sliding window
+# --------------------------------------------------------------------------
+
+def dilated_mask(T, W, mode, dilation):
+    """Boolean [T, T] mask of the dilated window: query i may see key j when
+    i - j is a multiple of the dilation and the quotient m = (i - j) / dilation
+    lies in the undilated window (causal 0 <= m <= W-1, symmetric
+    |m| <= floor(W/2)), clipped to the sequence.
+
+    aivaro section 4.2 takes every d-th token of the window with gaps, like a
+    dilated convolution (robocikowo, dilated-SWA variant): the number of keys
+    stays that of the plain window while their span grows d-fold; its example
+    W = 512, d = 2 gives 256 keys on each side spanning 1024 positions.  With
+    dilation 1 this is window_mask.
+    """
+    if dilation < 1:
+        raise ValueError("dilation must be >= 1")
+    pos = np.arange(T)
+    offset = pos[:, None] - pos[None, :]
+    on_grid = offset % dilation == 0
+    m = offset // dilation
+    if mode == CAUSAL:
+        return on_grid & (m >= 0) & (m <= W - 1)
+    if mode == SYMMETRIC:
+        return on_grid & (np.abs(m) <= W // 2)
+    raise ValueError("unknown mode %r" % (mode,))
+
+
+def attention_dilated_dense(q, k, v, W, mode, scale, dilation):
+    """Dense [T, T] scores plus the dilated additive mask (the additive-mask
+    form of Finding 15, "Why this needed no exporter changes")."""
+    q, k, v = _as64(q, k, v)
+    B, Hq, Hkv, T, d = _check_shapes(q, k, v)
+    M = np.where(dilated_mask(T, W, mode, dilation), 0.0, -np.inf)
+    out = np.empty((B, Hq, T, d))
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            S = scale * (q[b, h] @ k[b, g].T) + M
+            out[b, h] = _softmax_rows(S) @ v[b, g]
+    return out
+
+
+def attention_dilated_rows(q, k, v, W, mode, scale, dilation, b, h, rows):
+    """Selected query rows of one (b, h), each over exactly its dilated
+    window's keys (for sampled checks of full-size problems).  Returns
+    float64 [len(rows), d]."""
+    B, Hq, T, d = q.shape
+    g = kv_head(h, Hq, k.shape[1])
+    res = np.empty((len(rows), d))
+    for n, i in enumerate(rows):
+        i = int(i)
+        if mode == CAUSAL:
+            m = np.arange(0, W)
+        else:
+            m = np.arange(-(W // 2), W // 2 + 1)
+        keys = i - dilation * m
+        keys = np.sort(keys[(keys >= 0) & (keys < T)])
+        qi = np.asarray(q[b, h, i], dtype=np.float64)
+        kk = np.asarray(k[b, g, keys], dtype=np.float64)
+        vv = np.asarray(v[b, g, keys], dtype=np.float64)
+        sc = scale * (kk @ qi)
+        e = np.exp(sc - sc.max())
+        res[n] = (e / e.sum()) @ vv
+    return res

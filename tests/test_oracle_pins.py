@@ -418,3 +418,74 @@ def test_mutant_chunk_ring_slot_is_caught():
         vr[:, :, (t + 1) % W] = v[:, :, t]
     got = oracle.prefill_chunk(q[:, :, p:], k[:, :, p:], v[:, :, p:], kr, vr, np.full(B, p), W, 0.5)
     assert np.abs(got - want).max() > 1e-3
+
+
+# ------------------------------------------------------ dilated sliding window
+
+def test_page_dilation_example(golden):
+    """An interior row of the symmetric window W=512 at dilation 2 has 256 keys
+    on each side and spans 1024 positions (aivaro section 4.2)."""
+    g = golden("dilation_longformer.txt")
+    W, dil = g["window"], g["dilation"]
+    T = 2 * dil * W + 1
+    i = T // 2
+    row = oracle.dilated_mask(T, W, SYMMETRIC, dil)[i]
+    keys = np.flatnonzero(row)
+    assert int((keys < i).sum()) == g["keys_each_side"] == int((keys > i).sum())
+    assert int(keys.max() - keys.min()) == g["span"]
+
+
+def test_mutant_dilation_as_subsampled_window_is_caught(golden):
+    """The other reading (every d-th key of the undilated window) gives 128
+    keys a side over 512 positions and fails the page's example."""
+    g = golden("dilation_longformer.txt")
+    W, dil = g["window"], g["dilation"]
+    T = 2 * dil * W + 1
+    i = T // 2
+    row = oracle.window_mask(T, W, SYMMETRIC)[i] & ((i - np.arange(T)) % dil == 0)
+    keys = np.flatnonzero(row)
+    assert int((keys < i).sum()) != g["keys_each_side"]
+    assert int(keys.max() - keys.min()) != g["span"]
+
+
+@pytest.mark.parametrize("mode,T,W,dil", [(CAUSAL, 23, 4, 2), (CAUSAL, 31, 5, 3),
+                                          (SYMMETRIC, 29, 6, 2), (SYMMETRIC, 26, 5, 4),
+                                          (CAUSAL, 17, 3, 7), (SYMMETRIC, 12, 16, 3)])
+def test_dilated_equals_plain_window_on_strided_subsequences(mode, T, W, dil):
+    """Key j is visible from query i only when i = j (mod d), and then through
+    the plain window on the offset / d: dilated attention over the sequence is
+    plain windowed attention (pinned above) over each of the d subsequences
+    r, r+d, r+2d, ..."""
+    B, Hq, Hkv, d = 2, 4, 2, 8
+    q, k, v = rand((B, Hq, T, d), 90), rand((B, Hkv, T, d), 91), rand((B, Hkv, T, d), 92)
+    got = oracle.attention_dilated_dense(q, k, v, W, mode, 0.4, dil)
+    for r in range(dil):
+        sub = oracle.attention_dense(q[:, :, r::dil], k[:, :, r::dil], v[:, :, r::dil], W, mode, 0.4)
+        np.testing.assert_allclose(got[:, :, r::dil], sub, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("T,W,dil", [(40, 4, 3), (64, 16, 2), (10, 20, 5)])
+def test_dilated_causal_key_counts(T, W, dil):
+    """Causal row i has min(W, i // d + 1) keys."""
+    rows = oracle.dilated_mask(T, W, CAUSAL, dil).sum(axis=1)
+    assert rows.tolist() == [min(W, i // dil + 1) for i in range(T)]
+
+
+def test_dilation_one_is_the_plain_window():
+    for mode in (CAUSAL, SYMMETRIC):
+        assert np.array_equal(oracle.dilated_mask(21, 6, mode, 1), oracle.window_mask(21, 6, mode))
+    q, k, v = rand((1, 2, 19, 8), 93), rand((1, 1, 19, 8), 94), rand((1, 1, 19, 8), 95)
+    want = sdpa(q, k, v, 0.3, mask=torch_band(19, 5, CAUSAL))  # library
+    np.testing.assert_allclose(oracle.attention_dilated_dense(q, k, v, 5, CAUSAL, 0.3, 1), want,
+                               rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", [CAUSAL, SYMMETRIC])
+def test_dilated_rows_agree_with_dense(mode):
+    T, W, dil = 37, 6, 3
+    q, k, v = rand((1, 4, T, 8), 96), rand((1, 2, T, 8), 97), rand((1, 2, T, 8), 98)
+    dense = oracle.attention_dilated_dense(q, k, v, W, mode, 0.5, dil)
+    rows = [0, 1, 2, 5, 17, 35, 36]
+    for h in range(4):
+        got = oracle.attention_dilated_rows(q, k, v, W, mode, 0.5, dil, 0, h, rows)
+        np.testing.assert_allclose(got, dense[0, h, rows], rtol=0, atol=1e-12)
