@@ -183,13 +183,19 @@ def cpu_baseline(pos_np, q_dec, kr, vr, qkv_pre):
     }
 
 
-def band_pairs(T, W, mode):
-    """(query, key) pairs inside the windows of one head, either mode."""
-    if mode == 0:
-        return band_pairs_causal(T, W)
-    h = W // 2
+def band_pairs(T, W, mode, dilation=1):
+    """(query, key) pairs inside the windows of one head, either mode; with a
+    dilation, row i has the window's offsets m with i - m * dilation in
+    [0, T)."""
     i = np.arange(T, dtype=np.int64)
-    return int((np.minimum(T - 1, i + h) - np.maximum(0, i - h) + 1).sum())
+    if mode == 0:
+        if dilation == 1:
+            return band_pairs_causal(T, W)
+        return int(np.minimum(W - 1, i // dilation).sum() + T)
+    h = W // 2
+    left = np.minimum(h, i // dilation)
+    right = np.minimum(h, (T - 1 - i) // dilation)
+    return int((left + right + 1).sum())
 
 
 def all_configs(reps):
@@ -219,13 +225,15 @@ def all_configs(reps):
         torch.cuda.synchronize()
         return float(np.median([a.elapsed_time(b) for a, b in ev[3:]]))
 
-    for wl in (2, 3, 5):
+    for wl in (2, 3, 5, 7):
         c = si.WORKLOADS[wl]
         q, k, v = (si.to_torch(t, dev) for t in si.prefill_inputs(wl))
         out = torch.empty_like(q)
         scale = 1.0 / math.sqrt(c["d"])
-        fn = lambda: swa.prefill(q, k, v, c["W"], mode=c["mode"], scale=scale, out=out)  # noqa: E731
-        flops = 4 * c["d"] * band_pairs(c["T"], c["W"], c["mode"]) * c["Hq"] * c["B"]
+        dil = c.get("dilation", 1)
+        fn = lambda: swa.prefill_dilated(q, k, v, c["W"], dil, mode=c["mode"], scale=scale,  # noqa: E731
+                                         out=out)
+        flops = 4 * c["d"] * band_pairs(c["T"], c["W"], c["mode"], dil) * c["Hq"] * c["B"]
         bytes_ = 2 * c["T"] * c["d"] * c["B"] * (2 * c["Hq"] + 2 * c["Hkv"])
         t_roof = max(flops / (PEAK_BF16_TFLOPS * 1e12), bytes_ / (PEAK_HBM_GBS * 1e9)) * 1e3
         bound = "mfma" if flops / PEAK_BF16_TFLOPS / 1e12 >= bytes_ / PEAK_HBM_GBS / 1e9 else "hbm"

@@ -94,6 +94,25 @@ int swa_prefill(const void* q, const void* k, const void* v, void* out, int T, i
                 int Hkv, int d, int mode, float scale, int dtype, void* stream);
 
 /*
+ * swa_prefill_dilated - windowed attention with a dilated window.
+ *
+ * Key j is in the window of query i when i - j is a multiple of `dilation`
+ * and m = (i - j) / dilation lies in the plain window of `mode` (causal
+ * 0 <= m <= W-1; symmetric |m| <= floor(W/2)), clipped to 0 <= j < T.  The
+ * window keeps its number of keys and spreads them `dilation` apart
+ * (aivaro.ru answer 629, section 4.2: W = 512 at dilation 2 gives 256 keys
+ * each side over 1024 positions; robocikowo glossary, dilated-SWA variant:
+ * gaps as in a dilated convolution).  dilation = 1 is swa_prefill.
+ *
+ *   Arguments, layouts and errors as swa_prefill, plus
+ *   dilation >= 1 (SWA_ERR_INVALID_ARG otherwise); dilation * d * element
+ *   size * 64 < 2^31 (SWA_ERR_UNSUPPORTED otherwise).
+ */
+int swa_prefill_dilated(const void* q, const void* k, const void* v, void* out, int T, int W,
+                        int Hq, int Hkv, int d, int mode, float scale, int dilation, int dtype,
+                        void* stream);
+
+/*
  * swa_cache_append - write one new K/V row per sequence into the ring cache.
  *
  *   k_ring[b, :, pos[b] mod W, :] = k_new[b, :, :]   (and the same for v)

@@ -51,6 +51,8 @@ def load():
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.swa_prefill.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
     lib.swa_prefill.restype = i
+    lib.swa_prefill_dilated.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+    lib.swa_prefill_dilated.restype = i
     lib.swa_cache_append.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.swa_cache_append.restype = i
     lib.swa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
@@ -123,6 +125,31 @@ def prefill(q, k, v, W, mode=CAUSAL, scale=None, out=None, stream=None):
                             B * Hq, B * Hkv, d, int(mode), float(scale), _dtype_code(q),
                             _stream(stream))
     _raise("swa_prefill", st)
+    return out
+
+
+def prefill_dilated(q, k, v, W, dilation, mode=CAUSAL, scale=None, out=None, stream=None):
+    """Windowed attention with keys `dilation` apart in the window; returns
+    `out` [B, Hq, T, d].  dilation=1 is `prefill`."""
+    import torch
+    _check(q, "q", 4)
+    _check(k, "k", 4, q.dtype)
+    _check(v, "v", 4, q.dtype)
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, T, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("shape mismatch q%s k%s v%s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", 4, q.dtype)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = load().swa_prefill_dilated(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), T,
+                                    int(W), B * Hq, B * Hkv, d, int(mode), float(scale),
+                                    int(dilation), _dtype_code(q), _stream(stream))
+    _raise("swa_prefill_dilated", st)
     return out
 
 

@@ -44,6 +44,30 @@ int swa_prefill(const void* q, const void* k, const void* v, void* out, int T, i
   return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH;
 }
 
+int swa_prefill_dilated(const void* q, const void* k, const void* v, void* out, int T, int W,
+                        int Hq, int Hkv, int d, int mode, float scale, int dilation, int dtype,
+                        void* stream) {
+  if (!q || !k || !v || !out) return SWA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SWA_ERR_INVALID_ARG;
+  if (T <= 0 || W <= 0 || Hq <= 0 || Hkv <= 0 || dilation <= 0) return SWA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return SWA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return SWA_ERR_INVALID_ARG;
+  if (!supported_d(d) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
+  if (mode != SWA_CAUSAL && mode != SWA_SYMMETRIC) return SWA_ERR_UNSUPPORTED;
+  // a tile's 64 rows, dilation rows apart, are addressed with 32-bit byte offsets
+  if ((long long)dilation * d * elem_bytes(dtype) * 64 > 2147483647LL) return SWA_ERR_UNSUPPORTED;
+  // workgroup counts: 16-row blocks (fp32); 128-row blocks of each residue class (bf16)
+  if ((long long)((T + 15) / 16) * Hq > kMaxGrid) return SWA_ERR_UNSUPPORTED;
+  const long long class_rows = (T + (long long)dilation - 1) / dilation;
+  if ((class_rows + 127) / 128 * Hq * (long long)dilation > kMaxGrid) return SWA_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e =
+      (dtype == SWA_BF16)
+          ? swa::launch_prefill_dilated_bf16(q, k, v, out, T, W, Hq, Hkv, d, mode, scale, dilation, s)
+          : swa::launch_prefill_dilated_f32(q, k, v, out, T, W, Hq, Hkv, d, mode, scale, dilation, s);
+  return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH;
+}
+
 int swa_cache_append(void* k_ring, void* v_ring, const int32_t* pos, const void* k_new,
                      const void* v_new, int B, int Hkv, int W, int d, int dtype, void* stream) {
   if (!k_ring || !v_ring || !pos || !k_new || !v_new) return SWA_ERR_INVALID_ARG;

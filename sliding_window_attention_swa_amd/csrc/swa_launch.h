@@ -17,6 +17,15 @@ hipError_t launch_prefill_f32(const void* q, const void* k, const void* v, void*
                               int W, int Hq, int Hkv, int d, int mode, float scale,
                               hipStream_t stream);
 
+// Dilated window (dilation dil >= 1; dil = 1 is swa_prefill's window).
+hipError_t launch_prefill_dilated_bf16(const void* q, const void* k, const void* v, void* out,
+                                       int T, int W, int Hq, int Hkv, int d, int mode,
+                                       float scale, int dil, hipStream_t stream);
+
+hipError_t launch_prefill_dilated_f32(const void* q, const void* k, const void* v, void* out,
+                                      int T, int W, int Hq, int Hkv, int d, int mode, float scale,
+                                      int dil, hipStream_t stream);
+
 // Chunk of n tokens per sequence against its ring plus itself (causal).
 hipError_t launch_prefill_chunk_bf16(const void* q, const void* k, const void* v,
                                      const void* k_ring, const void* v_ring, const int32_t* pos,

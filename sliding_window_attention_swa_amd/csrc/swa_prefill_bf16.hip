@@ -49,6 +49,13 @@
 // r < 0 is position p + r, read from ring slot (p + r) mod W (Ultralytics
 // ring-buffer paragraph).  Tiles are aligned to the chunk start, so a tile is
 // wholly ring or wholly chunk; the window mask adds p + r >= 0.
+//
+// Dilated windows (MODES 3 and 4; aivaro answer 629, section 4.2): key j is
+// visible from query i when i - j is a multiple of the dilation d and
+// (i - j) / d lies in the plain window.  Rows of different residues mod d
+// never meet, so a workgroup takes the rows r, r + d, r + 2d, ... of one
+// residue class as a sequence of its own (row stride d * D) and runs the
+// plain causal or symmetric window on it.
 
 #include "swa_device.h"
 #include "swa_launch.h"
@@ -102,18 +109,20 @@ __device__ __forceinline__ int swz(int row) {
 template <int D>
 constexpr int kWavesPerSimd = D == 128 ? 2 : (D == 64 ? 3 : 5);
 
-// MODE: 0 causal, 1 symmetric, 2 causal chunk continuing a ring cache (T is
-// then the chunk length; kring/vring/pos/hkv_seq are used by MODE 2 only).
+// MODE: 0 causal, 1 symmetric, 2 causal chunk continuing a ring cache (Tseq
+// is then the chunk length; kring/vring/pos/hkv_seq are used by MODE 2 only),
+// 3 causal dilated, 4 symmetric dilated (dil is used by MODES 3 and 4 only).
 template <int D, int MODE>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>, kWavesPerSimd<D>)))
 void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-                         const __bf16* __restrict__ v, __bf16* __restrict__ out, int T, int W,
-                         int Hq, int Hkv, float c, uint32_t qsign, int n_qtiles,
+                         const __bf16* __restrict__ v, __bf16* __restrict__ out, int Tseq,
+                         int W, int Hq, int Hkv, float c, uint32_t qsign, int n_qtiles,
                          const __bf16* __restrict__ kring, const __bf16* __restrict__ vring,
-                         const int32_t* __restrict__ pos, int hkv_seq) {
-  constexpr bool kCausal = MODE != 1;
+                         const int32_t* __restrict__ pos, int hkv_seq, int dil) {
+  constexpr bool kCausal = MODE != 1 && MODE != 4;
   constexpr bool kChunk = MODE == 2;
+  constexpr bool kDil = MODE == 3 || MODE == 4;
   using Gm = Geo<D>;
   constexpr int ROWB = Gm::ROWB, TILEB = Gm::TILEB, KS = Gm::KS;
   constexpr int MD = Gm::MD, NLD = Gm::NLD;
@@ -133,8 +142,16 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   const int hg = id % G;
   const int rest = id / G;
   const int qt = rest % n_qtiles;
-  const int kvh = rest / n_qtiles;
+  int kvh = rest / n_qtiles;
+  int cls = 0;  // dilated modes: the residue class of this workgroup's rows
+  if constexpr (kDil) {
+    cls = kvh % dil;
+    kvh /= dil;
+  }
   const int h = kvh * G + hg;
+  // T rows of stride RS elements: the sequence itself, or one residue class
+  const int T = kDil ? (Tseq - cls + dil - 1) / dil : Tseq;
+  const int RS = kDil ? dil * D : D;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -144,9 +161,14 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   const int qw0 = q0 + wave * 32;
   const int qi = qw0 + (lane & 31);  // the query row this lane owns
 
-  const __bf16* qh = q + (size_t)h * T * D;
-  const __bf16* kh = k + (size_t)kvh * T * D;
-  const __bf16* vh = v + (size_t)kvh * T * D;
+  const __bf16* qh = q + (size_t)h * Tseq * D + (size_t)cls * D;
+  const __bf16* kh = k + (size_t)kvh * Tseq * D + (size_t)cls * D;
+  const __bf16* vh = v + (size_t)kvh * Tseq * D + (size_t)cls * D;
+  // a dilated class may be shorter than the longest one (or empty): a query
+  // block past its end has nothing to do (uniform over the workgroup)
+  if constexpr (kDil) {
+    if (q0 >= T) return;
+  }
 
   // chunk mode: position of the chunk's first token; the lowest key is -pstart
   int pstart = 0;
@@ -154,7 +176,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     pstart = pos[kvh / hkv_seq];
     if (pstart < 0) {  // inactive sequence: zero rows (uniform over the workgroup)
       if (qi < T) {
-        __bf16* orow = out + ((size_t)h * T + qi) * D;
+        __bf16* orow = out + ((size_t)h * Tseq + qi) * D;
 #pragma unroll
         for (int md = 0; md < Gm::MD; ++md)
 #pragma unroll
@@ -193,13 +215,13 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   bf16x8 qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    uint4 r = make_uint4(0, 0, 0, 0);
-    if (qi < T) r = *reinterpret_cast<const uint4*>(qh + (size_t)qi * D + ks * 16 + half * 8);
-    r.x ^= qsign;
-    r.y ^= qsign;
-    r.z ^= qsign;
-    r.w ^= qsign;
-    qf[ks] = __builtin_bit_cast(bf16x8, r);
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (qi < T) w = *reinterpret_cast<const uint4*>(qh + (size_t)qi * RS + ks * 16 + half * 8);
+    w.x ^= qsign;
+    w.y ^= qsign;
+    w.z ^= qsign;
+    w.w ^= qsign;
+    qf[ks] = __builtin_bit_cast(bf16x8, w);
   }
 
   // ---- global -> LDS tile copy with direct (buffer -> LDS) loads.  Load j
@@ -243,15 +265,16 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
       }
     }
     const int last = T - 1 - kbase;  // last valid row of this tile
-    const int bytes = (last + 1) * ROWB;
+    const int RSB = RS * 2;           // bytes between consecutive rows
+    const int bytes = kDil ? min(last, kBN - 1) * RSB + ROWB : (last + 1) * ROWB;
     const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(kh + (size_t)kbase * D), 0, bytes, kBufferFlags);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kh + (size_t)kbase * RS), 0, bytes, kBufferFlags);
     const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(vh + (size_t)kbase * D), 0, bytes, kBufferFlags);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vh + (size_t)kbase * RS), 0, bytes, kBufferFlags);
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       const int wbase = (j * kThreads + wave * 64) * 16;
-      const int off = min(src_row[j], last) * ROWB + src_off[j];
+      const int off = min(src_row[j], last) * RSB + src_off[j];
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass mishandles this builtin
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(Kdst + wbase), 16, off, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(Vdst + wbase), 16, off, 0, 0, 0);
@@ -517,7 +540,12 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   const float l_tot = l_part + __shfl_xor(l_part, 32);
   if (qi < T) {
     const float inv = 1.0f / l_tot;
-    __bf16* orow = out + ((size_t)h * T + qi) * D;
+    __bf16* orow;
+    if constexpr (kDil) {
+      orow = out + (size_t)h * Tseq * D + (size_t)cls * D + (size_t)qi * RS;
+    } else {
+      orow = out + ((size_t)h * T + qi) * D;
+    }
 #pragma unroll
     for (int md = 0; md < MD; ++md) {
 #pragma unroll
@@ -723,24 +751,53 @@ hipError_t launch_short(const void* q, const void* k, const void* v, void* out, 
   return hipGetLastError();
 }
 
+// softmax constant c = scale * log2(e) > 0; a negative scale is folded into
+// Q's sign bits (bf16 negation is exact); scale 0 makes every weight equal
+// while masked logits stay at -inf
+void fold_scale(float scale, float& c, uint32_t& qsign) {
+  c = scale * kLog2e;
+  qsign = 0;
+  if (c < 0.f) {
+    c = -c;
+    qsign = 0x80008000u;
+  }
+  if (c == 0.f) c = 1.0e-30f;
+}
+
 template <int D, int MODE>
 hipError_t launch(const void* q, const void* k, const void* v, void* out, int T, int W, int Hq,
                   int Hkv, float scale, hipStream_t stream) {
   const int n_qtiles = (T + kBM - 1) / kBM;
   const long long nwg = (long long)n_qtiles * Hq;
-  float c = scale * kLog2e;
-  uint32_t qsign = 0;
-  if (c < 0.f) {  // fold the sign into Q (bf16 negation is exact)
-    c = -c;
-    qsign = 0x80008000u;
-  }
-  if (c == 0.f) c = 1.0e-30f;  // all weights equal; masked logits stay at -inf
+  float c;
+  uint32_t qsign;
+  fold_scale(scale, c, qsign);
   if (short_window(W, MODE)) return launch_short<D, MODE>(q, k, v, out, T, W, Hq, Hkv, c, qsign, stream);
   hipLaunchKernelGGL((prefill_bf16_kernel<D, MODE>), dim3((unsigned)nwg), dim3(kThreads), 0,
                      stream, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                      static_cast<const __bf16*>(v), static_cast<__bf16*>(out), T, W, Hq, Hkv, c,
                      qsign, n_qtiles, static_cast<const __bf16*>(nullptr),
-                     static_cast<const __bf16*>(nullptr), static_cast<const int32_t*>(nullptr), 1);
+                     static_cast<const __bf16*>(nullptr), static_cast<const int32_t*>(nullptr), 1,
+                     1);
+  return hipGetLastError();
+}
+
+// Dilated windows: one workgroup per (query head, residue class, query block
+// of the class's rows); the longest class has ceil(T / dil) rows.
+template <int D, int MODE>
+hipError_t launch_dilated(const void* q, const void* k, const void* v, void* out, int T, int W,
+                          int Hq, int Hkv, float scale, int dil, hipStream_t stream) {
+  const int n_qtiles = ((T + dil - 1) / dil + kBM - 1) / kBM;
+  const long long nwg = (long long)n_qtiles * Hq * dil;
+  float c;
+  uint32_t qsign;
+  fold_scale(scale, c, qsign);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, MODE>), dim3((unsigned)nwg), dim3(kThreads), 0,
+                     stream, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+                     static_cast<const __bf16*>(v), static_cast<__bf16*>(out), T, W, Hq, Hkv, c,
+                     qsign, n_qtiles, static_cast<const __bf16*>(nullptr),
+                     static_cast<const __bf16*>(nullptr), static_cast<const int32_t*>(nullptr), 1,
+                     dil);
   return hipGetLastError();
 }
 
@@ -753,18 +810,14 @@ hipError_t launch_chunk(const void* q, const void* k, const void* v, const void*
                         int Hq, int Hkv, float scale, hipStream_t stream) {
   const int n_qtiles = (n + kBM - 1) / kBM;
   const long long nwg = (long long)n_qtiles * Hq * B;
-  float c = scale * kLog2e;
-  uint32_t qsign = 0;
-  if (c < 0.f) {
-    c = -c;
-    qsign = 0x80008000u;
-  }
-  if (c == 0.f) c = 1.0e-30f;
+  float c;
+  uint32_t qsign;
+  fold_scale(scale, c, qsign);
   hipLaunchKernelGGL((prefill_bf16_kernel<D, 2>), dim3((unsigned)nwg), dim3(kThreads), 0, stream,
                      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                      static_cast<const __bf16*>(v), static_cast<__bf16*>(out), n, W, Hq * B,
                      Hkv * B, c, qsign, n_qtiles, static_cast<const __bf16*>(k_ring),
-                     static_cast<const __bf16*>(v_ring), pos, Hkv);
+                     static_cast<const __bf16*>(v_ring), pos, Hkv, 1);
   return hipGetLastError();
 }
 
@@ -777,6 +830,20 @@ hipError_t launch_prefill_chunk_bf16(const void* q, const void* k, const void* v
   if (d == 32) return launch_chunk<32>(q, k, v, k_ring, v_ring, pos, out, B, n, W, Hq, Hkv, scale, stream);
   if (d == 64) return launch_chunk<64>(q, k, v, k_ring, v_ring, pos, out, B, n, W, Hq, Hkv, scale, stream);
   return launch_chunk<128>(q, k, v, k_ring, v_ring, pos, out, B, n, W, Hq, Hkv, scale, stream);
+}
+
+hipError_t launch_prefill_dilated_bf16(const void* q, const void* k, const void* v, void* out,
+                                       int T, int W, int Hq, int Hkv, int d, int mode,
+                                       float scale, int dil, hipStream_t stream) {
+  if (dil == 1) return launch_prefill_bf16(q, k, v, out, T, W, Hq, Hkv, d, mode, scale, stream);
+  if (mode == 0) {
+    if (d == 32) return launch_dilated<32, 3>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream);
+    if (d == 64) return launch_dilated<64, 3>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream);
+    return launch_dilated<128, 3>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream);
+  }
+  if (d == 32) return launch_dilated<32, 4>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream);
+  if (d == 64) return launch_dilated<64, 4>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream);
+  return launch_dilated<128, 4>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream);
 }
 
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* out, int T,

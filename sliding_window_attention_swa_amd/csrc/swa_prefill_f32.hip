@@ -12,6 +12,9 @@
 // p + i of its sequence; its keys r = j - p in [max(-p, i-W+1), i] come from
 // ring slot (p + r) mod W when r < 0 (Ultralytics ring-buffer paragraph) and
 // from chunk row r otherwise.
+//
+// Dilated windows (dil > 1; aivaro answer 629, section 4.2): the row takes
+// every dil-th key, j = i - m * dil for m in the plain window's offsets.
 
 #include "swa_device.h"
 #include "swa_launch.h"
@@ -23,13 +26,14 @@ constexpr int kRowsPerBlock = 16;
 constexpr int kLanesPerRow = 16;
 
 // MODE: 0 causal, 1 symmetric, 2 causal chunk continuing a ring cache
-// (kring/vring/pos/hkv_seq are used by MODE 2 only).
+// (kring/vring/pos/hkv_seq are used by MODE 2 only).  dil: key stride of a
+// dilated window in MODES 0 and 1 (1 for the plain window and for MODE 2).
 template <int D, int MODE>
 __global__ __launch_bounds__(256) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ out, int T, int W, int Hq, int Hkv, float scale, int n_rowblocks,
     const float* __restrict__ kring, const float* __restrict__ vring,
-    const int32_t* __restrict__ pos, int hkv_seq) {
+    const int32_t* __restrict__ pos, int hkv_seq, int dil) {
   constexpr int DPL = D / kLanesPerRow;
   const int h = blockIdx.x / n_rowblocks;
   const int i = (blockIdx.x % n_rowblocks) * kRowsPerBlock + threadIdx.x / kLanesPerRow;
@@ -58,12 +62,15 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
     acc[e] = 0.f;
   }
   int lo, hi;
-  if (MODE != 1) {
+  if (MODE == 2) {
     lo = max(-pstart, i - W + 1);
     hi = i;
+  } else if (MODE == 0) {
+    lo = i - dil * min(W - 1, i / dil);
+    hi = i;
   } else {
-    lo = max(0, i - W / 2);
-    hi = min(T - 1, i + W / 2);
+    lo = i - dil * min(W / 2, i / dil);
+    hi = i + dil * min(W / 2, (T - 1 - i) / dil);
   }
   // chunk mode: ring slot of key lo (pstart + lo >= 0), advanced with the key
   unsigned slot = 0;
@@ -75,7 +82,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
     vrh = vring + (size_t)kvh * W * D + c * DPL;
   }
   float m = -INFINITY, l = 0.f;
-  for (int j = lo; j <= hi; ++j) {
+  for (int j = lo; j <= hi; j += dil) {
     const float* kr;
     const float* vr;
     if (MODE == 2 && j < 0) {  // a ring position
@@ -107,7 +114,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
 
 template <int D, int MODE>
 hipError_t launch(const void* q, const void* k, const void* v, void* out, int T, int W, int Hq,
-                  int Hkv, float scale, hipStream_t stream) {
+                  int Hkv, float scale, int dil, hipStream_t stream) {
   const int n_rowblocks = (T + kRowsPerBlock - 1) / kRowsPerBlock;
   const long long nwg = (long long)n_rowblocks * Hq;
   hipLaunchKernelGGL((prefill_f32_kernel<D, MODE>), dim3((unsigned)nwg),
@@ -115,7 +122,8 @@ hipError_t launch(const void* q, const void* k, const void* v, void* out, int T,
                      stream, static_cast<const float*>(q), static_cast<const float*>(k),
                      static_cast<const float*>(v), static_cast<float*>(out), T, W, Hq, Hkv,
                      scale, n_rowblocks, static_cast<const float*>(nullptr),
-                     static_cast<const float*>(nullptr), static_cast<const int32_t*>(nullptr), 1);
+                     static_cast<const float*>(nullptr), static_cast<const int32_t*>(nullptr), 1,
+                     dil);
   return hipGetLastError();
 }
 
@@ -130,7 +138,7 @@ hipError_t launch_chunk(const void* q, const void* k, const void* v, const void*
                      static_cast<const float*>(k), static_cast<const float*>(v),
                      static_cast<float*>(out), n, W, Hq * B, Hkv * B, scale, n_rowblocks,
                      static_cast<const float*>(k_ring), static_cast<const float*>(v_ring), pos,
-                     Hkv);
+                     Hkv, 1);
   return hipGetLastError();
 }
 
@@ -145,17 +153,23 @@ hipError_t launch_prefill_chunk_f32(const void* q, const void* k, const void* v,
   return launch_chunk<128>(q, k, v, k_ring, v_ring, pos, out, B, n, W, Hq, Hkv, scale, stream);
 }
 
+hipError_t launch_prefill_dilated_f32(const void* q, const void* k, const void* v, void* out,
+                                      int T, int W, int Hq, int Hkv, int d, int mode, float scale,
+                                      int dil, hipStream_t stream) {
+  if (mode == 0) {
+    if (d == 32) return launch<32, 0>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream);
+    if (d == 64) return launch<64, 0>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream);
+    return launch<128, 0>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream);
+  }
+  if (d == 32) return launch<32, 1>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream);
+  if (d == 64) return launch<64, 1>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream);
+  return launch<128, 1>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream);
+}
+
 hipError_t launch_prefill_f32(const void* q, const void* k, const void* v, void* out, int T,
                               int W, int Hq, int Hkv, int d, int mode, float scale,
                               hipStream_t stream) {
-  if (mode == 0) {
-    if (d == 32) return launch<32, 0>(q, k, v, out, T, W, Hq, Hkv, scale, stream);
-    if (d == 64) return launch<64, 0>(q, k, v, out, T, W, Hq, Hkv, scale, stream);
-    return launch<128, 0>(q, k, v, out, T, W, Hq, Hkv, scale, stream);
-  }
-  if (d == 32) return launch<32, 1>(q, k, v, out, T, W, Hq, Hkv, scale, stream);
-  if (d == 64) return launch<64, 1>(q, k, v, out, T, W, Hq, Hkv, scale, stream);
-  return launch<128, 1>(q, k, v, out, T, W, Hq, Hkv, scale, stream);
+  return launch_prefill_dilated_f32(q, k, v, out, T, W, Hq, Hkv, d, mode, scale, 1, stream);
 }
 
 }  // namespace swa

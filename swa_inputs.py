@@ -37,6 +37,9 @@ WORKLOADS = {
             W=4096, d=128, dtype=BF16, mode=CAUSAL, pos_lo=4096, pos_hi=32768),
     5: dict(name="Longformer symmetric prefill", kind="prefill", B=4, Hq=12, Hkv=12,
             T=4096, W=512, d=64, dtype=BF16, mode=SYMMETRIC),
+    # the dilated Longformer window of aivaro section 4.2 (W=512, dilation 2)
+    7: dict(name="Longformer dilated symmetric prefill", kind="prefill", B=4, Hq=12, Hkv=12,
+            T=4096, W=512, d=64, dtype=BF16, mode=SYMMETRIC, dilation=2),
     # serving-style chunked prefill: 4 sequences, each continuing with a
     # 2048-token chunk after at least W tokens are already in its ring
     6: dict(name="Mistral-7B chunked prefill", kind="chunk", B=4, Hq=32, Hkv=8, n=2048,

@@ -36,7 +36,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "swa_prefill", "swa_cache_append", "swa_decode", "swa_decode_workspace_bytes",
-        "swa_status_string", "swa_cache_append_chunk", "swa_prefill_chunk"])
+        "swa_status_string", "swa_cache_append_chunk", "swa_prefill_chunk",
+        "swa_prefill_dilated"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -61,6 +62,23 @@ def prefill(lib, q=P, k=P, v=P, out=P, T=16, W=4, Hq=4, Hkv=2, d=64, mode=0, sca
 ])
 def test_prefill_rejects(lib, kw, status):
     assert prefill(lib, **kw) == status
+
+
+def prefill_dilated(lib, q=P, k=P, v=P, out=P, T=16, W=4, Hq=4, Hkv=2, d=64, mode=0, scale=0.125,
+                    dil=2, dtype=1):
+    return lib.swa_prefill_dilated(q, k, v, out, T, W, Hq, Hkv, d, mode, scale, dil, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(out=None), INVALID), (dict(k=MIS), INVALID),
+    (dict(T=0), INVALID), (dict(W=0), INVALID), (dict(Hq=6, Hkv=4), INVALID),
+    (dict(dil=0), INVALID), (dict(dil=-2), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(d=48), UNSUPPORTED), (dict(mode=2), UNSUPPORTED), (dict(dtype=9), UNSUPPORTED),
+    (dict(dil=2**17, d=128), UNSUPPORTED),  # 64 strided rows beyond 32-bit byte offsets
+    (dict(T=2**30, Hq=2**10, Hkv=1, dil=1), UNSUPPORTED),
+])
+def test_prefill_dilated_rejects(lib, kw, status):
+    assert prefill_dilated(lib, **kw) == status
 
 
 def append(lib, kr=P, vr=P, pos=P, kn=P, vn=P, B=2, Hkv=2, W=8, d=64, dtype=1):

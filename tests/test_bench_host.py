@@ -1,0 +1,74 @@
+"""CPU tests of bench.py's host logic: the work counts its figures divide by
+(in-window pairs, FLOPs, algorithmic bytes) against the oracle's masks and
+brute force, the traffic read-back guard, and the one-GPU refusal."""
+
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import swa_inputs as si
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+@pytest.mark.parametrize("T,W", [(16, 4), (16, 16), (50, 7), (7, 50), (1, 1)])
+def test_causal_pairs_are_the_mask_count(T, W):
+    assert bench.band_pairs_causal(T, W) == int(oracle.window_mask(T, W, oracle.CAUSAL).sum())
+    assert bench.band_pairs(T, W, 0) == bench.band_pairs_causal(T, W)
+
+
+@pytest.mark.parametrize("T,W,mode,dil", [(50, 7, 1, 1), (53, 8, 1, 2), (40, 100, 1, 3),
+                                          (50, 7, 0, 3), (61, 5, 0, 4), (9, 4, 1, 11)])
+def test_band_pairs_are_the_mask_count(T, W, mode, dil):
+    assert bench.band_pairs(T, W, mode, dil) == int(oracle.dilated_mask(T, W, mode, dil).sum())
+
+
+def test_prefill_and_decode_work_of_the_workloads():
+    flops, bytes_ = bench.prefill_work()
+    assert flops == 962106228736  # 4 * 128 * 58,722,304 pairs * 32 heads
+    assert bytes_ == 335544320    # Q, K, V, O in bf16
+    pos = np.array([4096, 5000, 10, 0], dtype=np.int32)
+    flops, kv, qo = bench.decode_work(pos)
+    rows = 4096 + 4096 + 11 + 1
+    c = si.WORKLOADS[4]
+    assert kv == rows * c["Hkv"] * c["d"] * 4
+    assert flops == 4 * c["d"] * rows * c["Hq"]
+
+
+def test_chunk_work_by_brute_force():
+    c = dict(si.WORKLOADS[6], B=3, n=9, W=5, d=8, Hq=4, Hkv=2)
+    pos = np.array([0, 2, 40])
+    flops, bytes_ = bench.chunk_work(c, pos)
+    keys = 0
+    ring_rows = 0
+    for p in pos:
+        for i in range(c["n"]):
+            P = p + i
+            keys += len(range(max(0, P - c["W"] + 1), P + 1))
+        ring_rows += len(range(max(0, p - c["W"] + 1), p))  # ring positions some row reads
+    assert flops == 4 * c["d"] * keys * c["Hq"]
+    assert bytes_ == 2 * c["d"] * (c["B"] * c["n"] * (2 * c["Hq"] + 2 * c["Hkv"])
+                                   + 2 * c["Hkv"] * ring_rows)
+
+
+def test_traffic_is_null_for_another_source(tmp_path, monkeypatch):
+    f = tmp_path / "t.md"
+    f.write_text("traffic_bytes_per_launch: 123\ntraffic_kernel_sha256: %s\n"
+                 % bench.source_hash(bench.PREFILL_SOURCE))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.read_traffic("", bench.PREFILL_SOURCE) == 123
+    f.write_text("traffic_bytes_per_launch: 123\ntraffic_kernel_sha256: 00\n")
+    assert bench.read_traffic("", bench.PREFILL_SOURCE) is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
