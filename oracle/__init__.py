@@ -34,4 +34,7 @@ from .swa_ref import (  # noqa: F401
     dilated_mask,
     attention_dilated_dense,
     attention_dilated_rows,
+    global_mask,
+    attention_global_dense,
+    attention_global_rows,
 )

@@ -46,7 +46,10 @@ Readings of points the pages leave open (each also listed in the design doc):
   * dilated window (aivaro section 4.2, whose example numbers disagree with
     each other under the other reading): the window keeps its number of keys
     and spaces them d apart, so key j is allowed when (i - j) / d is a whole
-    number inside the undilated window.
+    number inside the undilated window;
+  * global tokens (aivaro section 4.3): added to the window as whole rows and
+    columns of the mask; in the causal mode the added pairs keep j <= i, so
+    global tokens at the first positions are attention sinks.
 """
 
 import math
@@ -429,6 +432,67 @@ def attention_dilated_rows(q, k, v, W, mode, scale, dilation, b, h, rows):
             m = np.arange(-(W // 2), W // 2 + 1)
         keys = i - dilation * m
         keys = np.sort(keys[(keys >= 0) & (keys < T)])
+        qi = np.asarray(q[b, h, i], dtype=np.float64)
+        kk = np.asarray(k[b, g, keys], dtype=np.float64)
+        vv = np.asarray(v[b, g, keys], dtype=np.float64)
+        sc = scale * (kk @ qi)
+        e = np.exp(sc - sc.max())
+        res[n] = (e / e.sum()) @ vv
+    return res
+
+
+# --------------------------------------------------------------------------
+# Sliding window plus global tokens
+# --------------------------------------------------------------------------
+
+def global_mask(T, W, mode, global_pos):
+    """Boolean [T, T] mask of the window plus global tokens.
+
+    aivaro section 4.3 (Longformer global attention) and robocikowo's global
+    tokens entry: a global token attends to every token and every token
+    attends to it, on top of the sliding window.  In the causal mode the
+    added pairs keep j <= i (no token sees a later one).  global_pos lists
+    distinct positions in [0, T).
+    """
+    m = window_mask(T, W, mode).copy()
+    g = np.zeros(T, dtype=bool)
+    g[np.asarray(global_pos, dtype=np.int64)] = True
+    extra = g[:, None] | g[None, :]
+    if mode == CAUSAL:
+        extra &= np.tri(T, dtype=bool)
+    return m | extra
+
+
+def attention_global_dense(q, k, v, W, mode, scale, global_pos):
+    """Dense [T, T] scores plus the additive form of global_mask."""
+    q, k, v = _as64(q, k, v)
+    B, Hq, Hkv, T, d = _check_shapes(q, k, v)
+    M = np.where(global_mask(T, W, mode, global_pos), 0.0, -np.inf)
+    out = np.empty((B, Hq, T, d))
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            S = scale * (q[b, h] @ k[b, g].T) + M
+            out[b, h] = _softmax_rows(S) @ v[b, g]
+    return out
+
+
+def attention_global_rows(q, k, v, W, mode, scale, global_pos, b, h, rows):
+    """Selected query rows of one (b, h) over exactly their keys: the
+    window, the global keys (j <= i when causal), or, for a global row, every
+    key (j <= i when causal).  Returns float64 [len(rows), d]."""
+    B, Hq, T, d = q.shape
+    g = kv_head(h, Hq, k.shape[1])
+    gset = set(int(x) for x in global_pos)
+    res = np.empty((len(rows), d))
+    for n, i in enumerate(rows):
+        i = int(i)
+        if i in gset:
+            keys = np.arange(0, i + 1) if mode == CAUSAL else np.arange(T)
+        else:
+            lo, hi = band(i, T, W, mode)
+            extra = [x for x in gset if (x <= i or mode != CAUSAL) and not lo <= x <= hi]
+            keys = np.sort(np.concatenate([np.arange(lo, hi + 1), np.array(extra, dtype=np.int64)]))
         qi = np.asarray(q[b, h, i], dtype=np.float64)
         kk = np.asarray(k[b, g, keys], dtype=np.float64)
         vv = np.asarray(v[b, g, keys], dtype=np.float64)

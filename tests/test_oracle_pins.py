@@ -489,3 +489,96 @@ def test_dilated_rows_agree_with_dense(mode):
     for h in range(4):
         got = oracle.attention_dilated_rows(q, k, v, W, mode, 0.5, dil, 0, h, rows)
         np.testing.assert_allclose(got, dense[0, h, rows], rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------- global tokens
+
+@pytest.mark.parametrize("T,W,Hq,Hkv", [(20, 4, 2, 1), (33, 7, 4, 2)])
+def test_all_global_is_full_attention(T, W, Hq, Hkv):
+    """Every token global: the library's full attention (bidirectional, or
+    causal in the causal mode)."""
+    d = 8
+    q, k, v = rand((1, Hq, T, d), 100), rand((1, Hkv, T, d), 101), rand((1, Hkv, T, d), 102)
+    allg = np.arange(T)
+    got = oracle.attention_global_dense(q, k, v, W, SYMMETRIC, 0.3, allg)
+    np.testing.assert_allclose(got, sdpa(q, k, v, 0.3), rtol=0, atol=1e-12)
+    got = oracle.attention_global_dense(q, k, v, W, CAUSAL, 0.3, allg)
+    np.testing.assert_allclose(got, sdpa(q, k, v, 0.3, is_causal=True), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", [CAUSAL, SYMMETRIC])
+def test_no_global_is_the_window(mode):
+    T, d = 25, 8
+    q, k, v = rand((1, 2, T, d), 103), rand((1, 1, T, d), 104), rand((1, 1, T, d), 105)
+    want = sdpa(q, k, v, 0.4, mask=torch_band(T, 6, mode))  # library
+    got = oracle.attention_global_dense(q, k, v, 6, mode, 0.4, [])
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode,T,W,gpos", [(SYMMETRIC, 40, 6, [0]), (SYMMETRIC, 40, 6, [0, 17, 39]),
+                                           (CAUSAL, 40, 5, [0, 1, 2]), (CAUSAL, 31, 4, [3, 20])])
+def test_global_pair_count_closed_form(mode, T, W, gpos):
+    """|window U rows(G) U cols(G)| by inclusion-exclusion: the window, plus
+    each global row and column (T each, or its causal part), minus what the
+    window already holds, minus the doubly counted (global, global) pairs."""
+    win = oracle.window_mask(T, W, mode)
+    g = np.zeros(T, dtype=bool)
+    g[gpos] = True
+    if mode == SYMMETRIC:
+        rows_cols = 2 * len(gpos) * T - len(gpos) ** 2
+        overlap = int(win[g, :].sum() + win[:, g].sum() - win[np.ix_(g, g)].sum())
+    else:
+        # causal: row i of a global token adds keys 0..i, column j adds queries j..T-1
+        rows_cols = sum(i + 1 for i in gpos) + sum(T - j for j in gpos) \
+            - sum(1 for a in gpos for b in gpos if b <= a)
+        overlap = int(win[g, :].sum() + win[:, g].sum() - win[np.ix_(g, g)].sum())
+    want = int(win.sum()) + rows_cols - overlap
+    assert int(oracle.global_mask(T, W, mode, gpos).sum()) == want
+
+
+def test_global_cost_is_linear_per_token():
+    """Each global token adds at most 2T - 1 pairs (its row and column): the
+    O(n) extra work per global token of aivaro section 4.3."""
+    T, W = 300, 32
+    base = int(oracle.window_mask(T, W, SYMMETRIC).sum())
+    for G in (1, 5, 10):
+        gpos = list(range(0, T, T // G))[:G]
+        extra = int(oracle.global_mask(T, W, SYMMETRIC, gpos).sum()) - base
+        assert extra <= G * (2 * T - 1)
+
+
+@pytest.mark.parametrize("mode", [CAUSAL, SYMMETRIC])
+def test_global_rows_agree_with_dense(mode):
+    T, W = 45, 6
+    gpos = [0, 9, 10, 44]
+    q, k, v = rand((1, 4, T, 8), 106), rand((1, 2, T, 8), 107), rand((1, 2, T, 8), 108)
+    dense = oracle.attention_global_dense(q, k, v, W, mode, 0.5, gpos)
+    rows = [0, 1, 5, 9, 10, 11, 20, 43, 44]
+    for h in range(4):
+        got = oracle.attention_global_rows(q, k, v, W, mode, 0.5, gpos, 0, h, rows)
+        np.testing.assert_allclose(got, dense[0, h, rows], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", [CAUSAL, SYMMETRIC])
+def test_global_token_row_is_full_attention(mode):
+    """A global token's own row attends to every key (every earlier key in
+    the causal mode): the library's full-attention row."""
+    T, gpos = 30, [4, 21]
+    q, k, v = rand((1, 2, T, 8), 112), rand((1, 2, T, 8), 113), rand((1, 2, T, 8), 114)
+    got = oracle.attention_global_dense(q, k, v, 3, mode, 0.6, gpos)
+    full = sdpa(q, k, v, 0.6, is_causal=mode == CAUSAL)
+    np.testing.assert_allclose(got[:, :, gpos], full[:, :, gpos], rtol=0, atol=1e-12)
+
+
+def test_mutant_global_columns_only_is_caught():
+    """Forgetting the global rows (tokens attend to the global token, but it
+    does not attend to everything) fails the global-row pin."""
+    T, g = 20, 5
+    q, k, v = rand((1, 1, T, 8), 109), rand((1, 1, T, 8), 110), rand((1, 1, T, 8), 111)
+    M = oracle.window_mask(T, 4, SYMMETRIC).copy()
+    M[:, g] = True
+    S = 0.3 * (q[0, 0] @ k[0, 0].T) + np.where(M, 0.0, -np.inf)
+    P = np.exp(S - S.max(axis=1, keepdims=True))
+    wrong = (P / P.sum(axis=1, keepdims=True)) @ v[0, 0]
+    full = sdpa(q, k, v, 0.3)[0, 0]
+    assert np.abs(wrong[g] - full[g]).max() > 1e-3
