@@ -113,6 +113,41 @@ int swa_prefill_dilated(const void* q, const void* k, const void* v, void* out, 
                         void* stream);
 
 /*
+ * swa_prefill_global - windowed attention plus global tokens.
+ *
+ * aivaro.ru answer 629, section 4.3 (Longformer global attention) and the
+ * robocikowo glossary's global-tokens entry: a few chosen tokens attend to
+ * every token, and every token attends to them, on top of the sliding
+ * window.  With G global positions p_1 < ... < p_G:
+ *   - a global row i = p_t attends to every key j (j <= i when causal);
+ *   - any other row i attends to its window plus the global keys
+ *     (those with j <= i when causal).
+ * Causal global tokens at the first positions are attention sinks.
+ * G = 0 is swa_prefill.  The same positions apply to every sequence of the
+ * batch (batch folded into the heads as for swa_prefill).
+ *
+ * Computed in two passes on `stream`: the windowed kernel visits the global
+ * keys as extra tiles (skipping those inside a row's window), then the
+ * split-K full-row pass of swa_decode writes the G global rows.
+ *
+ *   Arguments, layouts and errors as swa_prefill, plus
+ *   global_pos  device int32 [G], strictly increasing positions in [0, T)
+ *               (not checked on the host; entries outside [0, T) are
+ *               ignored, repeated or unsorted entries give unspecified rows,
+ *               never an access outside the buffers).  May be NULL when G = 0.
+ *   G >= 0.
+ *   workspace   device scratch of at least
+ *               swa_prefill_global_workspace_bytes(T, Hq, G, d) bytes when
+ *               G > 0 (partials of the global rows); no initialisation
+ *               needed; concurrent calls need distinct workspaces.
+ *               SWA_ERR_WORKSPACE if missing or too small.
+ *   T * d * element size < 2^31.
+ */
+int swa_prefill_global(const void* q, const void* k, const void* v, void* out, int T, int W,
+                       int Hq, int Hkv, int d, int mode, float scale, const int32_t* global_pos,
+                       int G, void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
+/*
  * swa_cache_append - write one new K/V row per sequence into the ring cache.
  *
  *   k_ring[b, :, pos[b] mod W, :] = k_new[b, :, :]   (and the same for v)
@@ -208,6 +243,10 @@ int swa_cache_append_chunk(void* k_ring, void* v_ring, const int32_t* pos, const
 int swa_prefill_chunk(const void* q, const void* k, const void* v, const void* k_ring,
                       const void* v_ring, const int32_t* pos, void* out, int B, int n, int W,
                       int Hq, int Hkv, int d, float scale, int dtype, void* stream);
+
+/* Workspace bytes swa_prefill_global needs for these sizes (Hq with the batch
+ * folded in; 0 for invalid sizes or G = 0). */
+size_t swa_prefill_global_workspace_bytes(int T, int Hq, int G, int d);
 
 /* Workspace bytes swa_decode needs for these sizes (0 for invalid sizes). */
 size_t swa_decode_workspace_bytes(int B, int Hq, int W, int d);

@@ -53,6 +53,8 @@ def load():
     lib.swa_prefill.restype = i
     lib.swa_prefill_dilated.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
     lib.swa_prefill_dilated.restype = i
+    lib.swa_prefill_global.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i, vp, sz, i, vp]
+    lib.swa_prefill_global.restype = i
     lib.swa_cache_append.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.swa_cache_append.restype = i
     lib.swa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
@@ -61,6 +63,8 @@ def load():
     lib.swa_cache_append_chunk.restype = i
     lib.swa_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
     lib.swa_prefill_chunk.restype = i
+    lib.swa_prefill_global_workspace_bytes.argtypes = [i, i, i, i]
+    lib.swa_prefill_global_workspace_bytes.restype = sz
     lib.swa_decode_workspace_bytes.argtypes = [i, i, i, i]
     lib.swa_decode_workspace_bytes.restype = sz
     lib.swa_status_string.argtypes = [i]
@@ -153,6 +157,39 @@ def prefill_dilated(q, k, v, W, dilation, mode=CAUSAL, scale=None, out=None, str
     return out
 
 
+def prefill_global(q, k, v, W, global_pos, mode=CAUSAL, scale=None, out=None, workspace=None,
+                   stream=None):
+    """Windowed attention plus global tokens at the positions `global_pos`
+    (device int32 [G], strictly increasing): they attend to every key and
+    every row attends to them (j <= i when causal).  Returns out [B, Hq, T, d]."""
+    import torch
+    _check(q, "q", 4)
+    _check(k, "k", 4, q.dtype)
+    _check(v, "v", 4, q.dtype)
+    _check(global_pos, "global_pos", 1, torch.int32)
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, T, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("shape mismatch q%s k%s v%s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", 4, q.dtype)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    G = global_pos.shape[0]
+    if workspace is None:
+        workspace = global_workspace(T, B * Hq, G, d, q.device)
+    st = load().swa_prefill_global(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), T,
+                                   int(W), B * Hq, B * Hkv, d, int(mode), float(scale),
+                                   global_pos.data_ptr() if G else None, G, workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), _dtype_code(q),
+                                   _stream(stream))
+    _raise("swa_prefill_global", st)
+    return out
+
+
 def cache_append(k_ring, v_ring, pos, k_new, v_new, stream=None):
     """Write k_new/v_new [B, Hkv, d] into slot pos[b] mod W of the rings."""
     import torch
@@ -179,6 +216,16 @@ def decode_workspace(B, Hq, W, d, device="cuda"):
     """A zero-filled decode workspace (reusable across calls without clearing)."""
     import torch
     return torch.zeros(max(decode_workspace_bytes(B, Hq, W, d), 16), dtype=torch.uint8, device=device)
+
+
+def global_workspace_bytes(T, Hq, G, d):
+    return int(load().swa_prefill_global_workspace_bytes(int(T), int(Hq), int(G), int(d)))
+
+
+def global_workspace(T, Hq, G, d, device="cuda"):
+    """A workspace for prefill_global (Hq with the batch folded in)."""
+    import torch
+    return torch.zeros(max(global_workspace_bytes(T, Hq, G, d), 16), dtype=torch.uint8, device=device)
 
 
 def decode(q, k_ring, v_ring, pos, scale=None, out=None, workspace=None, stream=None):

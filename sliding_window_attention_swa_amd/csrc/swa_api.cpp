@@ -68,6 +68,38 @@ int swa_prefill_dilated(const void* q, const void* k, const void* v, void* out, 
   return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH;
 }
 
+int swa_prefill_global(const void* q, const void* k, const void* v, void* out, int T, int W,
+                       int Hq, int Hkv, int d, int mode, float scale, const int32_t* global_pos,
+                       int G, void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  if (G == 0)
+    return swa_prefill(q, k, v, out, T, W, Hq, Hkv, d, mode, scale, dtype, stream);
+  if (!q || !k || !v || !out || !global_pos) return SWA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(global_pos))
+    return SWA_ERR_INVALID_ARG;
+  if (T <= 0 || W <= 0 || Hq <= 0 || Hkv <= 0 || G < 0) return SWA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return SWA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return SWA_ERR_INVALID_ARG;
+  if (!supported_d(d) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
+  if (mode != SWA_CAUSAL && mode != SWA_SYMMETRIC) return SWA_ERR_UNSUPPORTED;
+  // global keys are gathered with 32-bit byte offsets into a head's K/V
+  if ((long long)T * d * elem_bytes(dtype) > 2147483647LL) return SWA_ERR_UNSUPPORTED;
+  if ((long long)((T + 15) / 16) * Hq > kMaxGrid) return SWA_ERR_UNSUPPORTED;
+  const int S = swa::global_splits(G, Hq, T);
+  if ((long long)G * Hq * S > kMaxGrid) return SWA_ERR_UNSUPPORTED;
+  const size_t need = swa_prefill_global_workspace_bytes(T, Hq, G, d);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return SWA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = (dtype == SWA_BF16)
+                     ? swa::launch_prefill_global_window_bf16(q, k, v, out, T, W, Hq, Hkv, d, mode,
+                                                              scale, global_pos, G, s)
+                     : swa::launch_prefill_global_window_f32(q, k, v, out, T, W, Hq, Hkv, d, mode,
+                                                             scale, global_pos, G, s);
+  if (e != hipSuccess) return SWA_ERR_LAUNCH;
+  e = swa::launch_global_rows(q, k, v, global_pos, out, G, T, Hq, Hkv, d, mode, scale, dtype,
+                              static_cast<float*>(workspace), s);
+  return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH;
+}
+
 int swa_cache_append(void* k_ring, void* v_ring, const int32_t* pos, const void* k_new,
                      const void* v_new, int B, int Hkv, int W, int d, int dtype, void* stream) {
   if (!k_ring || !v_ring || !pos || !k_new || !v_new) return SWA_ERR_INVALID_ARG;
@@ -124,6 +156,12 @@ int swa_prefill_chunk(const void* q, const void* k, const void* v, const void* k
           : swa::launch_prefill_chunk_f32(q, k, v, k_ring, v_ring, pos, out, B, n, W, Hq, Hkv, d,
                                           scale, s);
   return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH;
+}
+
+size_t swa_prefill_global_workspace_bytes(int T, int Hq, int G, int d) {
+  if (T <= 0 || Hq <= 0 || G <= 0 || !supported_d(d)) return 0;
+  const int S = swa::global_splits(G, Hq, T);
+  return (size_t)G * Hq * S * (size_t)(d + 2) * sizeof(float);
 }
 
 size_t swa_decode_workspace_bytes(int B, int Hq, int W, int d) {

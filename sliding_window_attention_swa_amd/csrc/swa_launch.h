@@ -26,6 +26,28 @@ hipError_t launch_prefill_dilated_f32(const void* q, const void* k, const void* 
                                       int T, int W, int Hq, int Hkv, int d, int mode, float scale,
                                       int dil, hipStream_t stream);
 
+// Window plus global keys for every row (the global rows are left for
+// launch_global_rows).
+hipError_t launch_prefill_global_window_bf16(const void* q, const void* k, const void* v,
+                                             void* out, int T, int W, int Hq, int Hkv, int d,
+                                             int mode, float scale, const int32_t* gpos, int ngl,
+                                             hipStream_t stream);
+
+hipError_t launch_prefill_global_window_f32(const void* q, const void* k, const void* v,
+                                            void* out, int T, int W, int Hq, int Hkv, int d,
+                                            int mode, float scale, const int32_t* gpos, int ngl,
+                                            hipStream_t stream);
+
+// Number of key chunks the global-row pass splits each row into.
+int global_splits(int G, int Hq, int T);
+
+// The rows of the global tokens: each attends to every key (every earlier
+// key when causal).  Workspace: G * Hq * global_splits(G, Hq, T) partial
+// records of d + 2 floats.
+hipError_t launch_global_rows(const void* q, const void* k, const void* v, const int32_t* gpos,
+                              void* out, int ngl, int T, int Hq, int Hkv, int d, int mode,
+                              float scale, int dtype, float* workspace, hipStream_t stream);
+
 // Chunk of n tokens per sequence against its ring plus itself (causal).
 hipError_t launch_prefill_chunk_bf16(const void* q, const void* k, const void* v,
                                      const void* k_ring, const void* v_ring, const int32_t* pos,

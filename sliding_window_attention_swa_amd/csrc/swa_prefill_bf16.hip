@@ -56,6 +56,14 @@
 // never meet, so a workgroup takes the rows r, r + d, r + 2d, ... of one
 // residue class as a sequence of its own (row stride d * D) and runs the
 // plain causal or symmetric window on it.
+//
+// Global tokens (MODES 5 and 6; aivaro answer 629, section 4.3): every row
+// also attends to the G global keys (those at or before it in the causal
+// mode).  They are visited after the window's tiles, as extra tiles whose
+// rows are gathered from the global positions; a global key already inside a
+// row's window is masked there so that no key counts twice.  The global rows
+// themselves attend to every key and are written by the full-row pass of the
+// decode kernel afterwards.
 
 #include "swa_device.h"
 #include "swa_launch.h"
@@ -108,21 +116,29 @@ __device__ __forceinline__ int swz(int row) {
 // windows.
 template <int D>
 constexpr int kWavesPerSimd = D == 128 ? 2 : (D == 64 ? 3 : 5);
+// the global-key modes carry one more tile body; at d = 32 it needs the
+// registers of four waves per SIMD rather than five
+template <int D, int MODE>
+constexpr int kWavesFor = (MODE == 5 || MODE == 6) && D == 32 ? 4 : kWavesPerSimd<D>;
 
 // MODE: 0 causal, 1 symmetric, 2 causal chunk continuing a ring cache (Tseq
 // is then the chunk length; kring/vring/pos/hkv_seq are used by MODE 2 only),
-// 3 causal dilated, 4 symmetric dilated (dil is used by MODES 3 and 4 only).
+// 3 causal dilated, 4 symmetric dilated (dil is used by MODES 3 and 4 only),
+// 5 causal and 6 symmetric window plus the ngl global keys at gpos (MODES 5
+// and 6 only).
 template <int D, int MODE>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>, kWavesPerSimd<D>)))
+__attribute__((amdgpu_waves_per_eu(kWavesFor<D, MODE>, kWavesFor<D, MODE>)))
 void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                          const __bf16* __restrict__ v, __bf16* __restrict__ out, int Tseq,
                          int W, int Hq, int Hkv, float c, uint32_t qsign, int n_qtiles,
                          const __bf16* __restrict__ kring, const __bf16* __restrict__ vring,
-                         const int32_t* __restrict__ pos, int hkv_seq, int dil) {
-  constexpr bool kCausal = MODE != 1 && MODE != 4;
+                         const int32_t* __restrict__ pos, int hkv_seq, int dil,
+                         const int32_t* __restrict__ gpos, int ngl) {
+  constexpr bool kCausal = MODE != 1 && MODE != 4 && MODE != 6;
   constexpr bool kChunk = MODE == 2;
   constexpr bool kDil = MODE == 3 || MODE == 4;
+  constexpr bool kGlobal = MODE == 5 || MODE == 6;
   using Gm = Geo<D>;
   constexpr int ROWB = Gm::ROWB, TILEB = Gm::TILEB, KS = Gm::KS;
   constexpr int MD = Gm::MD, NLD = Gm::NLD;
@@ -132,6 +148,8 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   __shared__ __attribute__((aligned(1024))) char lds_v0[TILEB];
   __shared__ __attribute__((aligned(1024))) char lds_k1[TILEB];
   __shared__ __attribute__((aligned(1024))) char lds_v1[TILEB];
+  // global modes: the positions of the global key tile held in each stage
+  __shared__ __attribute__((aligned(16))) int lds_gp[2][kGlobal ? kBN : 1];
 
   // ---- which (query head, query block) this workgroup owns
   const int G = Hq / Hkv;
@@ -203,6 +221,8 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     kt0 = lo / kBN;
   }
   const int kt1 = hi / kBN;
+  // global modes: the global key tiles follow the window's, as kt1+1 .. kt_end
+  const int kt_end = kGlobal ? kt1 + (ngl + kBN - 1) / kBN : kt1;
 
   // this wave's rows and key range
   const bool wave_active = qw0 < T;
@@ -240,6 +260,34 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   }
   auto load_tile = [&](char* Kdst, char* Vdst, int kt) __attribute__((always_inline)) {
     const int kbase = kt * kBN;
+    if constexpr (kGlobal) {
+      if (kt > kt1) {
+        // a global key tile: row j holds the key at gpos[t0 + j]; rows past
+        // the last global key, and positions outside [0, T), re-read a valid
+        // row (masked in global_tile)
+        const int t0 = (kt - kt1 - 1) * kBN;
+        // the tile's 64 global positions, for the mask (same stage discipline
+        // as the K/V tiles: written after the barrier that frees the stage)
+        if (tid < kBN) lds_gp[(kt - kt0) & 1][tid] = gpos[min(t0 + tid, ngl - 1)];
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc((void*)kh, 0, T * ROWB, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc((void*)vh, 0, T * ROWB, kBufferFlags);
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) {
+          const int wbase = (j * kThreads + wave * 64) * 16;
+          const int gp = min(max(gpos[min(t0 + src_row[j], ngl - 1)], 0), T - 1);
+          const int off = gp * ROWB + src_off[j];
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass mishandles this builtin
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(Kdst + wbase), 16, off, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(Vdst + wbase), 16, off, 0, 0, 0);
+#else
+          (void)rk, (void)rv, (void)wbase, (void)off;
+#endif
+        }
+        return;
+      }
+    }
     if constexpr (kChunk) {
       if (kbase < 0) {
         // a ring tile: key r = kbase + row is position pstart + r < pstart, in
@@ -506,13 +554,63 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     }
   };
 
+  // A tile of gathered global keys (global modes): key t0 + kl sits at
+  // gpos[t0 + kl] and counts for this row only when it is outside the row's
+  // window (the window tiles already counted it) and, in the causal mode, not
+  // after the row.  The lane's 32 keys are kl = 8 * g + 4 * half + e
+  // (g = 0..7, e = 0..3), i.e. score register r of block mb holds key group
+  // g = 4 * mb + r / 4; their verdicts are packed into one bit each first.
+  // When at most 32 global keys are left, only the first 32-key block is
+  // computed.
+  auto global_tile = [&](const char* Ks, const char* Vs, int t0, const int* gp_tile) __attribute__((always_inline)) {
+    uint32_t okbits = 0;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const int4 gp4 = *reinterpret_cast<const int4*>(gp_tile + 8 * g + 4 * half);
+      const int gpv[4] = {gp4.x, gp4.y, gp4.z, gp4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int idx = t0 + 8 * g + 4 * half + e;
+        const int gp = gpv[e];
+        const int diff = qi - gp;
+        const bool in_window = kCausal ? (diff >= 0 && diff < W) : (diff >= -hw && diff <= hw);
+        bool ok = idx < ngl && gp >= 0 && gp < T && !in_window;
+        if (kCausal) ok = ok && diff >= 0;
+        okbits |= (uint32_t)ok << (4 * g + e);
+      }
+    }
+    // one 32-key block at a time, and only the blocks holding global keys
+    const int nblk = ngl - t0 > 32 ? 2 : 1;
+#pragma unroll 1
+    for (int mb = 0; mb < nblk; ++mb) {
+      f32x16 sb = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(Ks, mb, ks), qf[ks], sb, 0, 0, 0);
+      const uint32_t bits = okbits >> (16 * mb);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (!((bits >> r) & 1u)) sb[r] = -INFINITY;
+      }
+      bf16x8 pb[2];
+      float lb;
+      probs(sb, -m_ref * c, pb, lb);
+      if (raise_max(&sb, 1, lb)) probs(sb, -m_ref * c, pb, lb);
+      l_part += lb;
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(Vs, md, 2 * mb + kk), pb[kk], o[md], 0, 0, 0);
+      }
+    }
+  };
+
   // One tile: wait for its loads (issued during the previous tile) and for
   // every wave to be done with the other stage, refill that stage with the
   // next tile, then consume this one.
   auto step = [&](const char* Ks, const char* Vs, char* Kn, char* Vn, int kt) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    if (kt < kt1) load_tile(Kn, Vn, kt + 1);
+    if (kt < kt_end) load_tile(Kn, Vn, kt + 1);
     const int k0 = kt * kBN;
     if (!(wave_active && k0 <= whi && k0 + kBN - 1 >= wlo)) return;
     bool full;
@@ -533,6 +631,19 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     step(lds_k0, lds_v0, lds_k1, lds_v1, kt);
     if (kt + 1 > kt1) break;
     step(lds_k1, lds_v1, lds_k0, lds_v0, kt + 1);
+  }
+  // global modes: the global key tiles, in a loop of their own (inside the
+  // window loop their code would raise its register pressure); the last
+  // window step already requested the first of them.  Tile kt sits in stage
+  // (kt - kt0) & 1.
+  if constexpr (kGlobal) {
+    for (int kt = kt1 + 1; kt <= kt_end; ++kt) {
+      const int st = (kt - kt0) & 1;
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __syncthreads();
+      if (kt < kt_end) load_tile(st ? lds_k0 : lds_k1, st ? lds_v0 : lds_v1, kt + 1);
+      if (wave_active) global_tile(st ? lds_k1 : lds_k0, st ? lds_v1 : lds_v0, (kt - kt1 - 1) * kBN, lds_gp[st]);
+    }
   }
 
   // ---- epilogue: divide by the row sum, round to bf16, store.  The
@@ -778,7 +889,7 @@ hipError_t launch(const void* q, const void* k, const void* v, void* out, int T,
                      static_cast<const __bf16*>(v), static_cast<__bf16*>(out), T, W, Hq, Hkv, c,
                      qsign, n_qtiles, static_cast<const __bf16*>(nullptr),
                      static_cast<const __bf16*>(nullptr), static_cast<const int32_t*>(nullptr), 1,
-                     1);
+                     1, static_cast<const int32_t*>(nullptr), 0);
   return hipGetLastError();
 }
 
@@ -797,7 +908,26 @@ hipError_t launch_dilated(const void* q, const void* k, const void* v, void* out
                      static_cast<const __bf16*>(v), static_cast<__bf16*>(out), T, W, Hq, Hkv, c,
                      qsign, n_qtiles, static_cast<const __bf16*>(nullptr),
                      static_cast<const __bf16*>(nullptr), static_cast<const int32_t*>(nullptr), 1,
-                     dil);
+                     dil, static_cast<const int32_t*>(nullptr), 0);
+  return hipGetLastError();
+}
+
+// Window plus global keys (the global rows are written by a later pass).
+template <int D, int MODE>
+hipError_t launch_global(const void* q, const void* k, const void* v, void* out, int T, int W,
+                         int Hq, int Hkv, float scale, const int32_t* gpos, int ngl,
+                         hipStream_t stream) {
+  const int n_qtiles = (T + kBM - 1) / kBM;
+  const long long nwg = (long long)n_qtiles * Hq;
+  float c;
+  uint32_t qsign;
+  fold_scale(scale, c, qsign);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, MODE>), dim3((unsigned)nwg), dim3(kThreads), 0,
+                     stream, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+                     static_cast<const __bf16*>(v), static_cast<__bf16*>(out), T, W, Hq, Hkv, c,
+                     qsign, n_qtiles, static_cast<const __bf16*>(nullptr),
+                     static_cast<const __bf16*>(nullptr), static_cast<const int32_t*>(nullptr), 1,
+                     1, gpos, ngl);
   return hipGetLastError();
 }
 
@@ -817,7 +947,8 @@ hipError_t launch_chunk(const void* q, const void* k, const void* v, const void*
                      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                      static_cast<const __bf16*>(v), static_cast<__bf16*>(out), n, W, Hq * B,
                      Hkv * B, c, qsign, n_qtiles, static_cast<const __bf16*>(k_ring),
-                     static_cast<const __bf16*>(v_ring), pos, Hkv, 1);
+                     static_cast<const __bf16*>(v_ring), pos, Hkv, 1,
+                     static_cast<const int32_t*>(nullptr), 0);
   return hipGetLastError();
 }
 
@@ -830,6 +961,20 @@ hipError_t launch_prefill_chunk_bf16(const void* q, const void* k, const void* v
   if (d == 32) return launch_chunk<32>(q, k, v, k_ring, v_ring, pos, out, B, n, W, Hq, Hkv, scale, stream);
   if (d == 64) return launch_chunk<64>(q, k, v, k_ring, v_ring, pos, out, B, n, W, Hq, Hkv, scale, stream);
   return launch_chunk<128>(q, k, v, k_ring, v_ring, pos, out, B, n, W, Hq, Hkv, scale, stream);
+}
+
+hipError_t launch_prefill_global_window_bf16(const void* q, const void* k, const void* v,
+                                             void* out, int T, int W, int Hq, int Hkv, int d,
+                                             int mode, float scale, const int32_t* gpos, int ngl,
+                                             hipStream_t stream) {
+  if (mode == 0) {
+    if (d == 32) return launch_global<32, 5>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, stream);
+    if (d == 64) return launch_global<64, 5>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, stream);
+    return launch_global<128, 5>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, stream);
+  }
+  if (d == 32) return launch_global<32, 6>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, stream);
+  if (d == 64) return launch_global<64, 6>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, stream);
+  return launch_global<128, 6>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, stream);
 }
 
 hipError_t launch_prefill_dilated_bf16(const void* q, const void* k, const void* v, void* out,

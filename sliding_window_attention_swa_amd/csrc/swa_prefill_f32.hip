@@ -15,6 +15,11 @@
 //
 // Dilated windows (dil > 1; aivaro answer 629, section 4.2): the row takes
 // every dil-th key, j = i - m * dil for m in the plain window's offsets.
+//
+// Global tokens (MODES 5 causal, 6 symmetric; aivaro section 4.3): after its
+// window the row also takes each global key outside the window (not after
+// the row when causal).  The global rows themselves are written afterwards
+// by the full-row pass.
 
 #include "swa_device.h"
 #include "swa_launch.h"
@@ -26,15 +31,18 @@ constexpr int kRowsPerBlock = 16;
 constexpr int kLanesPerRow = 16;
 
 // MODE: 0 causal, 1 symmetric, 2 causal chunk continuing a ring cache
-// (kring/vring/pos/hkv_seq are used by MODE 2 only).  dil: key stride of a
-// dilated window in MODES 0 and 1 (1 for the plain window and for MODE 2).
+// (kring/vring/pos/hkv_seq are used by MODE 2 only), 5 causal and 6
+// symmetric window plus the ngl global keys at gpos.  dil: key stride of a
+// dilated window in MODES 0 and 1 (1 otherwise).
 template <int D, int MODE>
 __global__ __launch_bounds__(256) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ out, int T, int W, int Hq, int Hkv, float scale, int n_rowblocks,
     const float* __restrict__ kring, const float* __restrict__ vring,
-    const int32_t* __restrict__ pos, int hkv_seq, int dil) {
+    const int32_t* __restrict__ pos, int hkv_seq, int dil, const int32_t* __restrict__ gpos,
+    int ngl) {
   constexpr int DPL = D / kLanesPerRow;
+  constexpr bool kCausal = MODE != 1 && MODE != 6;
   const int h = blockIdx.x / n_rowblocks;
   const int i = (blockIdx.x % n_rowblocks) * kRowsPerBlock + threadIdx.x / kLanesPerRow;
   const int c = threadIdx.x % kLanesPerRow;
@@ -65,7 +73,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
   if (MODE == 2) {
     lo = max(-pstart, i - W + 1);
     hi = i;
-  } else if (MODE == 0) {
+  } else if (kCausal) {
     lo = i - dil * min(W - 1, i / dil);
     hi = i;
   } else {
@@ -82,17 +90,8 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
     vrh = vring + (size_t)kvh * W * D + c * DPL;
   }
   float m = -INFINITY, l = 0.f;
-  for (int j = lo; j <= hi; j += dil) {
-    const float* kr;
-    const float* vr;
-    if (MODE == 2 && j < 0) {  // a ring position
-      kr = krh + (size_t)slot * D;
-      vr = vrh + (size_t)slot * D;
-      slot = slot + 1 == (unsigned)W ? 0u : slot + 1;
-    } else {
-      kr = kh + (size_t)j * D;
-      vr = vh + (size_t)j * D;
-    }
+  // one key: score, running maximum and sum, accumulate its value row
+  auto visit = [&](const float* kr, const float* vr) {
     float s = 0.f;
 #pragma unroll
     for (int e = 0; e < DPL; ++e) s = fmaf(qv[e], kr[e], s);
@@ -106,6 +105,28 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
 #pragma unroll
     for (int e = 0; e < DPL; ++e) acc[e] = fmaf(p, vr[e], acc[e] * alpha);
     m = m_new;
+  };
+  for (int j = lo; j <= hi; j += dil) {
+    const float* kr;
+    const float* vr;
+    if (MODE == 2 && j < 0) {  // a ring position
+      kr = krh + (size_t)slot * D;
+      vr = vrh + (size_t)slot * D;
+      slot = slot + 1 == (unsigned)W ? 0u : slot + 1;
+    } else {
+      kr = kh + (size_t)j * D;
+      vr = vh + (size_t)j * D;
+    }
+    visit(kr, vr);
+  }
+  if constexpr (MODE == 5 || MODE == 6) {
+    for (int t = 0; t < ngl; ++t) {
+      const int gp = gpos[t];
+      const int diff = i - gp;
+      const bool in_window = kCausal ? (diff >= 0 && diff < W) : (diff >= -(W / 2) && diff <= W / 2);
+      if (gp < 0 || gp >= T || in_window || (kCausal && diff < 0)) continue;
+      visit(kh + (size_t)gp * D, vh + (size_t)gp * D);
+    }
   }
   const float inv = 1.0f / l;
 #pragma unroll
@@ -123,7 +144,7 @@ hipError_t launch(const void* q, const void* k, const void* v, void* out, int T,
                      static_cast<const float*>(v), static_cast<float*>(out), T, W, Hq, Hkv,
                      scale, n_rowblocks, static_cast<const float*>(nullptr),
                      static_cast<const float*>(nullptr), static_cast<const int32_t*>(nullptr), 1,
-                     dil);
+                     dil, static_cast<const int32_t*>(nullptr), 0);
   return hipGetLastError();
 }
 
@@ -138,11 +159,40 @@ hipError_t launch_chunk(const void* q, const void* k, const void* v, const void*
                      static_cast<const float*>(k), static_cast<const float*>(v),
                      static_cast<float*>(out), n, W, Hq * B, Hkv * B, scale, n_rowblocks,
                      static_cast<const float*>(k_ring), static_cast<const float*>(v_ring), pos,
-                     Hkv, 1);
+                     Hkv, 1, static_cast<const int32_t*>(nullptr), 0);
+  return hipGetLastError();
+}
+
+template <int D, int MODE>
+hipError_t launch_global(const void* q, const void* k, const void* v, void* out, int T, int W,
+                         int Hq, int Hkv, float scale, const int32_t* gpos, int ngl,
+                         hipStream_t stream) {
+  const int n_rowblocks = (T + kRowsPerBlock - 1) / kRowsPerBlock;
+  const long long nwg = (long long)n_rowblocks * Hq;
+  hipLaunchKernelGGL((prefill_f32_kernel<D, MODE>), dim3((unsigned)nwg),
+                     dim3(kRowsPerBlock * kLanesPerRow), 0, stream, static_cast<const float*>(q),
+                     static_cast<const float*>(k), static_cast<const float*>(v),
+                     static_cast<float*>(out), T, W, Hq, Hkv, scale, n_rowblocks,
+                     static_cast<const float*>(nullptr), static_cast<const float*>(nullptr),
+                     static_cast<const int32_t*>(nullptr), 1, 1, gpos, ngl);
   return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_prefill_global_window_f32(const void* q, const void* k, const void* v,
+                                            void* out, int T, int W, int Hq, int Hkv, int d,
+                                            int mode, float scale, const int32_t* gpos, int ngl,
+                                            hipStream_t stream) {
+  if (mode == 0) {
+    if (d == 32) return launch_global<32, 5>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, stream);
+    if (d == 64) return launch_global<64, 5>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, stream);
+    return launch_global<128, 5>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, stream);
+  }
+  if (d == 32) return launch_global<32, 6>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, stream);
+  if (d == 64) return launch_global<64, 6>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, stream);
+  return launch_global<128, 6>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, stream);
+}
 
 hipError_t launch_prefill_chunk_f32(const void* q, const void* k, const void* v,
                                     const void* k_ring, const void* v_ring, const int32_t* pos,

@@ -24,6 +24,14 @@
 //     when the maximum grows by more than 2^8), merged once per workgroup
 //     through LDS; a small second kernel merges the splits with the usual
 //     log-sum-exp rule and writes the output.
+//
+// The same two kernels also write the rows of global tokens (aivaro answer
+// 629, section 4.3: a global token attends to every token): with GR != 0 a
+// workgroup takes NQ (global row t, query head) pairs of one KV head, so
+// they share every K/V read; the query of a pair is row gpos[t] of the
+// prefill queries, and the linear K/V of the sequence serve as a ring of T
+// slots of which gpos[t] + 1 (causal, GR = 1) or all T (symmetric, GR = 2)
+// are valid.
 
 #include "swa_device.h"
 #include "swa_launch.h"
@@ -40,6 +48,15 @@ constexpr int kDecodeWaves = kDecodeThreads / 64;
 #endif
 #ifndef SWA_DECODE_ITEMS
 #define SWA_DECODE_ITEMS 2048
+#endif
+#ifndef SWA_GLOBAL_ITEMS
+#define SWA_GLOBAL_ITEMS 2048
+#endif
+#ifndef SWA_GLOBAL_NQ
+#define SWA_GLOBAL_NQ 4
+#endif
+#ifndef SWA_GLOBAL_NT
+#define SWA_GLOBAL_NT 0
 #endif
 constexpr int kUnroll = SWA_DECODE_UNROLL;  // K and V rows in flight per lane
 
@@ -155,12 +172,15 @@ __device__ __forceinline__ uint4 stream_load(const E* p) {
 
 // ------------------------------------------------------------ split pass
 
-template <typename E, int D, int NQ>
+template <typename E, int D, int NQ, int GR>
 __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     const E* __restrict__ q, const E* __restrict__ k_ring, const E* __restrict__ v_ring,
     const int32_t* __restrict__ pos, E* __restrict__ out, float* __restrict__ ws_acc,
     float* __restrict__ ws_m, float* __restrict__ ws_l, int Hq, int Hkv, int W, float scale_log2,
-    int S, int chunk, int n_hchunks) {
+    int S, int chunk, int n_hchunks, int n_pairs) {
+  // GR != 0: pos holds the global positions, W is the sequence length and
+  // pair pi = hc * NQ + hq (of n_pairs = global rows * group size) is global
+  // row pi / G with query head kvh * G + pi % G
   constexpr int EPL = Elem<E>::PER16;  // elements per 16-byte load
   constexpr int LPR = D / EPL;         // lanes per ring row
   constexpr int RPW = 64 / LPR;        // rows per wave load
@@ -188,14 +208,41 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
   const int li = lane % LPR;
 
   const int p = pos[b];
-  const int nvalid = p < 0 ? 0 : (p >= W ? W : p + 1);
+  int nvalid;
+  int gph[NQ], hh[NQ], s1h[NQ];  // global rows: each pair's position, head, key end
+  if constexpr (GR != 0) {
+    nvalid = 0;
+#pragma unroll
+    for (int hq = 0; hq < NQ; ++hq) {
+      const int pi = hc * NQ + hq;
+      const int gp = pi < n_pairs ? pos[pi / G] : -1;
+      const bool ok = gp >= 0 && gp < W;  // positions outside the sequence are ignored
+      gph[hq] = ok ? gp : -1;
+      hh[hq] = kvh * G + pi % G;
+      s1h[hq] = ok ? (GR == 1 ? gp + 1 : W) : 0;
+      nvalid = max(nvalid, s1h[hq]);
+    }
+    if (nvalid == 0) return;  // no valid pair (uniform over the workgroup)
+  } else {
+    nvalid = p < 0 ? 0 : (p >= W ? W : p + 1);
+  }
   const int s0 = split * chunk;
   const int s1 = min(s0 + chunk, nvalid);
+  if constexpr (GR != 0) {
+#pragma unroll
+    for (int hq = 0; hq < NQ; ++hq) s1h[hq] = min(s0 + chunk, s1h[hq]);
+  }
 
   uint4 qraw[NQ];  // this lane's EPL query elements of each head, as stored
 #pragma unroll
-  for (int hq = 0; hq < NQ; ++hq)
-    qraw[hq] = *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + h0 + hq) * D + li * EPL);
+  for (int hq = 0; hq < NQ; ++hq) {
+    if constexpr (GR != 0) {  // row gph of the head's prefill queries
+      qraw[hq] = gph[hq] < 0 ? make_uint4(0, 0, 0, 0)
+                             : *reinterpret_cast<const uint4*>(q + ((size_t)hh[hq] * W + gph[hq]) * D + li * EPL);
+    } else {
+      qraw[hq] = *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + h0 + hq) * D + li * EPL);
+    }
+  }
   float m[NQ], l[NQ], acc[NQ][EPL];
 #pragma unroll
   for (int hq = 0; hq < NQ; ++hq) {
@@ -205,7 +252,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     for (int e = 0; e < EPL; ++e) acc[hq][e] = 0.f;
   }
 
-  const size_t ring_off = ((size_t)b * Hkv + kvh) * (size_t)W * D + li * EPL;
+  size_t ring_off;
+  if constexpr (GR != 0) {  // the sequence's linear K/V
+    ring_off = (size_t)kvh * (size_t)W * D + li * EPL;
+  } else {
+    ring_off = ((size_t)b * Hkv + kvh) * (size_t)W * D + li * EPL;
+  }
   const E* kb = k_ring + ring_off;
   const E* vb = v_ring + ring_off;
 
@@ -217,8 +269,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
       const int r = base + (u * kDecodeWaves + wave) * RPW + rg;
       valid[u] = r < s1;
       if (valid[u]) {
-        kraw[u] = stream_load(kb + (size_t)r * D);
-        vraw[u] = stream_load(vb + (size_t)r * D);
+        if constexpr (GR != 0 && !SWA_GLOBAL_NT) {  // rows the windowed pass just read
+          kraw[u] = *reinterpret_cast<const uint4*>(kb + (size_t)r * D);
+          vraw[u] = *reinterpret_cast<const uint4*>(vb + (size_t)r * D);
+        } else {
+          kraw[u] = stream_load(kb + (size_t)r * D);
+          vraw[u] = stream_load(vb + (size_t)r * D);
+        }
       } else {
         kraw[u] = make_uint4(0, 0, 0, 0);
         vraw[u] = make_uint4(0, 0, 0, 0);
@@ -235,7 +292,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
 #pragma unroll
       for (int hq = 0; hq < NQ; ++hq) {
         const float s = group_sum<LPR>(sc[u][hq]) * scale_log2;
-        sc[u][hq] = valid[u] ? s : -INFINITY;
+        if constexpr (GR != 0) {  // each pair has its own key range
+          const int r = base + (u * kDecodeWaves + wave) * RPW + rg;
+          sc[u][hq] = r < s1h[hq] ? s : -INFINITY;
+        } else {
+          sc[u][hq] = valid[u] ? s : -INFINITY;
+        }
       }
     }
     float vf[kUnroll][EPL];
@@ -288,11 +350,23 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
       a = fmaf(w, sm_acc[hq][s][dim], a);
       L = fmaf(w, sm_l[hq][s], L);
     }
-    if (S == 1) {  // no other split to merge with: finish here
-      Elem<E>::store(out + ((size_t)b * Hq + h0 + hq) * D + dim, L > 0.f ? a / L : 0.f);
-      continue;
+    size_t slot;
+    if constexpr (GR != 0) {  // the pair's position and head, recomputed (hq varies here)
+      const int pi = hc * NQ + hq;
+      const int gp = pi < n_pairs ? pos[pi / G] : -1;
+      if (gp < 0 || gp >= W) continue;
+      if (S == 1) {
+        Elem<E>::store(out + ((size_t)(kvh * G + pi % G) * W + gp) * D + dim, L > 0.f ? a / L : 0.f);
+        continue;
+      }
+      slot = ((size_t)kvh * n_pairs + pi) * S + split;
+    } else {
+      if (S == 1) {  // no other split to merge with: finish here
+        Elem<E>::store(out + ((size_t)b * Hq + h0 + hq) * D + dim, L > 0.f ? a / L : 0.f);
+        continue;
+      }
+      slot = ((size_t)b * Hq + h0 + hq) * S + split;
     }
-    const size_t slot = ((size_t)b * Hq + h0 + hq) * S + split;
     ws_acc[slot * D + dim] = a;
     if (dim == 0) {
       ws_m[slot] = M;
@@ -303,12 +377,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
 
 // ------------------------------------------------------------ split merge
 
-template <typename E, int D>
+template <typename E, int D, int GR>
 __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restrict__ ws_acc,
                                                            const float* __restrict__ ws_m,
                                                            const float* __restrict__ ws_l,
-                                                           E* __restrict__ out, int S) {
-  const size_t row = blockIdx.x;  // b * Hq + h
+                                                           E* __restrict__ out, int S,
+                                                           const int32_t* __restrict__ gpos,
+                                                           int T, int G, int n_pairs) {
+  // b * Hq + h; GR != 0: kvh * n_pairs + pi for pair pi of KV head kvh
+  const size_t row = blockIdx.x;
   const int dim = threadIdx.x;
   const float* m = ws_m + row * S;
   const float* l = ws_l + row * S;
@@ -320,52 +397,63 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
     L = fmaf(w, l[s], L);
     a = fmaf(w, ws_acc[(row * S + s) * D + dim], a);
   }
-  Elem<E>::store(out + row * D + dim, L > 0.f ? a / L : 0.f);
+  size_t orow = row * D;
+  if constexpr (GR != 0) {
+    const int kvh = (int)(row / n_pairs), pi = (int)(row % n_pairs);
+    const int p = gpos[pi / G];
+    if (p < 0 || p >= T) return;
+    orow = ((size_t)(kvh * G + pi % G) * T + p) * D;
+  }
+  Elem<E>::store(out + orow + dim, L > 0.f ? a / L : 0.f);
 }
 
-template <typename E, int D, int NQ>
+template <typename E, int D, int NQ, int GR>
 hipError_t launch_decode_t(const void* q, const void* k_ring, const void* v_ring,
                            const int32_t* pos, void* out, int B, int Hq, int Hkv, int W,
                            float scale, float* workspace, hipStream_t stream) {
-  const int S = decode_splits(B, Hq, W);
+  const int S = GR != 0 ? global_splits(B, Hq, W) : decode_splits(B, Hq, W);
   const int chunk = (W + S - 1) / S;
   const int G = Hq / Hkv;
-  const int n_hchunks = G / NQ;
+  // global rows: B (global rows) x G pairs per KV head, NQ per workgroup
+  const int n_pairs = GR != 0 ? B * G : 0;
+  const int n_hchunks = GR != 0 ? (n_pairs + NQ - 1) / NQ : G / NQ;
   const size_t rows = (size_t)B * Hq * S;
   float* ws_acc = workspace;
   float* ws_m = ws_acc + rows * D;
   float* ws_l = ws_m + rows;
-  const long long nwg = (long long)B * Hkv * n_hchunks * S;
-  hipLaunchKernelGGL((decode_split_kernel<E, D, NQ>), dim3((unsigned)nwg), dim3(kDecodeThreads), 0,
+  const long long nwg = (long long)(GR != 0 ? 1 : B) * Hkv * n_hchunks * S;
+  hipLaunchKernelGGL((decode_split_kernel<E, D, NQ, GR>), dim3((unsigned)nwg), dim3(kDecodeThreads), 0,
                      stream, static_cast<const E*>(q), static_cast<const E*>(k_ring),
                      static_cast<const E*>(v_ring), pos, static_cast<E*>(out), ws_acc, ws_m, ws_l,
-                     Hq, Hkv, W, scale * kLog2e, S, chunk, n_hchunks);
+                     Hq, Hkv, W, scale * kLog2e, S, chunk, n_hchunks, n_pairs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<E, D>), dim3((unsigned)((size_t)B * Hq)), dim3(D), 0,
-                     stream, ws_acc, ws_m, ws_l, static_cast<E*>(out), S);
+  hipLaunchKernelGGL((decode_combine_kernel<E, D, GR>), dim3((unsigned)((size_t)B * Hq)), dim3(D), 0,
+                     stream, ws_acc, ws_m, ws_l, static_cast<E*>(out), S, pos, W, G, n_pairs);
   return hipGetLastError();
 }
 
-template <typename E, int D>
+template <typename E, int D, int GR>
 hipError_t launch_decode_d(const void* q, const void* k_ring, const void* v_ring,
                            const int32_t* pos, void* out, int B, int Hq, int Hkv, int W,
                            float scale, float* workspace, hipStream_t stream) {
   const int G = Hq / Hkv;
+  if constexpr (GR != 0)  // global rows: SWA_GLOBAL_NQ pairs per workgroup
+    return launch_decode_t<E, D, SWA_GLOBAL_NQ, GR>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
   if (G % 4 == 0)
-    return launch_decode_t<E, D, 4>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
+    return launch_decode_t<E, D, 4, GR>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
   if (G % 2 == 0)
-    return launch_decode_t<E, D, 2>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
-  return launch_decode_t<E, D, 1>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
+    return launch_decode_t<E, D, 2, GR>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
+  return launch_decode_t<E, D, 1, GR>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
 }
 
-template <typename E>
+template <typename E, int GR>
 hipError_t launch_decode_e(const void* q, const void* k_ring, const void* v_ring,
                            const int32_t* pos, void* out, int B, int Hq, int Hkv, int W, int d,
                            float scale, float* workspace, hipStream_t stream) {
-  if (d == 32) return launch_decode_d<E, 32>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
-  if (d == 64) return launch_decode_d<E, 64>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
-  return launch_decode_d<E, 128>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
+  if (d == 32) return launch_decode_d<E, 32, GR>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
+  if (d == 64) return launch_decode_d<E, 64, GR>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
+  return launch_decode_d<E, 128, GR>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
 }
 
 }  // namespace
@@ -408,12 +496,40 @@ int decode_splits(int B, int Hq, int W) {
   return (int)(want < cap ? want : cap);
 }
 
+int global_splits(int G, int Hq, int T) {
+  // ~SWA_GLOBAL_ITEMS (row, head, split) items, never below 64 keys.  The
+  // pass is bound by its vector arithmetic (one dot product, exponential
+  // and d FMAs per key and pair), not by memory: finer splits (8192 items)
+  // or 8 pairs per workgroup (registers for one wave per SIMD) measured
+  // slower.  Its loads are ordinary (cached) ones: the windowed pass has just
+  // read the same K/V.
+  const long long rows = (long long)G * Hq;
+  long long want = (SWA_GLOBAL_ITEMS + rows - 1) / rows;
+  if (want < 1) want = 1;
+  const long long cap = (T + 63) / 64;
+  return (int)(want < cap ? want : cap);
+}
+
 hipError_t launch_decode(const void* q, const void* k_ring, const void* v_ring,
                          const int32_t* pos, void* out, int B, int Hq, int Hkv, int W, int d,
                          float scale, int dtype, float* workspace, hipStream_t stream) {
   if (dtype == 1)
-    return launch_decode_e<__bf16>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, d, scale, workspace, stream);
-  return launch_decode_e<float>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, d, scale, workspace, stream);
+    return launch_decode_e<__bf16, 0>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, d, scale, workspace, stream);
+  return launch_decode_e<float, 0>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, d, scale, workspace, stream);
+}
+
+hipError_t launch_global_rows(const void* q, const void* k, const void* v, const int32_t* gpos,
+                              void* out, int ngl, int T, int Hq, int Hkv, int d, int mode,
+                              float scale, int dtype, float* workspace, hipStream_t stream) {
+  // ngl "sequences" (the global rows), each against the whole K/V as a ring of T slots
+  if (dtype == 1) {
+    if (mode == 0)
+      return launch_decode_e<__bf16, 1>(q, k, v, gpos, out, ngl, Hq, Hkv, T, d, scale, workspace, stream);
+    return launch_decode_e<__bf16, 2>(q, k, v, gpos, out, ngl, Hq, Hkv, T, d, scale, workspace, stream);
+  }
+  if (mode == 0)
+    return launch_decode_e<float, 1>(q, k, v, gpos, out, ngl, Hq, Hkv, T, d, scale, workspace, stream);
+  return launch_decode_e<float, 2>(q, k, v, gpos, out, ngl, Hq, Hkv, T, d, scale, workspace, stream);
 }
 
 }  // namespace swa

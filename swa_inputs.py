@@ -40,6 +40,11 @@ WORKLOADS = {
     # the dilated Longformer window of aivaro section 4.2 (W=512, dilation 2)
     7: dict(name="Longformer dilated symmetric prefill", kind="prefill", B=4, Hq=12, Hkv=12,
             T=4096, W=512, d=64, dtype=BF16, mode=SYMMETRIC, dilation=2),
+    # Longformer with global attention (aivaro section 4.3: usually 1 to 10
+    # global tokens): [CLS] at position 0 and seven question tokens after it
+    8: dict(name="Longformer symmetric prefill + 8 global tokens", kind="prefill", B=4, Hq=12,
+            Hkv=12, T=4096, W=512, d=64, dtype=BF16, mode=SYMMETRIC,
+            global_pos=[0, 1, 2, 3, 4, 5, 6, 7]),
     # serving-style chunked prefill: 4 sequences, each continuing with a
     # 2048-token chunk after at least W tokens are already in its ring
     6: dict(name="Mistral-7B chunked prefill", kind="chunk", B=4, Hq=32, Hkv=8, n=2048,

@@ -37,7 +37,7 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "swa_prefill", "swa_cache_append", "swa_decode", "swa_decode_workspace_bytes",
         "swa_status_string", "swa_cache_append_chunk", "swa_prefill_chunk",
-        "swa_prefill_dilated"])
+        "swa_prefill_dilated", "swa_prefill_global", "swa_prefill_global_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -79,6 +79,42 @@ def prefill_dilated(lib, q=P, k=P, v=P, out=P, T=16, W=4, Hq=4, Hkv=2, d=64, mod
 ])
 def test_prefill_dilated_rejects(lib, kw, status):
     assert prefill_dilated(lib, **kw) == status
+
+
+def prefill_global(lib, q=P, k=P, v=P, out=P, T=16, W=4, Hq=4, Hkv=2, d=64, mode=0, scale=0.125,
+                   gpos=P, G=2, ws=P, ws_bytes=None, dtype=1):
+    if ws_bytes is None:
+        ws_bytes = lib.swa_prefill_global_workspace_bytes(T, Hq, G, d) if G > 0 and Hq > 0 and T > 0 else 0
+    return lib.swa_prefill_global(q, k, v, out, T, W, Hq, Hkv, d, mode, scale, gpos, G, ws,
+                                  ws_bytes, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(gpos=None), INVALID), (dict(gpos=MIS), INVALID),
+    (dict(G=-1), INVALID), (dict(T=0), INVALID), (dict(Hq=6, Hkv=4), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(d=40), UNSUPPORTED), (dict(mode=3), UNSUPPORTED),
+    (dict(dtype=4), UNSUPPORTED), (dict(ws=None), WORKSPACE), (dict(ws=MIS), WORKSPACE),
+    (dict(ws_bytes=16), WORKSPACE),
+    (dict(T=2**24, d=128), UNSUPPORTED),  # gathered rows beyond 32-bit byte offsets
+])
+def test_prefill_global_rejects(lib, kw, status):
+    assert prefill_global(lib, **kw) == status
+
+
+def test_global_workspace_bytes(lib):
+    f = lib.swa_prefill_global_workspace_bytes
+    assert f(0, 8, 2, 64) == 0 and f(100, 0, 2, 64) == 0 and f(100, 8, 0, 64) == 0
+    assert f(100, 8, 2, 48) == 0
+    for T, Hq, G, d in [(4096, 48, 8, 64), (16, 1, 1, 32), (100000, 32, 3, 128)]:
+        n = f(T, Hq, G, d)
+        assert n > 0 and n % (4 * (d + 2) * G * Hq) == 0
+        assert 1 <= n // (4 * (d + 2) * G * Hq) <= max(1, (T + 63) // 64)
+
+
+def test_prefill_global_without_globals_is_prefill_validation(lib):
+    # G = 0 takes swa_prefill's path (and its checks): no positions or workspace needed
+    assert prefill_global(lib, G=0, gpos=None, ws=None, ws_bytes=0, T=0) == INVALID
+    assert prefill_global(lib, G=0, gpos=None, ws=None, ws_bytes=0, d=48) == UNSUPPORTED
 
 
 def append(lib, kr=P, vr=P, pos=P, kn=P, vn=P, B=2, Hkv=2, W=8, d=64, dtype=1):

@@ -29,6 +29,13 @@ def test_band_pairs_are_the_mask_count(T, W, mode, dil):
     assert bench.band_pairs(T, W, mode, dil) == int(oracle.dilated_mask(T, W, mode, dil).sum())
 
 
+@pytest.mark.parametrize("T,W,mode,gpos", [(50, 7, 1, [0]), (50, 7, 0, [0, 3, 49]),
+                                           (61, 9, 1, list(range(0, 61, 5))), (40, 100, 0, [10, 20]),
+                                           (33, 1, 0, [32]), (33, 4, 1, [])])
+def test_global_pairs_are_the_mask_count(T, W, mode, gpos):
+    assert bench.global_pairs(T, W, mode, gpos) == int(oracle.global_mask(T, W, mode, gpos).sum())
+
+
 def test_prefill_and_decode_work_of_the_workloads():
     flops, bytes_ = bench.prefill_work()
     assert flops == 962106228736  # 4 * 128 * 58,722,304 pairs * 32 heads
