@@ -37,4 +37,5 @@ from .swa_ref import (  # noqa: F401
     global_mask,
     attention_global_dense,
     attention_global_rows,
+    decode_sinks,
 )

@@ -49,7 +49,10 @@ Readings of points the pages leave open (each also listed in the design doc):
     number inside the undilated window;
   * global tokens (aivaro section 4.3): added to the window as whole rows and
     columns of the mask; in the causal mode the added pairs keep j <= i, so
-    global tokens at the first positions are attention sinks.
+    global tokens at the first positions are attention sinks;
+  * decode with sinks: the first S positions are kept in sink slots beside
+    the ring and the query sees them together with its window, each
+    position once.
 """
 
 import math
@@ -500,3 +503,43 @@ def attention_global_rows(q, k, v, W, mode, scale, global_pos, b, h, rows):
         e = np.exp(sc - sc.max())
         res[n] = (e / e.sum()) @ vv
     return res
+
+
+# --------------------------------------------------------------------------
+# Decode with attention sinks
+# --------------------------------------------------------------------------
+
+def decode_sinks(q, k_ring, v_ring, k_sink, v_sink, pos, scale):
+    """One query token per sequence against its ring plus S sink slots.
+
+    Ultralytics glossary, terms section ("Pozzi di attenzione"): the first
+    tokens of a sequence soak up excess attention weight, and StreamingLLM
+    keeps them in the cache beside the window.  The query at position p sees
+    the positions {0, ..., min(S-1, p)} together with its causal window
+    [max(0, p-W+1), p], each position once: window positions come from ring
+    slot p' mod W, the sink positions before the window from k_sink[b, :, p'].
+
+    q [B, Hq, d]; rings [B, Hkv, W, d]; sinks [B, Hkv, S, d]; pos [B].
+    Returns float64 [B, Hq, d]; a sequence with p < 0 gives zeros.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, d = q.shape
+    Hkv, W = k_ring.shape[1], k_ring.shape[2]
+    S = k_sink.shape[2]
+    out = np.zeros((B, Hq, d))
+    for b, p in enumerate(np.asarray(pos).tolist()):
+        if p < 0:
+            continue
+        first = max(0, p - W + 1)
+        window = np.arange(first, p + 1)
+        sinks = np.arange(0, min(S, first))  # sink positions before the window
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            kk = np.concatenate([np.asarray(k_sink[b, g, sinks], dtype=np.float64),
+                                 np.asarray(k_ring[b, g, window % W], dtype=np.float64)])
+            vv = np.concatenate([np.asarray(v_sink[b, g, sinks], dtype=np.float64),
+                                 np.asarray(v_ring[b, g, window % W], dtype=np.float64)])
+            sc = scale * (kk @ q[b, h])
+            e = np.exp(sc - sc.max())
+            out[b, h] = (e / e.sum()) @ vv
+    return out

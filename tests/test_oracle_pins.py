@@ -582,3 +582,48 @@ def test_mutant_global_columns_only_is_caught():
     wrong = (P / P.sum(axis=1, keepdims=True)) @ v[0, 0]
     full = sdpa(q, k, v, 0.3)[0, 0]
     assert np.abs(wrong[g] - full[g]).max() > 1e-3
+
+
+# ------------------------------------------------------ attention sinks
+
+@pytest.mark.parametrize("W,S,T", [(4, 2, 16), (5, 4, 30), (8, 8, 20), (3, 1, 9), (6, 9, 25)])
+def test_decode_with_sinks_equals_library_masked_row(W, S, T):
+    """Filling the ring and the sink slots from a sequence and decoding every
+    position gives the library's attention row p with the mask 'window of p
+    or one of the first S positions' (built with torch's triangle routines)."""
+    B, Hq, Hkv, d = 2, 4, 2, 8
+    q, k, v = rand((B, Hq, T, d), 120), rand((B, Hkv, T, d), 121), rand((B, Hkv, T, d), 122)
+    mask = torch_band(T, W, CAUSAL)
+    first_cols = torch.ones(T, T, dtype=torch.bool).tril(0)
+    first_cols[:, S:] = False
+    want = sdpa(q, k, v, 0.5, mask=mask | first_cols.numpy())  # library
+    kr, vr = np.full((B, Hkv, W, d), np.nan), np.full((B, Hkv, W, d), np.nan)
+    ks, vs = k[:, :, :S].copy(), v[:, :, :S].copy()
+    for p in range(T):
+        oracle.ring_append(kr, vr, np.full(B, p), k[:, :, p], v[:, :, p])
+        got = oracle.decode_sinks(q[:, :, p], kr, vr, ks, vs, np.full(B, p), 0.5)
+        np.testing.assert_allclose(got, want[:, :, p], rtol=0, atol=1e-12)
+
+
+def test_decode_with_no_sinks_is_decode():
+    rng = np.random.default_rng(123)
+    q = rng.standard_normal((3, 4, 6))
+    kr, vr = rng.standard_normal((3, 2, 5, 6)), rng.standard_normal((3, 2, 5, 6))
+    empty = np.zeros((3, 2, 0, 6))
+    pos = np.array([-1, 2, 17])
+    np.testing.assert_allclose(oracle.decode_sinks(q, kr, vr, empty, empty, pos, 0.3),
+                               oracle.decode(q, kr, vr, pos, 0.3), rtol=0, atol=1e-13)
+
+
+def test_mutant_sinks_counted_twice_is_caught():
+    """Reading the sinks in addition to a window that already holds them
+    double-counts them and fails the library pin."""
+    W, S, T, d = 6, 3, 8, 8
+    q, k, v = rand((1, 1, T, d), 124), rand((1, 1, T, d), 125), rand((1, 1, T, d), 126)
+    p = 4  # the window [0, 4] holds all three sinks
+    keys = np.concatenate([np.arange(S), np.arange(0, p + 1)])
+    sc = 0.5 * (k[0, 0, keys] @ q[0, 0, p])
+    e = np.exp(sc - sc.max())
+    wrong = (e / e.sum()) @ v[0, 0, keys]
+    want = sdpa(q, k, v, 0.5, mask=torch_band(T, W, CAUSAL))[0, 0, p]
+    assert np.abs(wrong - want).max() > 1e-3
