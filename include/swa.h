@@ -248,6 +248,35 @@ int swa_prefill_chunk(const void* q, const void* k, const void* v, const void* k
  * folded in; 0 for invalid sizes or G = 0). */
 size_t swa_prefill_global_workspace_bytes(int T, int Hq, int G, int d);
 
+/*
+ * swa_decode_sinks - swa_decode with attention sinks kept beside the ring.
+ *
+ * Ultralytics glossary, terms section ("Pozzi di attenzione"): the first
+ * tokens of a sequence absorb excess attention weight, and StreamingLLM keeps
+ * them in the cache beside the window.  The query at position p = pos[b]
+ * attends to the positions {0, ..., min(n_sink-1, p)} together with its
+ * window [max(0, p-W+1), p], each position once: window positions from the
+ * ring (slot p' mod W), the sink positions before the window from
+ * k_sink / v_sink.  Equals row p of swa_prefill_global (causal, global
+ * positions 0 .. n_sink-1) when n_sink <= W.  n_sink = 0 is swa_decode.
+ *
+ *   Arguments, layouts and errors as swa_decode, plus
+ *   k_sink, v_sink  input [B, Hkv, n_sink, d]: row s holds the key / value of
+ *                   position s (copied from the prompt's K/V by the caller).
+ *                   May be NULL when n_sink = 0.
+ *   n_sink >= 0.
+ *   workspace       at least swa_decode_sinks_workspace_bytes(B, Hq, W, d)
+ *                   bytes (n_sink > 0).
+ */
+int swa_decode_sinks(const void* q, const void* k_ring, const void* v_ring, const void* k_sink,
+                     const void* v_sink, int n_sink, const int32_t* pos, void* out, int B, int Hq,
+                     int Hkv, int W, int d, float scale, int dtype, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* Workspace bytes swa_decode_sinks needs for these sizes (0 for invalid
+ * sizes). */
+size_t swa_decode_sinks_workspace_bytes(int B, int Hq, int W, int d);
+
 /* Workspace bytes swa_decode needs for these sizes (0 for invalid sizes). */
 size_t swa_decode_workspace_bytes(int B, int Hq, int W, int d);
 

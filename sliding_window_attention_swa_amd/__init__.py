@@ -63,6 +63,10 @@ def load():
     lib.swa_cache_append_chunk.restype = i
     lib.swa_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
     lib.swa_prefill_chunk.restype = i
+    lib.swa_decode_sinks.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.swa_decode_sinks.restype = i
+    lib.swa_decode_sinks_workspace_bytes.argtypes = [i, i, i, i]
+    lib.swa_decode_sinks_workspace_bytes.restype = sz
     lib.swa_prefill_global_workspace_bytes.argtypes = [i, i, i, i]
     lib.swa_prefill_global_workspace_bytes.restype = sz
     lib.swa_decode_workspace_bytes.argtypes = [i, i, i, i]
@@ -305,4 +309,39 @@ def prefill_chunk(q, k, v, k_ring, v_ring, pos, scale=None, out=None, stream=Non
                                   v_ring.data_ptr(), pos.data_ptr(), out.data_ptr(), B, n, W, Hq,
                                   Hkv, d, float(scale), _dtype_code(q), _stream(stream))
     _raise("swa_prefill_chunk", st)
+    return out
+
+
+def decode_sinks(q, k_ring, v_ring, k_sink, v_sink, pos, scale=None, out=None, workspace=None,
+                 stream=None):
+    """decode with attention sinks: k_sink/v_sink [B, Hkv, S, d] hold the
+    first S positions, kept beside the ring; returns out [B, Hq, d]."""
+    import torch
+    _check(q, "q", 3)
+    _check(k_ring, "k_ring", 4, q.dtype)
+    _check(v_ring, "v_ring", 4, q.dtype)
+    _check(k_sink, "k_sink", 4, q.dtype)
+    _check(v_sink, "v_sink", 4, q.dtype)
+    _check(pos, "pos", 1, torch.int32)
+    B, Hq, d = q.shape
+    Hkv, W = k_ring.shape[1], k_ring.shape[2]
+    S = k_sink.shape[2]
+    if tuple(k_ring.shape) != (B, Hkv, W, d) or tuple(v_ring.shape) != tuple(k_ring.shape) \
+            or tuple(k_sink.shape) != (B, Hkv, S, d) or tuple(v_sink.shape) != tuple(k_sink.shape) \
+            or pos.shape[0] != B:
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", 3, q.dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        n = int(load().swa_decode_sinks_workspace_bytes(B, Hq, W, d))
+        workspace = torch.zeros(max(n, 16), dtype=torch.uint8, device=q.device)
+    st = load().swa_decode_sinks(q.data_ptr(), k_ring.data_ptr(), v_ring.data_ptr(),
+                                 k_sink.data_ptr() if S else None, v_sink.data_ptr() if S else None,
+                                 S, pos.data_ptr(), out.data_ptr(), B, Hq, Hkv, W, d, float(scale),
+                                 _dtype_code(q), workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(), _stream(stream))
+    _raise("swa_decode_sinks", st)
     return out

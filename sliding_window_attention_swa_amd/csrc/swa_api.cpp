@@ -191,6 +191,38 @@ int swa_decode(const void* q, const void* k_ring, const void* v_ring, const int3
   return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH;
 }
 
+size_t swa_decode_sinks_workspace_bytes(int B, int Hq, int W, int d) {
+  if (B <= 0 || Hq <= 0 || W <= 0 || !supported_d(d)) return 0;
+  const int S = swa::decode_splits(B, Hq, W);
+  return (size_t)B * Hq * (S + 1) * (size_t)(d + 2) * sizeof(float);
+}
+
+int swa_decode_sinks(const void* q, const void* k_ring, const void* v_ring, const void* k_sink,
+                     const void* v_sink, int n_sink, const int32_t* pos, void* out, int B, int Hq,
+                     int Hkv, int W, int d, float scale, int dtype, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (n_sink == 0)
+    return swa_decode(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, d, scale, dtype, workspace,
+                      workspace_bytes, stream);
+  if (!q || !k_ring || !v_ring || !k_sink || !v_sink || !pos || !out) return SWA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_ring) || !aligned16(v_ring) || !aligned16(k_sink) ||
+      !aligned16(v_sink) || !aligned16(pos) || !aligned16(out))
+    return SWA_ERR_INVALID_ARG;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || W <= 0 || n_sink < 0) return SWA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return SWA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return SWA_ERR_INVALID_ARG;
+  if (!supported_d(d) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
+  const size_t need = swa_decode_sinks_workspace_bytes(B, Hq, W, d);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return SWA_ERR_WORKSPACE;
+  const int S = swa::decode_splits(B, Hq, W);
+  if ((long long)B * Hq * (S + 1) > kMaxGrid) return SWA_ERR_UNSUPPORTED;
+  hipError_t e = swa::launch_decode_sinks(q, k_ring, v_ring, k_sink, v_sink, n_sink, pos, out, B,
+                                          Hq, Hkv, W, d, scale, dtype,
+                                          static_cast<float*>(workspace),
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH;
+}
+
 const char* swa_status_string(int status) {
   switch (status) {
     case SWA_OK:

@@ -38,6 +38,14 @@ hipError_t launch_prefill_global_window_f32(const void* q, const void* k, const 
                                             int mode, float scale, const int32_t* gpos, int ngl,
                                             hipStream_t stream);
 
+// Decode with n_sink attention-sink slots beside the ring.  Workspace:
+// B * Hq * (decode_splits(B, Hq, W) + 1) partial records of d + 2 floats.
+hipError_t launch_decode_sinks(const void* q, const void* k_ring, const void* v_ring,
+                               const void* k_sink, const void* v_sink, int n_sink,
+                               const int32_t* pos, void* out, int B, int Hq, int Hkv, int W,
+                               int d, float scale, int dtype, float* workspace,
+                               hipStream_t stream);
+
 // Number of key chunks the global-row pass splits each row into.
 int global_splits(int G, int Hq, int T);
 

@@ -172,6 +172,12 @@ __device__ __forceinline__ uint4 stream_load(const E* p) {
 
 // ------------------------------------------------------------ split pass
 
+// GR: 0 decode, 1 / 2 rows of causal / symmetric global tokens, 3 decode
+// whose every split writes its partial (slot split of S + 1 per row; the
+// last slot holds the attention sinks' partial)
+template <int GR>
+constexpr bool kRows = GR == 1 || GR == 2;
+
 template <typename E, int D, int NQ, int GR>
 __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     const E* __restrict__ q, const E* __restrict__ k_ring, const E* __restrict__ v_ring,
@@ -210,7 +216,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
   const int p = pos[b];
   int nvalid;
   int gph[NQ], hh[NQ], s1h[NQ];  // global rows: each pair's position, head, key end
-  if constexpr (GR != 0) {
+  if constexpr (kRows<GR>) {
     nvalid = 0;
 #pragma unroll
     for (int hq = 0; hq < NQ; ++hq) {
@@ -228,7 +234,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
   }
   const int s0 = split * chunk;
   const int s1 = min(s0 + chunk, nvalid);
-  if constexpr (GR != 0) {
+  if constexpr (kRows<GR>) {
 #pragma unroll
     for (int hq = 0; hq < NQ; ++hq) s1h[hq] = min(s0 + chunk, s1h[hq]);
   }
@@ -236,7 +242,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
   uint4 qraw[NQ];  // this lane's EPL query elements of each head, as stored
 #pragma unroll
   for (int hq = 0; hq < NQ; ++hq) {
-    if constexpr (GR != 0) {  // row gph of the head's prefill queries
+    if constexpr (kRows<GR>) {  // row gph of the head's prefill queries
       qraw[hq] = gph[hq] < 0 ? make_uint4(0, 0, 0, 0)
                              : *reinterpret_cast<const uint4*>(q + ((size_t)hh[hq] * W + gph[hq]) * D + li * EPL);
     } else {
@@ -253,7 +259,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
   }
 
   size_t ring_off;
-  if constexpr (GR != 0) {  // the sequence's linear K/V
+  if constexpr (kRows<GR>) {  // the sequence's linear K/V
     ring_off = (size_t)kvh * (size_t)W * D + li * EPL;
   } else {
     ring_off = ((size_t)b * Hkv + kvh) * (size_t)W * D + li * EPL;
@@ -269,7 +275,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
       const int r = base + (u * kDecodeWaves + wave) * RPW + rg;
       valid[u] = r < s1;
       if (valid[u]) {
-        if constexpr (GR != 0 && !SWA_GLOBAL_NT) {  // rows the windowed pass just read
+        if constexpr (kRows<GR> && !SWA_GLOBAL_NT) {  // rows the windowed pass just read
           kraw[u] = *reinterpret_cast<const uint4*>(kb + (size_t)r * D);
           vraw[u] = *reinterpret_cast<const uint4*>(vb + (size_t)r * D);
         } else {
@@ -292,7 +298,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
 #pragma unroll
       for (int hq = 0; hq < NQ; ++hq) {
         const float s = group_sum<LPR>(sc[u][hq]) * scale_log2;
-        if constexpr (GR != 0) {  // each pair has its own key range
+        if constexpr (kRows<GR>) {  // each pair has its own key range
           const int r = base + (u * kDecodeWaves + wave) * RPW + rg;
           sc[u][hq] = r < s1h[hq] ? s : -INFINITY;
         } else {
@@ -351,7 +357,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
       L = fmaf(w, sm_l[hq][s], L);
     }
     size_t slot;
-    if constexpr (GR != 0) {  // the pair's position and head, recomputed (hq varies here)
+    if constexpr (kRows<GR>) {  // the pair's position and head, recomputed (hq varies here)
       const int pi = hc * NQ + hq;
       const int gp = pi < n_pairs ? pos[pi / G] : -1;
       if (gp < 0 || gp >= W) continue;
@@ -360,6 +366,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
         continue;
       }
       slot = ((size_t)kvh * n_pairs + pi) * S + split;
+    } else if constexpr (GR == 3) {  // always a partial; one more slot per row
+      slot = ((size_t)b * Hq + h0 + hq) * (S + 1) + split;
     } else {
       if (S == 1) {  // no other split to merge with: finish here
         Elem<E>::store(out + ((size_t)b * Hq + h0 + hq) * D + dim, L > 0.f ? a / L : 0.f);
@@ -372,6 +380,70 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
       ws_m[slot] = M;
       ws_l[slot] = L;
     }
+  }
+}
+
+// ------------------------------------------------------------ attention sinks
+
+// The sinks' partial of one (sequence, query head) for decode with sinks
+// (Ultralytics glossary, terms section: StreamingLLM keeps the first tokens
+// in the cache beside the window): the sink positions s < min(n_sink,
+// p - W + 1), i.e. those before the window, read from k_sink / v_sink; the
+// window's sinks are in the ring already.  One wave; written as partial S
+// of the row's S + 1 (same units as the split pass: scores times
+// scale * log2(e)).
+template <typename E, int D>
+__global__ __launch_bounds__(64) void sink_partial_kernel(
+    const E* __restrict__ q, const E* __restrict__ k_sink, const E* __restrict__ v_sink,
+    const int32_t* __restrict__ pos, float* __restrict__ ws_acc, float* __restrict__ ws_m,
+    float* __restrict__ ws_l, int Hq, int Hkv, int W, int n_sink, float scale_log2, int S) {
+  constexpr int DPL = (D + 63) / 64;  // dims per lane
+  const size_t row = blockIdx.x;      // b * Hq + h
+  const int b = (int)(row / Hq), h = (int)(row % Hq);
+  const int kvh = h / (Hq / Hkv);
+  const int lane = threadIdx.x;
+  const int p = pos[b];
+  const int ns = p < 0 ? 0 : min(n_sink, max(0, p - W + 1));
+  float qv[DPL], acc[DPL];
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) {
+    const int dim = lane + 64 * j;
+    qv[j] = dim < D ? static_cast<float>(q[row * D + dim]) : 0.f;
+    acc[j] = 0.f;
+  }
+  float m = kNegBig, l = 0.f;
+  const size_t base = ((size_t)b * Hkv + kvh) * (size_t)n_sink * D;
+  for (int s = 0; s < ns; ++s) {
+    float part = 0.f;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) {
+      const int dim = lane + 64 * j;
+      if (dim < D) part = fmaf(qv[j], static_cast<float>(k_sink[base + (size_t)s * D + dim]), part);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
+    const float sc = part * scale_log2;
+    const float m_new = fmaxf(m, sc);
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    const float pr = __builtin_amdgcn_exp2f(sc - m_new);
+    l = l * alpha + pr;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) {
+      const int dim = lane + 64 * j;
+      const float vv = dim < D ? static_cast<float>(v_sink[base + (size_t)s * D + dim]) : 0.f;
+      acc[j] = fmaf(pr, vv, acc[j] * alpha);
+    }
+    m = m_new;
+  }
+  const size_t slot = row * (S + 1) + S;
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) {
+    const int dim = lane + 64 * j;
+    if (dim < D) ws_acc[slot * D + dim] = acc[j];
+  }
+  if (lane == 0) {
+    ws_m[slot] = m;
+    ws_l[slot] = l;
   }
 }
 
@@ -398,7 +470,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
     a = fmaf(w, ws_acc[(row * S + s) * D + dim], a);
   }
   size_t orow = row * D;
-  if constexpr (GR != 0) {
+  if constexpr (kRows<GR>) {
     const int kvh = (int)(row / n_pairs), pi = (int)(row % n_pairs);
     const int p = gpos[pi / G];
     if (p < 0 || p >= T) return;
@@ -411,22 +483,23 @@ template <typename E, int D, int NQ, int GR>
 hipError_t launch_decode_t(const void* q, const void* k_ring, const void* v_ring,
                            const int32_t* pos, void* out, int B, int Hq, int Hkv, int W,
                            float scale, float* workspace, hipStream_t stream) {
-  const int S = GR != 0 ? global_splits(B, Hq, W) : decode_splits(B, Hq, W);
+  const int S = kRows<GR> ? global_splits(B, Hq, W) : decode_splits(B, Hq, W);
   const int chunk = (W + S - 1) / S;
   const int G = Hq / Hkv;
   // global rows: B (global rows) x G pairs per KV head, NQ per workgroup
-  const int n_pairs = GR != 0 ? B * G : 0;
-  const int n_hchunks = GR != 0 ? (n_pairs + NQ - 1) / NQ : G / NQ;
-  const size_t rows = (size_t)B * Hq * S;
+  const int n_pairs = kRows<GR> ? B * G : 0;
+  const int n_hchunks = kRows<GR> ? (n_pairs + NQ - 1) / NQ : G / NQ;
+  const size_t rows = (size_t)B * Hq * (GR == 3 ? S + 1 : S);
   float* ws_acc = workspace;
   float* ws_m = ws_acc + rows * D;
   float* ws_l = ws_m + rows;
-  const long long nwg = (long long)(GR != 0 ? 1 : B) * Hkv * n_hchunks * S;
+  const long long nwg = (long long)(kRows<GR> ? 1 : B) * Hkv * n_hchunks * S;
   hipLaunchKernelGGL((decode_split_kernel<E, D, NQ, GR>), dim3((unsigned)nwg), dim3(kDecodeThreads), 0,
                      stream, static_cast<const E*>(q), static_cast<const E*>(k_ring),
                      static_cast<const E*>(v_ring), pos, static_cast<E*>(out), ws_acc, ws_m, ws_l,
                      Hq, Hkv, W, scale * kLog2e, S, chunk, n_hchunks, n_pairs);
   hipError_t e = hipGetLastError();
+  if (GR == 3) return e;  // the sinks' partial and the merge follow
   if (e != hipSuccess || S == 1) return e;
   hipLaunchKernelGGL((decode_combine_kernel<E, D, GR>), dim3((unsigned)((size_t)B * Hq)), dim3(D), 0,
                      stream, ws_acc, ws_m, ws_l, static_cast<E*>(out), S, pos, W, G, n_pairs);
@@ -438,13 +511,44 @@ hipError_t launch_decode_d(const void* q, const void* k_ring, const void* v_ring
                            const int32_t* pos, void* out, int B, int Hq, int Hkv, int W,
                            float scale, float* workspace, hipStream_t stream) {
   const int G = Hq / Hkv;
-  if constexpr (GR != 0)  // global rows: SWA_GLOBAL_NQ pairs per workgroup
+  if constexpr (kRows<GR>)  // global rows: SWA_GLOBAL_NQ pairs per workgroup
     return launch_decode_t<E, D, SWA_GLOBAL_NQ, GR>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
   if (G % 4 == 0)
     return launch_decode_t<E, D, 4, GR>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
   if (G % 2 == 0)
     return launch_decode_t<E, D, 2, GR>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
   return launch_decode_t<E, D, 1, GR>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
+}
+
+template <typename E, int D>
+hipError_t launch_decode_sinks_d(const void* q, const void* k_ring, const void* v_ring,
+                                 const void* k_sink, const void* v_sink, int n_sink,
+                                 const int32_t* pos, void* out, int B, int Hq, int Hkv, int W,
+                                 float scale, float* workspace, hipStream_t stream) {
+  const int G = Hq / Hkv;
+  hipError_t e;
+  if (G % 4 == 0)
+    e = launch_decode_t<E, D, 4, 3>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
+  else if (G % 2 == 0)
+    e = launch_decode_t<E, D, 2, 3>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
+  else
+    e = launch_decode_t<E, D, 1, 3>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
+  if (e != hipSuccess) return e;
+  const int S = decode_splits(B, Hq, W);
+  const size_t rows = (size_t)B * Hq * (S + 1);
+  float* ws_acc = workspace;
+  float* ws_m = ws_acc + rows * D;
+  float* ws_l = ws_m + rows;
+  hipLaunchKernelGGL((sink_partial_kernel<E, D>), dim3((unsigned)((size_t)B * Hq)), dim3(64), 0,
+                     stream, static_cast<const E*>(q), static_cast<const E*>(k_sink),
+                     static_cast<const E*>(v_sink), pos, ws_acc, ws_m, ws_l, Hq, Hkv, W, n_sink,
+                     scale * kLog2e, S);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<E, D, 0>), dim3((unsigned)((size_t)B * Hq)), dim3(D), 0,
+                     stream, ws_acc, ws_m, ws_l, static_cast<E*>(out), S + 1,
+                     static_cast<const int32_t*>(nullptr), 0, 1, 0);
+  return hipGetLastError();
 }
 
 template <typename E, int GR>
@@ -494,6 +598,21 @@ int decode_splits(int B, int Hq, int W) {
   if (want < 1) want = 1;
   const long long cap = (W + 63) / 64;
   return (int)(want < cap ? want : cap);
+}
+
+hipError_t launch_decode_sinks(const void* q, const void* k_ring, const void* v_ring,
+                               const void* k_sink, const void* v_sink, int n_sink,
+                               const int32_t* pos, void* out, int B, int Hq, int Hkv, int W,
+                               int d, float scale, int dtype, float* workspace,
+                               hipStream_t stream) {
+  if (dtype == 1) {
+    if (d == 32) return launch_decode_sinks_d<__bf16, 32>(q, k_ring, v_ring, k_sink, v_sink, n_sink, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
+    if (d == 64) return launch_decode_sinks_d<__bf16, 64>(q, k_ring, v_ring, k_sink, v_sink, n_sink, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
+    return launch_decode_sinks_d<__bf16, 128>(q, k_ring, v_ring, k_sink, v_sink, n_sink, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
+  }
+  if (d == 32) return launch_decode_sinks_d<float, 32>(q, k_ring, v_ring, k_sink, v_sink, n_sink, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
+  if (d == 64) return launch_decode_sinks_d<float, 64>(q, k_ring, v_ring, k_sink, v_sink, n_sink, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
+  return launch_decode_sinks_d<float, 128>(q, k_ring, v_ring, k_sink, v_sink, n_sink, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
 }
 
 int global_splits(int G, int Hq, int T) {

@@ -37,7 +37,8 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "swa_prefill", "swa_cache_append", "swa_decode", "swa_decode_workspace_bytes",
         "swa_status_string", "swa_cache_append_chunk", "swa_prefill_chunk",
-        "swa_prefill_dilated", "swa_prefill_global", "swa_prefill_global_workspace_bytes"])
+        "swa_prefill_dilated", "swa_prefill_global", "swa_prefill_global_workspace_bytes",
+        "swa_decode_sinks", "swa_decode_sinks_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -184,6 +185,31 @@ def decode(lib, q=P, kr=P, vr=P, pos=P, out=P, B=2, Hq=8, Hkv=2, W=64, d=64, sca
 ])
 def test_decode_rejects(lib, kw, status):
     assert decode(lib, **kw) == status
+
+
+def decode_sinks(lib, q=P, kr=P, vr=P, ks=P, vs=P, S=4, pos=P, out=P, B=2, Hq=8, Hkv=2, W=64,
+                 d=64, scale=0.125, dtype=1, ws=P, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.swa_decode_sinks_workspace_bytes(B, Hq, W, d) if B > 0 and Hq > 0 and W > 0 else 0
+    return lib.swa_decode_sinks(q, kr, vr, ks, vs, S, pos, out, B, Hq, Hkv, W, d, scale, dtype, ws,
+                                ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ks=None), INVALID), (dict(vs=None), INVALID), (dict(ks=MIS), INVALID),
+    (dict(S=-1), INVALID), (dict(q=None), INVALID), (dict(B=0), INVALID),
+    (dict(Hq=6, Hkv=4), INVALID), (dict(d=16), UNSUPPORTED), (dict(dtype=8), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=64), WORKSPACE),
+])
+def test_decode_sinks_rejects(lib, kw, status):
+    assert decode_sinks(lib, **kw) == status
+
+
+def test_decode_sinks_workspace_is_one_split_more_than_decode(lib):
+    for B, Hq, W, d in [(64, 32, 4096, 128), (1, 2, 100, 64), (3, 8, 37, 32)]:
+        per_split = 4 * (d + 2) * B * Hq
+        assert lib.swa_decode_sinks_workspace_bytes(B, Hq, W, d) == \
+            lib.swa_decode_workspace_bytes(B, Hq, W, d) + per_split
 
 
 def test_decode_rejects_one_byte_short_workspace(lib):
