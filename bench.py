@@ -301,7 +301,23 @@ def all_configs(reps):
         row[tag] = {"ms": round(ms, 5), "kv_gbs": round(kv_bytes / ms / 1e6, 1),
                     "frac_roofline": round(t_roof / ms, 3)}
     print(json.dumps(row), flush=True)
-    del q, kr, vr, out, ws
+    del out, ws
+
+    # the same decode with 4 attention sinks beside each ring
+    ks = si.to_torch(si.normal(si.seed_for(4, si.ROLE_K_RING), (c["B"], c["Hkv"], 4, c["d"]), c["dtype"]), dev)
+    vs = si.to_torch(si.normal(si.seed_for(4, si.ROLE_V_RING), (c["B"], c["Hkv"], 4, c["d"]), c["dtype"]), dev)
+    out = torch.empty_like(q)
+    ws = swa.decode_sinks_workspace(c["B"], c["Hq"], c["W"], c["d"], dev)
+    fn = lambda: swa.decode_sinks(q, kr, vr, ks, vs, pos, scale=1.0 / math.sqrt(c["d"]), out=out,  # noqa: E731
+                                  workspace=ws)
+    row = {"config": c["name"] + " + 4 sinks", "kernel": "decode_sinks", "bound": "hbm",
+           "roofline_ms": round(t_roof, 5)}
+    for tag, fl in (("warm", False), ("flushed", True)):
+        ms = timed(fn, fl)
+        row[tag] = {"ms": round(ms, 5), "kv_gbs": round(kv_bytes / ms / 1e6, 1),
+                    "frac_roofline": round(t_roof / ms, 3)}
+    print(json.dumps(row), flush=True)
+    del q, kr, vr, ks, vs, out, ws
 
     # chunked prefill into full rings, then the chunk's append
     c = si.WORKLOADS[6]

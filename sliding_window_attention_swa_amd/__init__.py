@@ -312,6 +312,13 @@ def prefill_chunk(q, k, v, k_ring, v_ring, pos, scale=None, out=None, stream=Non
     return out
 
 
+def decode_sinks_workspace(B, Hq, W, d, device="cuda"):
+    """A workspace for decode_sinks (reusable across calls without clearing)."""
+    import torch
+    n = int(load().swa_decode_sinks_workspace_bytes(int(B), int(Hq), int(W), int(d)))
+    return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
+
+
 def decode_sinks(q, k_ring, v_ring, k_sink, v_sink, pos, scale=None, out=None, workspace=None,
                  stream=None):
     """decode with attention sinks: k_sink/v_sink [B, Hkv, S, d] hold the
@@ -336,8 +343,7 @@ def decode_sinks(q, k_ring, v_ring, k_sink, v_sink, pos, scale=None, out=None, w
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if workspace is None:
-        n = int(load().swa_decode_sinks_workspace_bytes(B, Hq, W, d))
-        workspace = torch.zeros(max(n, 16), dtype=torch.uint8, device=q.device)
+        workspace = decode_sinks_workspace(B, Hq, W, d, q.device)
     st = load().swa_decode_sinks(q.data_ptr(), k_ring.data_ptr(), v_ring.data_ptr(),
                                  k_sink.data_ptr() if S else None, v_sink.data_ptr() if S else None,
                                  S, pos.data_ptr(), out.data_ptr(), B, Hq, Hkv, W, d, float(scale),
