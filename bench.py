@@ -146,6 +146,67 @@ def summarize_pmc(paths):
     return 0
 
 
+N_XCD, N_SIMD = 8, 1024  # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+MFMA_FLOP_PER_SIMD_CYCLE = 1024  # v_mfma_f32_32x32x16_bf16: 32768 FLOP in 32 cycles
+
+
+def summarize_counters(paths):
+    """MFMA and instruction-mix figures of the prefill (and decode) dispatch
+    of a --pmc-workload run, from rocprofv3 counter CSVs: each counter is
+    summed over the dispatch's hardware instances (GRBM_GUI_ACTIVE over the
+    8 XCDs, SQ counters over SEs and SIMDs)."""
+    import csv
+    kinds = {"prefill_bf16_kernel": "prefill", "decode_split_kernel": "decode"}
+    per, dur = {}, {}
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            for pat, kind in kinds.items():
+                if pat in r["Kernel_Name"]:
+                    per[(kind, r["Counter_Name"])] = per.get((kind, r["Counter_Name"]), 0.0) + \
+                        float(r["Counter_Value"])
+                    dur[kind] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    if "prefill" not in dur:
+        print("no prefill dispatch in the counter files", file=sys.stderr)
+        return 1
+    for kind in ("prefill", "decode"):
+        if kind not in dur:
+            continue
+        g = lambda c: per.get((kind, c))  # noqa: E731
+        print("%s: dispatch %.1f us" % (kind, dur[kind] * 1e6))
+        for c in sorted(k for (kk, k) in per if kk == kind):
+            print("  %-30s %.6g" % (c, per[(kind, c)]))
+        gui = g("GRBM_GUI_ACTIVE")
+        if not gui:
+            continue
+        cycles = gui / N_XCD
+        clock = cycles / dur[kind]
+        print("  cycles per XCD %.0f -> clock %.0f MHz during the dispatch" % (cycles, clock / 1e6))
+        busy = g("SQ_VALU_MFMA_BUSY_CYCLES")
+        if busy is not None:
+            print("  MFMA busy: %.1f%% of SIMD cycles" % (100.0 * busy / (cycles * N_SIMD)))
+        mops = g("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        if mops is not None and kind == "prefill":
+            flops, _ = prefill_work()
+            issued = mops * 512
+            print("  MFMA FLOPs issued %.4g = %.3f x the in-window FLOPs" % (issued, issued / flops))
+            print("  issued MFMA rate %.0f TFLOP/s; peak at this clock %.0f TFLOP/s (%.1f%%); "
+                  "in-window rate %.0f TFLOP/s" % (
+                      issued / dur[kind] / 1e12, N_SIMD * MFMA_FLOP_PER_SIMD_CYCLE * clock / 1e12,
+                      100.0 * issued / dur[kind] / (N_SIMD * MFMA_FLOP_PER_SIMD_CYCLE * clock),
+                      flops / dur[kind] / 1e12))
+        if g("SQ_INSTS_VALU") and g("SQ_INSTS_MFMA"):
+            print("  VALU instructions per MFMA: %.2f" % (g("SQ_INSTS_VALU") / g("SQ_INSTS_MFMA")))
+        if g("SQ_INSTS_VALU_TRANS_F32") and kind == "prefill":
+            c = si.WORKLOADS[3]
+            exps = band_pairs_causal(c["T"], c["W"]) * c["Hq"] * c["B"] / 64.0
+            print("  transcendental instructions %.4g = %.3f x one exp per in-window score"
+                  % (g("SQ_INSTS_VALU_TRANS_F32"), g("SQ_INSTS_VALU_TRANS_F32") / exps))
+        if g("SQ_LDS_BANK_CONFLICT") is not None:
+            print("  LDS bank-conflict cycles: %.3g (%.2f%% of SIMD cycles)"
+                  % (g("SQ_LDS_BANK_CONFLICT"), 100.0 * g("SQ_LDS_BANK_CONFLICT") / (cycles * N_SIMD)))
+    return 0
+
+
 def cpu_baseline(pos_np, q_dec, kr, vr, qkv_pre):
     """fp64 oracle on the host cores over a bounded sample of one step:
     8 of the 32 prefill query heads (all 16384 rows each) and 8 of the 64
@@ -378,12 +439,17 @@ def main():
     ap.add_argument("--summarize-pmc", nargs="+", metavar="CSV",
                     help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs of a "
                          "--pmc-workload run into the prefill traffic summary")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
+                    help="turn rocprofv3 MFMA / instruction counter CSVs of a --pmc-workload run "
+                         "into utilisation figures")
     ap.add_argument("--all-configs", action="store_true",
                     help="instead of the benchmark line: every configuration, cache-warm and "
                          "flushed, against its roofline (one JSON line each)")
     args = ap.parse_args()
     if args.summarize_pmc:
         return summarize_pmc(args.summarize_pmc)
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters)
     if args.all_configs:
         return all_configs(max(args.steps, 20))
 

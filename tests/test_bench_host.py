@@ -79,3 +79,24 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120, cwd=ROOT)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_counter_summary_arithmetic(tmp_path, capsys):
+    """A synthetic prefill dispatch of 1 ms at 1.8 GHz on every XCD, with the
+    matrix cores busy half of the SIMD cycles and exactly the in-window FLOPs
+    issued."""
+    flops, _ = bench.prefill_work()
+    cycles = 1.8e9 * 1e-3
+    rows = [("GRBM_GUI_ACTIVE", cycles * bench.N_XCD),
+            ("SQ_VALU_MFMA_BUSY_CYCLES", 0.5 * cycles * bench.N_SIMD),
+            ("SQ_INSTS_VALU_MFMA_MOPS_BF16", flops / 512)]
+    f = tmp_path / "c.csv"
+    with open(f, "w") as fh:
+        fh.write('"Kernel_Name","Counter_Name","Counter_Value","Start_Timestamp","End_Timestamp"\n')
+        for name, val in rows:
+            fh.write('"swa::prefill_bf16_kernel<128, 0>","%s",%r,1000000,2000000\n' % (name, val))
+    assert bench.summarize_counters([str(f)]) == 0
+    out = capsys.readouterr().out
+    assert "clock 1800 MHz" in out
+    assert "MFMA busy: 50.0%" in out
+    assert "1.000 x the in-window FLOPs" in out
