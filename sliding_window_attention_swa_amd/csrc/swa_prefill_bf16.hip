@@ -684,8 +684,13 @@ constexpr int kShortOff = MODE == 0 ? 32 : 16;
 
 bool short_window(int W, int mode) { return mode == 0 ? W <= 33 : (W >> 1) <= 16; }
 
+// The occupancy target keeps the matrix results in ordinary registers (with
+// one wave per workgroup the compiler otherwise keeps them in accumulation
+// registers and copies them out).
 template <int D, int MODE>
-__global__ __launch_bounds__(64) void prefill_short_kernel(
+__global__ __launch_bounds__(64)
+__attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>)))
+void prefill_short_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ out, int T, int W, int Hq, int Hkv, float c, uint32_t qsign,
     int n_wtiles) {
@@ -766,21 +771,24 @@ __global__ __launch_bounds__(64) void prefill_short_kernel(
       s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[mb], 0, 0, 0);
     }
   }
+  // The window and the sequence ends as one unsigned range test per score on
+  // diff = qi - key, with the lane's bounds computed once: keys >= 0 means
+  // diff <= qi; keys < T means diff > qi - T (automatic in the causal mode for
+  // a row inside the sequence; rows past T are never stored).  A symmetric
+  // row far past T gets dlo > dhi: the span wraps and keeps every score of its
+  // clamped, finite rows.
   const int hw = W >> 1;
+  const int dlo = MODE == 0 ? 0 : max(-hw, qi - T + 1);
+  const int dhi = MODE == 0 ? min(W - 1, qi) : min(hw, qi);
+  const unsigned span = (unsigned)(dhi - dlo);
+  const int d0 = qi - kb0 - dlo;  // diff - dlo of key kb0
   float mx = -INFINITY;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = kb0 + mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-      const int diff = qi - key;
-      bool ok = key >= 0 && key < T;
-      if (MODE == 0) {
-        ok = ok && diff >= 0 && diff < W;
-      } else {
-        ok = ok && diff >= -hw && diff <= hw;
-      }
-      if (!ok) s[mb][r] = -INFINITY;
+      const int kc = mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);  // key - kb0
+      if (!((unsigned)(d0 - kc) <= span)) s[mb][r] = -INFINITY;
       mx = fmaxf(mx, s[mb][r]);
     }
   }
