@@ -522,20 +522,39 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(Ks, mb, ks), qf[ks], s[mb], 0, 0, 0);
     }
+    if constexpr (kCausal && !kChunk) {
+      // causal: window and sequence ends as one unsigned test per score,
+      // 0 <= diff <= min(W - 1, qi) with diff = qi - key (keys >= 0; keys < T
+      // follow for a row inside the sequence, and rows past T are never
+      // stored)
+      const unsigned span = (unsigned)min(W - 1, qi);
+      const int d0 = qi - k0;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        const int diff = qi - key;
-        bool ok = key < T;
-        if (kCausal) {
-          ok = ok && diff >= 0 && diff < W;
-          if (kChunk) ok = ok && key >= -pstart;
-        } else {
-          ok = ok && diff >= -hw && diff <= hw;
+        for (int r = 0; r < 16; ++r) {
+          const int kc = mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);  // key - k0
+          if (!((unsigned)(d0 - kc) <= span)) s[mb][r] = -INFINITY;
         }
-        if (!ok) s[mb][r] = -INFINITY;
+      }
+    } else {
+      // symmetric and chunk modes: the single test keeps more values live
+      // through the tile loop and spills there, so the bounds are tested
+      // directly
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const int diff = qi - key;
+          bool ok = key < T;
+          if (kCausal) {
+            ok = ok && diff >= 0 && diff < W && key >= -pstart;
+          } else {
+            ok = ok && diff >= -hw && diff <= hw;
+          }
+          if (!ok) s[mb][r] = -INFINITY;
+        }
       }
     }
     bf16x8 pb[4];
