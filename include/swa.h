@@ -13,7 +13,11 @@
  *   - aivaro.ru answer 629, section 4.1: the Longformer window takes W/2
  *     neighbours on each side;
  *   - "Sliding-window and hybrid attention", section "Walking through it":
- *     windowed decode reads only the window's KV for each new token.
+ *     windowed decode reads only the window's KV for each new token;
+ *   - aivaro.ru answer 629, sections 4.2 and 4.3: the dilated window and the
+ *     global tokens of Longformer;
+ *   - Ultralytics glossary, terms section: attention sinks kept beside the
+ *     window (StreamingLLM).
  *
  * Conventions shared by every entry point
  *   - All tensors are dense, contiguous and head-major:
@@ -24,6 +28,8 @@
  *       pos           [B] int32
  *     and for a chunk of n tokens per sequence (chunked prefill)
  *       q, out        [B, Hq, n, d]    k, v  [B, Hkv, n, d]
+ *     attention sinks beside a ring: k_sink, v_sink [B, Hkv, S, d];
+ *     global token positions: global_pos [G] int32.
  *     Element type is selected by `dtype` (swa_dtype): IEEE fp32 or bfloat16.
  *   - Query head h reads KV head h / (Hq / Hkv) (contiguous GQA groups); Hq
  *     must be a multiple of Hkv.
@@ -34,7 +40,9 @@
  *     asynchronously; calls are thread-safe.
  *   - Arguments are validated on the host before anything is enqueued.  An
  *     invalid call returns a negative swa_status and launches nothing; a
- *     failed launch returns SWA_ERR_LAUNCH.  Device-side contents (e.g. pos)
+ *     failed launch returns SWA_ERR_LAUNCH (for the calls made of two or
+ *     three kernels, the ones before the failure may already be enqueued, and
+ *     the output is then undefined).  Device-side contents (e.g. pos)
  *     are not validated on the host; the behaviour for out-of-range positions
  *     is stated per entry point and never touches memory outside the buffers.
  *   - Accumulation and softmax run in fp32; bf16 outputs are rounded to

@@ -212,14 +212,15 @@ def test_longformer_full(swa):
 
 
 def test_mistral_full_sampled(swa):
-    """B=1, T=16384, W=4096, 32/8 heads, d=128, bf16: two whole heads (from
-    different KV groups) plus edge and random rows of every head."""
+    """B=1, T=16384, W=4096, 32/8 heads, d=128, bf16: one whole query head of
+    every KV group (each position in the group twice) plus edge and random
+    rows of every head."""
     cfg = si.WORKLOADS[3]
     T, W, d = cfg["T"], cfg["W"], cfg["d"]
     scale = 1 / math.sqrt(d)
     q, k, v = si.prefill_inputs(3)
     got = to_f64(run(swa, q, k, v, W, cfg["mode"]))
-    heads = [(0, 0), (0, 21)]
+    heads = [(0, 4 * g + g % 4) for g in range(cfg["Hkv"])]
     ref = oracle.attention_banded(q.values, k.values, v.values, W, cfg["mode"], scale,
                                   heads=heads)
     for b, h in heads:
