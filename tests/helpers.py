@@ -35,9 +35,18 @@ def errors(got, ref):
     return max_abs, rel_l2
 
 
+def cosine(got, ref):
+    """Cosine similarity of the flattened outputs (logged, not gated)."""
+    a = np.asarray(got, dtype=np.float64).ravel()
+    b = np.asarray(ref, dtype=np.float64).ravel()
+    den = float(np.linalg.norm(a) * np.linalg.norm(b))
+    return float(a @ b / den) if den > 0 else 1.0
+
+
 def assert_parity(got, ref, dtype, what=""):
     assert np.all(np.isfinite(got)), "%s: non-finite output" % what
     max_abs, rel_l2 = errors(got, ref)
+    print("%s: max-abs %.3g rel-L2 %.3g cosine %.9f" % (what, max_abs, rel_l2, cosine(got, ref)))
     if dtype == "f32":
         assert max_abs <= FP32_MAX_ABS, "%s: max-abs %.3g > %.1g" % (what, max_abs, FP32_MAX_ABS)
     else:
