@@ -134,9 +134,11 @@ int swa_prefill_dilated(const void* q, const void* k, const void* v, void* out, 
  * G = 0 is swa_prefill.  The same positions apply to every sequence of the
  * batch (batch folded into the heads as for swa_prefill).
  *
- * Computed in two passes on `stream`: the windowed kernel visits the global
- * keys as extra tiles (skipping those inside a row's window), then the
- * split-K full-row pass of swa_decode writes the G global rows.
+ * Computed in passes on `stream`: the windowed kernel visits the global
+ * keys as extra tiles (skipping those inside a row's window), then a split-K
+ * pass over the whole sequence writes partials of the G global rows (bf16: on
+ * the matrix cores, 128 keys per split; fp32: the split-K kernel of
+ * swa_decode), merged into those rows of `out`.
  *
  *   Arguments, layouts and errors as swa_prefill, plus
  *   global_pos  device int32 [G], strictly increasing positions in [0, T)

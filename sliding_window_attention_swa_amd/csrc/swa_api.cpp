@@ -86,6 +86,8 @@ int swa_prefill_global(const void* q, const void* k, const void* v, void* out, i
   if ((long long)((T + 15) / 16) * Hq > kMaxGrid) return SWA_ERR_UNSUPPORTED;
   const int S = swa::global_splits(G, Hq, T);
   if ((long long)G * Hq * S > kMaxGrid) return SWA_ERR_UNSUPPORTED;
+  const int S1 = swa::global_rows_mfma_splits(T);
+  if ((long long)Hkv * ((G * (Hq / Hkv) + 31) / 32) * S1 > kMaxGrid) return SWA_ERR_UNSUPPORTED;
   const size_t need = swa_prefill_global_workspace_bytes(T, Hq, G, d);
   if (!workspace || !aligned16(workspace) || workspace_bytes < need) return SWA_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -95,8 +97,16 @@ int swa_prefill_global(const void* q, const void* k, const void* v, void* out, i
                      : swa::launch_prefill_global_window_f32(q, k, v, out, T, W, Hq, Hkv, d, mode,
                                                              scale, global_pos, G, s);
   if (e != hipSuccess) return SWA_ERR_LAUNCH;
-  e = swa::launch_global_rows(q, k, v, global_pos, out, G, T, Hq, Hkv, d, mode, scale, dtype,
-                              static_cast<float*>(workspace), s);
+  float* ws = static_cast<float*>(workspace);
+  if (dtype == SWA_BF16) {  // the global rows on the matrix cores, then their merge
+    e = swa::launch_global_rows_mfma_bf16(q, k, v, global_pos, G, T, Hq, Hkv, d, mode, scale, ws, s);
+    if (e != hipSuccess) return SWA_ERR_LAUNCH;
+    e = swa::launch_global_combine(ws, out, global_pos, G, T, Hq, Hkv, d,
+                                   swa::global_rows_mfma_splits(T), dtype, s);
+  } else {
+    e = swa::launch_global_rows(q, k, v, global_pos, out, G, T, Hq, Hkv, d, mode, scale, dtype, ws,
+                                s);
+  }
   return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH;
 }
 
@@ -160,8 +170,11 @@ int swa_prefill_chunk(const void* q, const void* k, const void* v, const void* k
 
 size_t swa_prefill_global_workspace_bytes(int T, int Hq, int G, int d) {
   if (T <= 0 || Hq <= 0 || G <= 0 || !supported_d(d)) return 0;
-  const int S = swa::global_splits(G, Hq, T);
-  return (size_t)G * Hq * S * (size_t)(d + 2) * sizeof(float);
+  // the larger of the two global-row passes (matrix cores for bf16, vector
+  // units for fp32)
+  const int S0 = swa::global_splits(G, Hq, T);
+  const int S1 = swa::global_rows_mfma_splits(T);
+  return (size_t)G * Hq * (S0 > S1 ? S0 : S1) * (size_t)(d + 2) * sizeof(float);
 }
 
 size_t swa_decode_workspace_bytes(int B, int Hq, int W, int d) {

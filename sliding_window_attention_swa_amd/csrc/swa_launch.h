@@ -46,6 +46,17 @@ hipError_t launch_decode_sinks(const void* q, const void* k_ring, const void* v_
                                int d, float scale, int dtype, float* workspace,
                                hipStream_t stream);
 
+// The rows of the global tokens on the matrix cores (bf16): split-K partials
+// of global_rows_mfma_splits(T) chunks into the workspace, merged by
+// launch_global_combine.
+int global_rows_mfma_splits(int T);
+hipError_t launch_global_rows_mfma_bf16(const void* q, const void* k, const void* v,
+                                        const int32_t* gpos, int ngl, int T, int Hq, int Hkv,
+                                        int d, int mode, float scale, float* workspace,
+                                        hipStream_t stream);
+hipError_t launch_global_combine(float* workspace, void* out, const int32_t* gpos, int ngl, int T,
+                                 int Hq, int Hkv, int d, int S, int dtype, hipStream_t stream);
+
 // Number of key chunks the global-row pass splits each row into.
 int global_splits(int G, int Hq, int T);
 

@@ -979,7 +979,234 @@ hipError_t launch_chunk(const void* q, const void* k, const void* v, const void*
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Rows of global tokens on the matrix cores (aivaro answer 629, section 4.3:
+// a global token attends to every token).  One wave takes 32 (global row,
+// query head) pairs of one KV head and one split of kGRowKeys keys: the pairs'
+// query rows are gathered as the B operand, 64-key K/V tiles are loaded into
+// LDS, and scores, masking (key <= the row's last key: its own position when
+// causal, T - 1 otherwise), an exact per-tile online softmax and O^T += V^T P^T
+// follow the tiled kernel.  The unnormalised partial (acc, max in log2 units,
+// sum) of each pair goes to the split-K workspace, merged afterwards by the
+// decode kernels' merge pass.
+#ifndef SWA_GROW_KEYS
+#define SWA_GROW_KEYS 128
+#endif
+constexpr int kGRowKeys = SWA_GROW_KEYS;
+
+template <int D, int MODE>
+__global__ __launch_bounds__(64)
+__attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>)))
+void global_rows_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                        const __bf16* __restrict__ v, const int32_t* __restrict__ gpos,
+                        float* __restrict__ ws_acc, float* __restrict__ ws_m,
+                        float* __restrict__ ws_l, int T, int Hq, int Hkv, int ngl, float c,
+                        uint32_t qsign, int S, int n_pchunks) {
+  using Gm = Geo<D>;
+  constexpr int ROWB = Gm::ROWB, KS = Gm::KS, MD = Gm::MD;
+  constexpr int TILEB = kBN * ROWB;
+  constexpr int NL = TILEB / (64 * 16);  // direct loads per lane per tile
+  __shared__ __attribute__((aligned(1024))) char lds_k[TILEB];
+  __shared__ __attribute__((aligned(1024))) char lds_v[TILEB];
+
+  const int G = Hq / Hkv;
+  const int n_pairs = ngl * G;
+  int id = blockIdx.x;
+  const int split = id % S;
+  id /= S;
+  const int pc = id % n_pchunks;
+  const int kvh = id / n_pchunks;
+  const int lane = threadIdx.x;
+  const int half = lane >> 5;
+
+  // this lane's row: pair pi = pc * 32 + lane % 32 (global row pi / G, query
+  // head kvh * G + pi % G); positions outside [0, T) and pairs past the last
+  // are rows without keys
+  const int pi = pc * 32 + (lane & 31);
+  int gp = -1, h = 0;
+  if (pi < n_pairs) {
+    gp = gpos[pi / G];
+    h = kvh * G + pi % G;
+    if (gp < 0 || gp >= T) gp = -1;
+  }
+  const int s0 = split * kGRowKeys;
+  const int s1 = min(T, s0 + kGRowKeys);
+  const int lim = gp < 0 ? -1 : min(MODE == 0 ? gp : T - 1, s1 - 1);  // last key of the row
+  // the wave stops after the last key any of its rows sees
+  int wlim = lim;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) wlim = max(wlim, __shfl_xor(wlim, off));
+
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (gp >= 0) w = *reinterpret_cast<const uint4*>(q + ((size_t)h * T + gp) * D + ks * 16 + half * 8);
+    w.x ^= qsign;
+    w.y ^= qsign;
+    w.z ^= qsign;
+    w.w ^= qsign;
+    qf[ks] = __builtin_bit_cast(bf16x8, w);
+  }
+  const __bf16* kh = k + (size_t)kvh * T * D;
+  const __bf16* vh = v + (size_t)kvh * T * D;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)kh, 0, T * ROWB, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)vh, 0, T * ROWB, kBufferFlags);
+
+  const int kr = lane & 31;
+  const int kf = swz<D>(kr);
+  const int tr_s = lane & 15, tr_g = lane >> 4;
+  const int tr_row = 4 * (tr_g >> 1) + (tr_s >> 2);
+  const int tr_c0 = 2 * (tr_g & 1) + ((tr_s & 3) >> 1);
+  const int tr_flo = swz<D>(tr_row), tr_fhi = swz<D>(tr_row + 8);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  f32x16 o[MD];
+#pragma unroll
+  for (int md = 0; md < MD; ++md) o[md] = f32x16{};
+  float m = -INFINITY, l = 0.f;  // raw-score maximum and sum of this lane's row
+
+  for (int k0 = s0; k0 <= wlim; k0 += kBN) {
+    // the tile: rows past T re-read row T - 1 (finite, masked); the previous
+    // tile's LDS reads are complete before it is overwritten
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int o16 = (64 * j + lane) * 16;
+      const int row = o16 / ROWB;
+      const int off = min(k0 + row, T - 1) * ROWB + ((((o16 % ROWB) / 16) ^ swz<D>(row)) * 16);
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass mishandles this builtin
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(lds_k + 64 * j * 16), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(lds_v + 64 * j * 16), 16, off, 0, 0, 0);
+#else
+      (void)rk, (void)rv, (void)off;
+#endif
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the tile is in LDS (one wave: no barrier)
+
+    f32x16 sb[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      sb[mb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds_k + (mb * 32 + kr) * ROWB + (((2 * ks + half) ^ kf) * 16));
+        sb[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sb[mb], 0, 0, 0);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (key > lim) sb[mb][r] = -INFINITY;
+        mx = fmaxf(mx, sb[mb][r]);
+      }
+    }
+    mx = max_lane_pair(mx);  // lanes l and l^32 hold the same row
+    const float m_new = fmaxf(m, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // a row without keys so far
+    const float alpha = __builtin_amdgcn_exp2f((m - m_use) * c);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[md][r] *= alpha;
+    }
+    const float mc = -m_use * c;
+    bf16x8 p[4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sb[mb][8 * k2 + 2 * e], c, mc));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sb[mb][8 * k2 + 2 * e + 1], c, mc));
+          w[e] = pack_bf16x2(p0, p1);
+          l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[e]), ones, l, false);
+        }
+        p[2 * mb + k2] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+      const int vlo = tr_row * ROWB + (((4 * md + tr_c0) ^ tr_flo) * 16) + (tr_s & 1) * 8;
+      const int vhi = (tr_row + 8) * ROWB + (((4 * md + tr_c0) ^ tr_fhi) * 16) + (tr_s & 1) * 8;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const char* src = lds_v + kk * 16 * ROWB;
+        const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + vlo));
+        const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + vhi));
+        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[kk], o[md], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- the pair's partial (the merge computes sum_s 2^(m_s - M) acc_s / ...)
+  const float l_tot = l + __shfl_xor(l, 32);
+  if (gp >= 0) {
+    const size_t slot = ((size_t)kvh * n_pairs + pi) * S + split;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int dim = 32 * md + 8 * rq + 4 * half;
+        *reinterpret_cast<float4*>(ws_acc + slot * D + dim) =
+            make_float4(o[md][4 * rq], o[md][4 * rq + 1], o[md][4 * rq + 2], o[md][4 * rq + 3]);
+      }
+    }
+    if (half == 0) {
+      ws_m[slot] = m == -INFINITY ? -1.0e30f : m * c;
+      ws_l[slot] = l_tot;
+    }
+  }
+}
+
+template <int D, int MODE>
+hipError_t launch_global_rows(const void* q, const void* k, const void* v, const int32_t* gpos,
+                              int ngl, int T, int Hq, int Hkv, float scale, float* workspace,
+                              hipStream_t stream) {
+  const int S = (T + kGRowKeys - 1) / kGRowKeys;
+  const int n_pairs = ngl * (Hq / Hkv);
+  const int n_pchunks = (n_pairs + 31) / 32;
+  const size_t rows = (size_t)ngl * Hq * S;
+  float* ws_acc = workspace;
+  float* ws_m = ws_acc + rows * D;
+  float* ws_l = ws_m + rows;
+  float c;
+  uint32_t qsign;
+  fold_scale(scale, c, qsign);
+  const long long nwg = (long long)Hkv * n_pchunks * S;
+  hipLaunchKernelGGL((global_rows_kernel<D, MODE>), dim3((unsigned)nwg), dim3(64), 0, stream,
+                     static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+                     static_cast<const __bf16*>(v), gpos, ws_acc, ws_m, ws_l, T, Hq, Hkv, ngl, c,
+                     qsign, S, n_pchunks);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+int global_rows_mfma_splits(int T) { return (T + kGRowKeys - 1) / kGRowKeys; }
+
+hipError_t launch_global_rows_mfma_bf16(const void* q, const void* k, const void* v,
+                                        const int32_t* gpos, int ngl, int T, int Hq, int Hkv,
+                                        int d, int mode, float scale, float* workspace,
+                                        hipStream_t stream) {
+  if (mode == 0) {
+    if (d == 32) return launch_global_rows<32, 0>(q, k, v, gpos, ngl, T, Hq, Hkv, scale, workspace, stream);
+    if (d == 64) return launch_global_rows<64, 0>(q, k, v, gpos, ngl, T, Hq, Hkv, scale, workspace, stream);
+    return launch_global_rows<128, 0>(q, k, v, gpos, ngl, T, Hq, Hkv, scale, workspace, stream);
+  }
+  if (d == 32) return launch_global_rows<32, 1>(q, k, v, gpos, ngl, T, Hq, Hkv, scale, workspace, stream);
+  if (d == 64) return launch_global_rows<64, 1>(q, k, v, gpos, ngl, T, Hq, Hkv, scale, workspace, stream);
+  return launch_global_rows<128, 1>(q, k, v, gpos, ngl, T, Hq, Hkv, scale, workspace, stream);
+}
 
 hipError_t launch_prefill_chunk_bf16(const void* q, const void* k, const void* v,
                                      const void* k_ring, const void* v_ring, const int32_t* pos,

@@ -55,6 +55,9 @@ constexpr int kDecodeWaves = kDecodeThreads / 64;
 #ifndef SWA_GLOBAL_NQ
 #define SWA_GLOBAL_NQ 4
 #endif
+#ifndef SWA_COMBINE_UNROLL
+#define SWA_COMBINE_UNROLL 8
+#endif
 #ifndef SWA_GLOBAL_NT
 #define SWA_GLOBAL_NT 0
 #endif
@@ -462,12 +465,23 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
   const float* m = ws_m + row * S;
   const float* l = ws_l + row * S;
   float M = m[0];
-  for (int s = 1; s < S; ++s) M = fmaxf(M, m[s]);
   float a = 0.f, L = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float w = __builtin_amdgcn_exp2f(m[s] - M);
-    L = fmaf(w, l[s], L);
-    a = fmaf(w, ws_acc[(row * S + s) * D + dim], a);
+  if constexpr (kRows<GR>) {  // many splits: several in flight at once
+#pragma unroll SWA_COMBINE_UNROLL
+    for (int s = 1; s < S; ++s) M = fmaxf(M, m[s]);
+#pragma unroll SWA_COMBINE_UNROLL
+    for (int s = 0; s < S; ++s) {
+      const float w = __builtin_amdgcn_exp2f(m[s] - M);
+      L = fmaf(w, l[s], L);
+      a = fmaf(w, ws_acc[(row * S + s) * D + dim], a);
+    }
+  } else {
+    for (int s = 1; s < S; ++s) M = fmaxf(M, m[s]);
+    for (int s = 0; s < S; ++s) {
+      const float w = __builtin_amdgcn_exp2f(m[s] - M);
+      L = fmaf(w, l[s], L);
+      a = fmaf(w, ws_acc[(row * S + s) * D + dim], a);
+    }
   }
   size_t orow = row * D;
   if constexpr (kRows<GR>) {
@@ -613,6 +627,32 @@ hipError_t launch_decode_sinks(const void* q, const void* k_ring, const void* v_
   if (d == 32) return launch_decode_sinks_d<float, 32>(q, k_ring, v_ring, k_sink, v_sink, n_sink, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
   if (d == 64) return launch_decode_sinks_d<float, 64>(q, k_ring, v_ring, k_sink, v_sink, n_sink, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
   return launch_decode_sinks_d<float, 128>(q, k_ring, v_ring, k_sink, v_sink, n_sink, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
+}
+
+hipError_t launch_global_combine(float* workspace, void* out, const int32_t* gpos, int ngl, int T,
+                                 int Hq, int Hkv, int d, int S, int dtype, hipStream_t stream) {
+  // merge of split partials laid out as the global-row pass writes them:
+  // row kvh * n_pairs + pi, S partials each
+  const size_t rows = (size_t)ngl * Hq;
+  float* ws_acc = workspace;
+  float* ws_m = ws_acc + rows * S * d;
+  float* ws_l = ws_m + rows * S;
+  const int G = Hq / Hkv;
+  const int n_pairs = ngl * G;
+#define SWA_COMBINE(E, DD)                                                                      \
+  hipLaunchKernelGGL((decode_combine_kernel<E, DD, 1>), dim3((unsigned)rows), dim3(DD), 0, stream, \
+                     ws_acc, ws_m, ws_l, static_cast<E*>(out), S, gpos, T, G, n_pairs)
+  if (dtype == 1) {
+    if (d == 32) SWA_COMBINE(__bf16, 32);
+    else if (d == 64) SWA_COMBINE(__bf16, 64);
+    else SWA_COMBINE(__bf16, 128);
+  } else {
+    if (d == 32) SWA_COMBINE(float, 32);
+    else if (d == 64) SWA_COMBINE(float, 64);
+    else SWA_COMBINE(float, 128);
+  }
+#undef SWA_COMBINE
+  return hipGetLastError();
 }
 
 int global_splits(int G, int Hq, int T) {

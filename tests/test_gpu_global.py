@@ -53,6 +53,7 @@ GLOBAL_SMALL = [
     (1, 1000, 129, 100, 1, 2, 2, 64),
     (0, 129, 300, 7, 2, 2, 1, 32),     # window longer than the sequence
     (1, 64, 1, 3, 1, 2, 1, 128),       # W = 1
+    (0, 1500, 200, 20, 1, 32, 8, 128), # 80 (row, head) pairs per KV head, 6 key splits
 ]
 
 
