@@ -62,8 +62,8 @@
 // mode).  They are visited after the window's tiles, as extra tiles whose
 // rows are gathered from the global positions; a global key already inside a
 // row's window is masked there so that no key counts twice.  The global rows
-// themselves attend to every key and are written by the full-row pass of the
-// decode kernel afterwards.
+// themselves attend to every key: global_rows_kernel below computes their
+// split-K partials afterwards, and the decode kernels' merge writes them.
 
 #include "swa_device.h"
 #include "swa_launch.h"
