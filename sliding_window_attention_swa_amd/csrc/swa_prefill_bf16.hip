@@ -443,7 +443,20 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   // waves the one with vector work to interleave goes first and the other's
   // matrix-only work fills the gaps (measured about 1% faster than equal
   // priority).
-  auto interior_tile = [&](const char* Ks, const char* Vs) __attribute__((always_inline)) {
+  //
+  // Masked (symmetric windows): a tile crossing a window edge or the sequence
+  // end runs the same schedule; key k0 + kc counts for this lane's row when
+  // mlo <= kc - 4 * half <= mhi, tested on each score block before its
+  // probabilities.
+  auto interior_tile = [&](const char* Ks, const char* Vs, auto masked, int mlo, int mhi) __attribute__((always_inline)) {
+    constexpr bool kMasked = decltype(masked)::value;
+    auto mask_block = [&](f32x16& sb, int mb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kc = mb * 32 + 8 * (r >> 2) + (r & 3);
+        if (kc < mlo || kc > mhi) sb[r] = -INFINITY;
+      }
+    };
     // S for keys 0..31: all K operands requested up front
     bf16x8 ka[KS];
 #pragma unroll
@@ -464,6 +477,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     f32x16 s1 = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], s1, 0, 0, 0);
+    if constexpr (kMasked) mask_block(s0, 0);
     probs(s0, -m_ref * c, p0, l0);
     pin(p0, l0);
     __builtin_amdgcn_sched_group_barrier(0x100, KS / 2, 0);
@@ -483,6 +497,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(Vs, md, kk), p0[kk], o[md], 0, 0, 0);
     }
+    if constexpr (kMasked) mask_block(s1, 1);
     probs(s1, -m_ref * c, p1, l1);
     pin(p1, l1);
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -640,7 +655,12 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
       full = (k0 >= qlast - hw) && (k0 + kBN - 1 <= qw0 + hw) && (k0 + kBN <= T);
     }
     if (full) {
-      interior_tile(Ks, Vs);
+      interior_tile(Ks, Vs, std::false_type{}, 0, 0);
+    } else if constexpr (!kCausal) {
+      // symmetric: keys k0 + kc with qi - hw <= k0 + kc <= min(qi + hw, T - 1)
+      const int mlo = qi - hw - k0 - 4 * half;
+      const int mhi = min(qi + hw, T - 1) - k0 - 4 * half;
+      interior_tile(Ks, Vs, std::true_type{}, mlo, mhi);
     } else {
       edge_tile(Ks, Vs, k0);
     }
