@@ -19,6 +19,8 @@ bounded sample of the same work.
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
        python bench.py --all-configs   (every configuration vs its roofline, warm and
                                         flushed; not the benchmark line)
+       python bench.py --peaks         (the matrix-core and streaming-read rates the box
+                                        sustains, from the library's calibration kernels)
 """
 
 import argparse
@@ -278,7 +280,36 @@ def global_pairs(T, W, mode, gpos):
     return int(n.sum())
 
 
-def all_configs(reps):
+def measured_peaks(swa, dev, timed):
+    """What the box sustains (the library's calibration kernels): bf16 matrix
+    TFLOP/s of an MFMA loop on N(0,1) operands (the attention inputs'
+    distribution), and GB/s of a non-temporal streaming read of 2 GiB (past
+    the Infinity Cache); each the best of three grids."""
+    import torch
+    ops = si.to_torch(si.normal(99, (32768,), "bf16"), dev)
+    # grids of whole rounds (three waves per SIMD fit: 768 workgroups fill the
+    # chip once) and a long one, at equal FLOPs; the best is the sustained rate
+    mfma_tflops = 0.0
+    for n_wg in (768, 1536, 6144):
+        iters = 1638400 // n_wg
+        sink = torch.empty(n_wg * 256, dtype=torch.float32, device=dev)
+        flops = n_wg * 4 * iters * 16 * 32768
+        ms = timed(lambda: swa.calib_mfma(ops, sink, n_wg, iters), False)
+        mfma_tflops = max(mfma_tflops, flops / ms / 1e9)
+    src = torch.ones(1 << 29, dtype=torch.int32, device=dev)  # 2 GiB
+    best = 0.0
+    for grid in (2048, 4096, 8192):
+        rsink = torch.empty(grid * 256, dtype=torch.int32, device=dev)
+        ms = timed(lambda: swa.calib_stream_read(src, rsink, grid), False)
+        best = max(best, src.numel() * 4 / ms / 1e6)
+    del src
+    return {"config": "measured peaks", "mfma_bf16_tflops": round(mfma_tflops, 1),
+            "frac_of_published_mfma": round(mfma_tflops / PEAK_BF16_TFLOPS, 3),
+            "stream_read_gbs": round(best, 1),
+            "frac_of_published_hbm": round(best / PEAK_HBM_GBS, 3)}
+
+
+def all_configs(reps, peaks_only=False):
     """Every configuration's kernel time, cache-warm (same inputs every
     repetition) and flushed (a 1 GiB write between repetitions evicts the L2s
     and the Infinity Cache), against its binding roofline.  One JSON line per
@@ -305,6 +336,16 @@ def all_configs(reps):
         torch.cuda.synchronize()
         return float(np.median([a.elapsed_time(b) for a, b in ev[3:]]))
 
+    peaks = measured_peaks(swa, dev, timed)
+    print(json.dumps(peaks), flush=True)
+    if peaks_only:
+        return 0
+
+    def meas(flops, bytes_, ms):
+        """Fraction of the roofline built from the measured peaks."""
+        t = max(flops / (peaks["mfma_bf16_tflops"] * 1e12), bytes_ / (peaks["stream_read_gbs"] * 1e9))
+        return round(t * 1e3 / ms, 3)
+
     for wl in (2, 3, 5, 7):
         c = si.WORKLOADS[wl]
         q, k, v = (si.to_torch(t, dev) for t in si.prefill_inputs(wl))
@@ -322,7 +363,8 @@ def all_configs(reps):
         for tag, fl in (("warm", False), ("flushed", True)):
             ms = timed(fn, fl)
             row[tag] = {"ms": round(ms, 5), "tflops": round(flops / ms / 1e9, 1),
-                        "gbs": round(bytes_ / ms / 1e6, 1), "frac_roofline": round(t_roof / ms, 3)}
+                        "gbs": round(bytes_ / ms / 1e6, 1), "frac_roofline": round(t_roof / ms, 3),
+                        "frac_measured": meas(flops, bytes_, ms)}
         print(json.dumps(row), flush=True)
         del q, k, v, out
 
@@ -343,7 +385,8 @@ def all_configs(reps):
     for tag, fl in (("warm", False), ("flushed", True)):
         ms = timed(fn, fl)
         row[tag] = {"ms": round(ms, 5), "tflops": round(flops / ms / 1e9, 1),
-                    "gbs": round(bytes_ / ms / 1e6, 1), "frac_roofline": round(t_roof / ms, 3)}
+                    "gbs": round(bytes_ / ms / 1e6, 1), "frac_roofline": round(t_roof / ms, 3),
+                    "frac_measured": meas(flops, bytes_, ms)}
     print(json.dumps(row), flush=True)
     del q, k, v, out, ws
 
@@ -360,7 +403,8 @@ def all_configs(reps):
     for tag, fl in (("warm", False), ("flushed", True)):
         ms = timed(fn, fl)
         row[tag] = {"ms": round(ms, 5), "kv_gbs": round(kv_bytes / ms / 1e6, 1),
-                    "frac_roofline": round(t_roof / ms, 3)}
+                    "frac_roofline": round(t_roof / ms, 3),
+                    "frac_measured": meas(0, kv_bytes + qo_bytes, ms)}
     print(json.dumps(row), flush=True)
     del out, ws
 
@@ -376,7 +420,8 @@ def all_configs(reps):
     for tag, fl in (("warm", False), ("flushed", True)):
         ms = timed(fn, fl)
         row[tag] = {"ms": round(ms, 5), "kv_gbs": round(kv_bytes / ms / 1e6, 1),
-                    "frac_roofline": round(t_roof / ms, 3)}
+                    "frac_roofline": round(t_roof / ms, 3),
+                    "frac_measured": meas(0, kv_bytes + qo_bytes, ms)}
     print(json.dumps(row), flush=True)
     del q, kr, vr, ks, vs, out, ws
 
@@ -396,7 +441,8 @@ def all_configs(reps):
     for tag, fl in (("warm", False), ("flushed", True)):
         ms = timed(fn, fl)
         row[tag] = {"ms": round(ms, 5), "tflops": round(flops / ms / 1e9, 1),
-                    "gbs": round(bytes_ / ms / 1e6, 1), "frac_roofline": round(t_roof / ms, 3)}
+                    "gbs": round(bytes_ / ms / 1e6, 1), "frac_roofline": round(t_roof / ms, 3),
+                    "frac_measured": meas(flops, bytes_, ms)}
     print(json.dumps(row), flush=True)
     # the append rewrites the same slots every repetition (same positions)
     fn = lambda: swa.cache_append_chunk(kr, vr, pos, k, v)  # noqa: E731
@@ -408,7 +454,8 @@ def all_configs(reps):
     for tag, fl in (("warm", False), ("flushed", True)):
         ms = timed(fn, fl)
         row[tag] = {"ms": round(ms, 5), "gbs": round(bytes_ / ms / 1e6, 1),
-                    "frac_roofline": round(t_roof / ms, 3)}
+                    "frac_roofline": round(t_roof / ms, 3),
+                    "frac_measured": meas(0, bytes_, ms)}
     print(json.dumps(row), flush=True)
     return 0
 
@@ -442,6 +489,9 @@ def main():
     ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
                     help="turn rocprofv3 MFMA / instruction counter CSVs of a --pmc-workload run "
                          "into utilisation figures")
+    ap.add_argument("--peaks", action="store_true",
+                    help="instead of the benchmark line: the matrix-core and streaming-read "
+                         "rates the box sustains (the library's calibration kernels)")
     ap.add_argument("--all-configs", action="store_true",
                     help="instead of the benchmark line: every configuration, cache-warm and "
                          "flushed, against its roofline (one JSON line each)")
@@ -450,8 +500,8 @@ def main():
         return summarize_pmc(args.summarize_pmc)
     if args.summarize_counters:
         return summarize_counters(args.summarize_counters)
-    if args.all_configs:
-        return all_configs(max(args.steps, 20))
+    if args.all_configs or args.peaks:
+        return all_configs(max(args.steps, 20), peaks_only=args.peaks)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

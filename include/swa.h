@@ -290,6 +290,36 @@ size_t swa_decode_sinks_workspace_bytes(int B, int Hq, int W, int d);
 /* Workspace bytes swa_decode needs for these sizes (0 for invalid sizes). */
 size_t swa_decode_workspace_bytes(int B, int Hq, int W, int d);
 
+/*
+ * Calibration kernels.  They compute nothing of the attention method: they
+ * measure, on the box the attention kernels run on, the two ceilings those
+ * kernels are bound by, so that their throughput can be quoted against what
+ * the chip sustains as well as against its published peaks.
+ *
+ * swa_calib_mfma_bf16 - n_wg workgroups of four waves; each wave runs
+ * iters x 16 v_mfma_f32_32x32x16_bf16 (32,768 FLOPs each) on operands taken
+ * from `operands` (device, bf16 bits, operand_bytes a multiple of 16, at
+ * least 16; random data gives the chip's power-limited rate, which is what
+ * attention operands see), rotating four A and four B fragments per lane
+ * over four accumulator chains.  Total FLOPs = n_wg * 4 * iters * 16 * 32768.
+ *   sink   output float [n_wg * 256] (per-lane sums, keeps the work live).
+ *   Errors: SWA_ERR_INVALID_ARG for null or unaligned pointers, bad sizes,
+ *   n_wg outside [1, 2^20], iters < 0; SWA_ERR_LAUNCH on launch failure.
+ *
+ * swa_calib_stream_read - reads `bytes` (a multiple of 16) from device memory
+ * `src` with 16-byte non-temporal loads: workgroup w of n_wg (256 lanes,
+ * eight loads in flight per lane) reads the w-th contiguous chunk.  Use a
+ * buffer larger than the 256 MB Infinity Cache to measure HBM.
+ *   sink   output uint32 [n_wg * 256] (XOR of what each lane read).
+ *   Errors as above (n_wg >= 1).
+ *
+ * Both are asynchronous on `stream`; time them with events on that stream.
+ */
+int swa_calib_mfma_bf16(const void* operands, size_t operand_bytes, float* sink, int n_wg,
+                        int iters, void* stream);
+int swa_calib_stream_read(const void* src, size_t bytes, unsigned* sink, int n_wg,
+                          void* stream);
+
 /* Static, human-readable text for a swa_status value. */
 const char* swa_status_string(int status);
 

@@ -71,6 +71,10 @@ def load():
     lib.swa_prefill_global_workspace_bytes.restype = sz
     lib.swa_decode_workspace_bytes.argtypes = [i, i, i, i]
     lib.swa_decode_workspace_bytes.restype = sz
+    lib.swa_calib_mfma_bf16.argtypes = [vp, sz, vp, i, i, vp]
+    lib.swa_calib_mfma_bf16.restype = i
+    lib.swa_calib_stream_read.argtypes = [vp, sz, vp, i, vp]
+    lib.swa_calib_stream_read.restype = i
     lib.swa_status_string.argtypes = [i]
     lib.swa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -351,3 +355,34 @@ def decode_sinks(q, k_ring, v_ring, k_sink, v_sink, pos, scale=None, out=None, w
                                  workspace.numel() * workspace.element_size(), _stream(stream))
     _raise("swa_decode_sinks", st)
     return out
+
+
+def calib_mfma(operands, sink, n_wg, iters, stream=None):
+    """Matrix-core calibration loop (see swa_calib_mfma_bf16): `operands` a
+    device bf16 tensor of random values, `sink` a float32 tensor of at least
+    n_wg * 256 elements.  Returns the FLOPs it issues."""
+    import torch
+    _check(operands, "operands", operands.dim(), torch.bfloat16)
+    _check(sink, "sink", sink.dim(), torch.float32)
+    if sink.numel() < n_wg * 256:
+        raise ValueError("sink needs n_wg * 256 elements")
+    st = load().swa_calib_mfma_bf16(operands.data_ptr(), operands.numel() * 2, sink.data_ptr(),
+                                    int(n_wg), int(iters), _stream(stream))
+    _raise("swa_calib_mfma_bf16", st)
+    return n_wg * 4 * iters * 16 * 32768
+
+
+def calib_stream_read(src, sink, n_wg, stream=None):
+    """Streaming-read calibration (see swa_calib_stream_read) of the whole of
+    the contiguous device tensor `src`; `sink` an int32 tensor of at least
+    n_wg * 256 elements.  Returns the bytes it reads."""
+    import torch
+    _check(src, "src", src.dim())
+    _check(sink, "sink", sink.dim(), torch.int32)
+    if sink.numel() < n_wg * 256:
+        raise ValueError("sink needs n_wg * 256 elements")
+    nbytes = src.numel() * src.element_size()
+    st = load().swa_calib_stream_read(src.data_ptr(), nbytes, sink.data_ptr(), int(n_wg),
+                                      _stream(stream))
+    _raise("swa_calib_stream_read", st)
+    return nbytes

@@ -26,7 +26,8 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
 ]
 
-SOURCES = ["swa_prefill_bf16.hip", "swa_prefill_f32.hip", "swa_ring.hip", "swa_api.cpp"]
+SOURCES = ["swa_prefill_bf16.hip", "swa_prefill_f32.hip", "swa_ring.hip", "swa_calib.hip",
+           "swa_api.cpp"]
 
 
 def _compile(src, csrc=CSRC, build_dir=BUILD, defines=()):

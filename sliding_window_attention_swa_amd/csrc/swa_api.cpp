@@ -236,6 +236,30 @@ int swa_decode_sinks(const void* q, const void* k_ring, const void* v_ring, cons
   return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH;
 }
 
+int swa_calib_mfma_bf16(const void* operands, size_t operand_bytes, float* sink, int n_wg,
+                        int iters, void* stream) {
+  if (!operands || !sink) return SWA_ERR_INVALID_ARG;
+  if (!aligned16(operands) || !aligned16(sink)) return SWA_ERR_INVALID_ARG;
+  if (operand_bytes < 16 || operand_bytes % 16 != 0) return SWA_ERR_INVALID_ARG;
+  if (operand_bytes / 16 > 2147483647ULL) return SWA_ERR_UNSUPPORTED;
+  // fragment indices 8 * (workgroup * 256 + lane) + 7 stay in int
+  if (n_wg <= 0 || n_wg > (1 << 20) || iters < 0) return SWA_ERR_INVALID_ARG;
+  const hipError_t e = swa::launch_calib_mfma(operands, (int)(operand_bytes / 16), sink, n_wg,
+                                              iters, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH;
+}
+
+int swa_calib_stream_read(const void* src, size_t bytes, unsigned* sink, int n_wg,
+                          void* stream) {
+  if (!src || !sink) return SWA_ERR_INVALID_ARG;
+  if (!aligned16(src) || !aligned16(sink)) return SWA_ERR_INVALID_ARG;
+  if (bytes < 16 || bytes % 16 != 0 || n_wg <= 0) return SWA_ERR_INVALID_ARG;
+  if ((long long)n_wg > kMaxGrid / 256) return SWA_ERR_UNSUPPORTED;
+  const hipError_t e =
+      swa::launch_calib_read(src, bytes / 16, sink, n_wg, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH;
+}
+
 const char* swa_status_string(int status) {
   switch (status) {
     case SWA_OK:

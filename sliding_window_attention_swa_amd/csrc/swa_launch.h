@@ -93,4 +93,11 @@ hipError_t launch_decode(const void* q, const void* k_ring, const void* v_ring,
                          const int32_t* pos, void* out, int B, int Hq, int Hkv, int W, int d,
                          float scale, int dtype, float* workspace, hipStream_t stream);
 
+// Calibration: a matrix-core loop on random bf16 operands (nfrag 16-byte
+// fragments) and a streaming non-temporal read of n16 16-byte vectors.
+hipError_t launch_calib_mfma(const void* ops, int nfrag, float* sink, int n_wg, int iters,
+                             hipStream_t stream);
+hipError_t launch_calib_read(const void* src, size_t n16, unsigned* sink, int n_wg,
+                             hipStream_t stream);
+
 }  // namespace swa

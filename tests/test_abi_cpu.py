@@ -30,7 +30,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(swa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(swa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_entry_points():
@@ -38,7 +38,8 @@ def test_header_declares_the_entry_points():
         "swa_prefill", "swa_cache_append", "swa_decode", "swa_decode_workspace_bytes",
         "swa_status_string", "swa_cache_append_chunk", "swa_prefill_chunk",
         "swa_prefill_dilated", "swa_prefill_global", "swa_prefill_global_workspace_bytes",
-        "swa_decode_sinks", "swa_decode_sinks_workspace_bytes"])
+        "swa_decode_sinks", "swa_decode_sinks_workspace_bytes", "swa_calib_mfma_bf16",
+        "swa_calib_stream_read"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -228,6 +229,33 @@ def test_workspace_bytes(lib):
         assert n > 0 and n % (4 * (d + 2) * B * Hq) == 0
         splits = n // (4 * (d + 2) * B * Hq)
         assert 1 <= splits <= max(1, (W + 63) // 64)
+
+
+def calib_mfma(lib, ops=P, nbytes=65536, sink=P, n_wg=8, iters=10):
+    return lib.swa_calib_mfma_bf16(ops, nbytes, sink, n_wg, iters, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ops=None), INVALID), (dict(sink=None), INVALID), (dict(ops=MIS), INVALID),
+    (dict(sink=MIS), INVALID), (dict(nbytes=0), INVALID), (dict(nbytes=8), INVALID),
+    (dict(nbytes=65540), INVALID), (dict(n_wg=0), INVALID), (dict(n_wg=2**20 + 1), INVALID),
+    (dict(iters=-1), INVALID), (dict(nbytes=2**36), UNSUPPORTED),
+])
+def test_calib_mfma_rejects(lib, kw, status):
+    assert calib_mfma(lib, **kw) == status
+
+
+def calib_read(lib, src=P, nbytes=2**20, sink=P, n_wg=8):
+    return lib.swa_calib_stream_read(src, nbytes, sink, n_wg, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(src=None), INVALID), (dict(sink=None), INVALID), (dict(src=MIS), INVALID),
+    (dict(sink=MIS), INVALID), (dict(nbytes=0), INVALID), (dict(nbytes=2**20 + 4), INVALID),
+    (dict(n_wg=0), INVALID), (dict(n_wg=2**24), UNSUPPORTED),
+])
+def test_calib_read_rejects(lib, kw, status):
+    assert calib_read(lib, **kw) == status
 
 
 def test_status_strings(lib):
