@@ -489,6 +489,9 @@ def main():
     ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
                     help="turn rocprofv3 MFMA / instruction counter CSVs of a --pmc-workload run "
                          "into utilisation figures")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measurement of the box's sustained matrix and read rates "
+                         "after the timed steps")
     ap.add_argument("--peaks", action="store_true",
                     help="instead of the benchmark line: the matrix-core and streaming-read "
                          "rates the box sustains (the library's calibration kernels)")
@@ -588,6 +591,18 @@ def main():
 
     traffic = read_traffic("", PREFILL_SOURCE)
     dec_traffic = read_traffic("decode_", DECODE_SOURCE)
+    peaks = None
+    if not args.no_peaks:  # after the timed region: what this machine sustains
+        def timed(fn, flushed):
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(8)]
+            for a, b in ev:
+                a.record()
+                fn()
+                b.record()
+            torch.cuda.synchronize()
+            return float(np.median([a.elapsed_time(b) for a, b in ev[2:]]))
+        peaks = measured_peaks(swa, dev, timed)
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -628,6 +643,8 @@ def main():
             "kernel": "prefill_bf16_kernel<128, causal>",
             "algorithmic_flops_per_launch": pre_flops,
             "algorithmic_bytes_per_launch": pre_bytes,
+            "measured_peak": peaks["mfma_bf16_tflops"] if peaks else None,
+            "frac_measured": round(pre_tflops / peaks["mfma_bf16_tflops"], 4) if peaks else None,
         },
         "decode_roofline": {
             "bound": "hbm",
@@ -638,6 +655,8 @@ def main():
             "traffic": dec_traffic,
             "kernel": "decode_split_kernel<bf16, 128, 4>",
             "algorithmic_bytes_per_launch": dec_kv_bytes + dec_qo_bytes,
+            "measured_peak": peaks["stream_read_gbs"] if peaks else None,
+            "frac_measured": round(dec_gbs / peaks["stream_read_gbs"], 4) if peaks else None,
         },
         "wall_s_timed": round(wall, 3),
     }
