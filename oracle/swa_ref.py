@@ -448,16 +448,21 @@ def attention_dilated_rows(q, k, v, W, mode, scale, dilation, b, h, rows):
 # Sliding window plus global tokens
 # --------------------------------------------------------------------------
 
-def global_mask(T, W, mode, global_pos):
+def global_mask(T, W, mode, global_pos, dilation=1):
     """Boolean [T, T] mask of the window plus global tokens.
 
     aivaro section 4.3 (Longformer global attention) and robocikowo's global
     tokens entry: a global token attends to every token and every token
     attends to it, on top of the sliding window.  In the causal mode the
     added pairs keep j <= i (no token sees a later one).  global_pos lists
-    distinct positions in [0, T).
+    distinct positions in [0, T).  With dilation > 1 the window is the
+    dilated one of section 4.2 (dilated_mask); Longformer combines the two,
+    and the global pairs are the same.
     """
-    m = window_mask(T, W, mode).copy()
+    if dilation == 1:
+        m = window_mask(T, W, mode).copy()
+    else:
+        m = dilated_mask(T, W, mode, dilation).copy()
     g = np.zeros(T, dtype=bool)
     g[np.asarray(global_pos, dtype=np.int64)] = True
     extra = g[:, None] | g[None, :]
@@ -466,11 +471,11 @@ def global_mask(T, W, mode, global_pos):
     return m | extra
 
 
-def attention_global_dense(q, k, v, W, mode, scale, global_pos):
+def attention_global_dense(q, k, v, W, mode, scale, global_pos, dilation=1):
     """Dense [T, T] scores plus the additive form of global_mask."""
     q, k, v = _as64(q, k, v)
     B, Hq, Hkv, T, d = _check_shapes(q, k, v)
-    M = np.where(global_mask(T, W, mode, global_pos), 0.0, -np.inf)
+    M = np.where(global_mask(T, W, mode, global_pos, dilation), 0.0, -np.inf)
     out = np.empty((B, Hq, T, d))
     for b in range(B):
         for h in range(Hq):
@@ -480,10 +485,10 @@ def attention_global_dense(q, k, v, W, mode, scale, global_pos):
     return out
 
 
-def attention_global_rows(q, k, v, W, mode, scale, global_pos, b, h, rows):
+def attention_global_rows(q, k, v, W, mode, scale, global_pos, b, h, rows, dilation=1):
     """Selected query rows of one (b, h) over exactly their keys: the
-    window, the global keys (j <= i when causal), or, for a global row, every
-    key (j <= i when causal).  Returns float64 [len(rows), d]."""
+    (dilated) window, the global keys (j <= i when causal), or, for a global
+    row, every key (j <= i when causal).  Returns float64 [len(rows), d]."""
     B, Hq, T, d = q.shape
     g = kv_head(h, Hq, k.shape[1])
     gset = set(int(x) for x in global_pos)
@@ -493,9 +498,16 @@ def attention_global_rows(q, k, v, W, mode, scale, global_pos, b, h, rows):
         if i in gset:
             keys = np.arange(0, i + 1) if mode == CAUSAL else np.arange(T)
         else:
-            lo, hi = band(i, T, W, mode)
-            extra = [x for x in gset if (x <= i or mode != CAUSAL) and not lo <= x <= hi]
-            keys = np.sort(np.concatenate([np.arange(lo, hi + 1), np.array(extra, dtype=np.int64)]))
+            if dilation == 1:
+                lo, hi = band(i, T, W, mode)
+                window = np.arange(lo, hi + 1)
+            else:
+                m = np.arange(0, W) if mode == CAUSAL else np.arange(-(W // 2), W // 2 + 1)
+                window = i - dilation * m
+                window = window[(window >= 0) & (window < T)]
+            wset = set(int(x) for x in window)
+            extra = [x for x in gset if (x <= i or mode != CAUSAL) and x not in wset]
+            keys = np.sort(np.concatenate([window, np.array(extra, dtype=np.int64)]))
         qi = np.asarray(q[b, h, i], dtype=np.float64)
         kk = np.asarray(k[b, g, keys], dtype=np.float64)
         vv = np.asarray(v[b, g, keys], dtype=np.float64)

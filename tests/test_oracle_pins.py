@@ -584,6 +584,87 @@ def test_mutant_global_columns_only_is_caught():
     assert np.abs(wrong[g] - full[g]).max() > 1e-3
 
 
+# ------------------------------------------ dilated window plus global tokens
+
+def brute_dilated_global(T, W, mode, dil, gpos):
+    """Pair by pair: key j is in query i's dilated window (i - j a multiple of
+    dil whose quotient lies in the plain window), or i or j is a global
+    position (j <= i when causal)."""
+    g = set(gpos)
+    M = np.zeros((T, T), dtype=bool)
+    for i in range(T):
+        for j in range(T):
+            win = False
+            if (i - j) % dil == 0:
+                m = (i - j) // dil
+                win = 0 <= m <= W - 1 if mode == CAUSAL else -(W // 2) <= m <= W // 2
+            M[i, j] = win or ((i in g or j in g) and (mode != CAUSAL or j <= i))
+    return M
+
+
+@pytest.mark.parametrize("T,W,mode,dil,gpos", [
+    (12, 3, CAUSAL, 2, [0]), (12, 3, SYMMETRIC, 2, [5]), (17, 4, CAUSAL, 3, [0, 1, 16]),
+    (17, 5, SYMMETRIC, 3, [2, 9]), (9, 1, CAUSAL, 2, [4]), (20, 6, SYMMETRIC, 4, [0, 10, 19]),
+    (7, 10, CAUSAL, 2, [3]), (11, 2, SYMMETRIC, 5, []),
+])
+def test_dilated_global_mask_by_brute_force(T, W, mode, dil, gpos):
+    assert np.array_equal(oracle.global_mask(T, W, mode, gpos, dil),
+                          brute_dilated_global(T, W, mode, dil, gpos))
+
+
+def test_dilated_global_pair_counts_by_hand():
+    """T = 8, W = 2, dilation 2.  Causal, global position 0: row i sees i and
+    i - 2 (14 pairs); key 0 adds rows 1, 3, 4, 5, 6, 7 (row 2 already sees it
+    through its window, row 0 is the global row and sees only key 0): 20.
+    Symmetric, global position 3: row i sees i and i +- 2 inside [0, 8)
+    (2+2+3+3+3+3+2+2 = 20); row 3 sees the 5 keys 0, 2, 4, 6, 7 beyond its
+    window and column 3 adds rows 0, 2, 4, 6, 7 (rows 1 and 5 have it): 30."""
+    assert int(oracle.global_mask(8, 2, CAUSAL, [0], 2).sum()) == 20
+    assert int(oracle.global_mask(8, 2, SYMMETRIC, [3], 2).sum()) == 30
+
+
+@pytest.mark.parametrize("mode", [CAUSAL, SYMMETRIC])
+def test_dilated_global_reduces_to_its_parts(mode):
+    T, W = 40, 5
+    assert np.array_equal(oracle.global_mask(T, W, mode, [], 3), oracle.dilated_mask(T, W, mode, 3))
+    assert np.array_equal(oracle.global_mask(T, W, mode, [2, 30], 1),
+                          oracle.global_mask(T, W, mode, [2, 30]))
+
+
+@pytest.mark.parametrize("mode", [CAUSAL, SYMMETRIC])
+def test_dilated_global_rows_agree_with_dense(mode):
+    T, W, dil = 45, 6, 3
+    gpos = [0, 9, 10, 44]
+    q, k, v = rand((1, 4, T, 8), 115), rand((1, 2, T, 8), 116), rand((1, 2, T, 8), 117)
+    dense = oracle.attention_global_dense(q, k, v, W, mode, 0.5, gpos, dil)
+    rows = [0, 1, 3, 5, 9, 10, 11, 12, 20, 43, 44]
+    for h in range(4):
+        got = oracle.attention_global_rows(q, k, v, W, mode, 0.5, gpos, 0, h, rows, dil)
+        np.testing.assert_allclose(got, dense[0, h, rows], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", [CAUSAL, SYMMETRIC])
+def test_dilated_global_token_row_is_full_attention(mode):
+    T, gpos = 30, [4, 21]
+    q, k, v = rand((1, 2, T, 8), 118), rand((1, 2, T, 8), 119), rand((1, 2, T, 8), 120)
+    got = oracle.attention_global_dense(q, k, v, 3, mode, 0.6, gpos, 4)
+    full = sdpa(q, k, v, 0.6, is_causal=mode == CAUSAL)
+    np.testing.assert_allclose(got[:, :, gpos], full[:, :, gpos], rtol=0, atol=1e-12)
+
+
+def test_mutant_plain_window_exclusion_is_caught():
+    """Excluding a global key from a row when it lies in the row's plain
+    (undilated) span rather than on its dilated grid would drop keys the row
+    must see: the brute-force mask tells them apart."""
+    T, W, dil, gpos = 12, 3, 2, [5]
+    wrong = oracle.dilated_mask(T, W, SYMMETRIC, dil).copy()
+    for i in range(T):
+        if abs(i - 5) > W // 2:  # outside the plain span: the (wrong) rule adds the column
+            wrong[i, 5] = True
+    wrong[5, :] = True
+    assert not np.array_equal(wrong, brute_dilated_global(T, W, SYMMETRIC, dil, gpos))
+
+
 # ------------------------------------------------------ attention sinks
 
 @pytest.mark.parametrize("W,S,T", [(4, 2, 16), (5, 4, 30), (8, 8, 20), (3, 1, 9), (6, 9, 25)])
