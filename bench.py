@@ -261,18 +261,20 @@ def band_pairs(T, W, mode, dilation=1):
     return int((left + right + 1).sum())
 
 
-def global_pairs(T, W, mode, gpos):
-    """(query, key) pairs of one head for the window plus global tokens: each
-    row's window, plus the global keys outside it (not after the row when
-    causal); a global row has every key (every earlier key when causal)."""
+def global_pairs(T, W, mode, gpos, dilation=1):
+    """(query, key) pairs of one head for the (dilated) window plus global
+    tokens: each row's window, plus the global keys outside it (not after the
+    row when causal); a global row has every key (every earlier key when
+    causal)."""
     i = np.arange(T, dtype=np.int64)
-    if mode == 0:
-        lo, hi = np.maximum(0, i - W + 1), i
-    else:
-        lo, hi = np.maximum(0, i - W // 2), np.minimum(T - 1, i + W // 2)
-    n = hi - lo + 1
+    mlo, mhi = (0, W - 1) if mode == 0 else (-(W // 2), W // 2)  # offsets m = (i - j) / dilation
+    top = np.minimum(mhi, i // dilation)                 # keys j = i - m * dilation >= 0
+    bot = np.maximum(mlo, -((T - 1 - i) // dilation))    # keys j < T
+    n = np.maximum(0, top - bot + 1)
     g = np.asarray(sorted(set(int(x) for x in gpos)), dtype=np.int64)
-    outside = (g[None, :] < lo[:, None]) | (g[None, :] > hi[:, None])
+    diff = i[:, None] - g[None, :]
+    m = diff // dilation
+    outside = ~((diff % dilation == 0) & (m >= mlo) & (m <= mhi))
     if mode == 0:
         outside &= g[None, :] <= i[:, None]
     n = n + outside.sum(axis=1)
@@ -368,27 +370,31 @@ def all_configs(reps, peaks_only=False):
         print(json.dumps(row), flush=True)
         del q, k, v, out
 
-    # window plus global tokens
-    c = si.WORKLOADS[8]
-    q, k, v = (si.to_torch(t, dev) for t in si.prefill_inputs(8))
-    out = torch.empty_like(q)
-    gpos = torch.tensor(c["global_pos"], dtype=torch.int32, device=dev)
-    ws = swa.global_workspace(c["T"], c["B"] * c["Hq"], len(c["global_pos"]), c["d"], dev)
-    fn = lambda: swa.prefill_global(q, k, v, c["W"], gpos, mode=c["mode"],  # noqa: E731
-                                    scale=1.0 / math.sqrt(c["d"]), out=out, workspace=ws)
-    flops = 4 * c["d"] * global_pairs(c["T"], c["W"], c["mode"], c["global_pos"]) * c["Hq"] * c["B"]
-    bytes_ = 2 * c["T"] * c["d"] * c["B"] * (2 * c["Hq"] + 2 * c["Hkv"])
-    t_roof = max(flops / (PEAK_BF16_TFLOPS * 1e12), bytes_ / (PEAK_HBM_GBS * 1e9)) * 1e3
-    bound = "mfma" if flops / PEAK_BF16_TFLOPS / 1e12 >= bytes_ / PEAK_HBM_GBS / 1e9 else "hbm"
-    row = {"config": c["name"], "kernel": "prefill_global", "bound": bound,
-           "roofline_ms": round(t_roof, 5)}
-    for tag, fl in (("warm", False), ("flushed", True)):
-        ms = timed(fn, fl)
-        row[tag] = {"ms": round(ms, 5), "tflops": round(flops / ms / 1e9, 1),
-                    "gbs": round(bytes_ / ms / 1e6, 1), "frac_roofline": round(t_roof / ms, 3),
-                    "frac_measured": meas(flops, bytes_, ms)}
-    print(json.dumps(row), flush=True)
-    del q, k, v, out, ws
+    # window (plain, then dilated) plus global tokens
+    for wl in (8, 9):
+        c = si.WORKLOADS[wl]
+        dil = c.get("dilation", 1)
+        q, k, v = (si.to_torch(t, dev) for t in si.prefill_inputs(wl))
+        out = torch.empty_like(q)
+        gpos = torch.tensor(c["global_pos"], dtype=torch.int32, device=dev)
+        ws = swa.global_workspace(c["T"], c["B"] * c["Hq"], len(c["global_pos"]), c["d"], dev)
+        fn = lambda: swa.prefill_global(q, k, v, c["W"], gpos, mode=c["mode"],  # noqa: E731
+                                        scale=1.0 / math.sqrt(c["d"]), out=out, workspace=ws,
+                                        dilation=dil)
+        flops = (4 * c["d"] * global_pairs(c["T"], c["W"], c["mode"], c["global_pos"], dil)
+                 * c["Hq"] * c["B"])
+        bytes_ = 2 * c["T"] * c["d"] * c["B"] * (2 * c["Hq"] + 2 * c["Hkv"])
+        t_roof = max(flops / (PEAK_BF16_TFLOPS * 1e12), bytes_ / (PEAK_HBM_GBS * 1e9)) * 1e3
+        bound = "mfma" if flops / PEAK_BF16_TFLOPS / 1e12 >= bytes_ / PEAK_HBM_GBS / 1e9 else "hbm"
+        row = {"config": c["name"], "kernel": "prefill_global", "bound": bound,
+               "roofline_ms": round(t_roof, 5)}
+        for tag, fl in (("warm", False), ("flushed", True)):
+            ms = timed(fn, fl)
+            row[tag] = {"ms": round(ms, 5), "tflops": round(flops / ms / 1e9, 1),
+                        "gbs": round(bytes_ / ms / 1e6, 1), "frac_roofline": round(t_roof / ms, 3),
+                        "frac_measured": meas(flops, bytes_, ms)}
+        print(json.dumps(row), flush=True)
+        del q, k, v, out, ws
 
     c = si.WORKLOADS[4]
     q_np, kr_np, vr_np, pos_np = si.decode_inputs(4)

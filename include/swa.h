@@ -158,6 +158,25 @@ int swa_prefill_global(const void* q, const void* k, const void* v, void* out, i
                        int G, void* workspace, size_t workspace_bytes, int dtype, void* stream);
 
 /*
+ * swa_prefill_dilated_global - dilated window plus global tokens.
+ *
+ * aivaro.ru answer 629, sections 4.2 and 4.3: Longformer combines the two.
+ * A non-global row i attends to its dilated window (keys i - m * dilation
+ * for m in the plain window's offsets, as swa_prefill_dilated) plus the
+ * global keys not already in it (j <= i when causal); a global row attends
+ * to every key (j <= i when causal), as in swa_prefill_global.
+ * dilation = 1 is swa_prefill_global; G = 0 is swa_prefill_dilated.
+ *
+ *   Arguments, layouts, workspace and errors as swa_prefill_global, plus
+ *   dilation >= 1 (SWA_ERR_INVALID_ARG otherwise), with
+ *   64 * dilation * d * element size < 2^31 (SWA_ERR_UNSUPPORTED).
+ */
+int swa_prefill_dilated_global(const void* q, const void* k, const void* v, void* out, int T,
+                               int W, int Hq, int Hkv, int d, int mode, float scale, int dilation,
+                               const int32_t* global_pos, int G, void* workspace,
+                               size_t workspace_bytes, int dtype, void* stream);
+
+/*
  * swa_cache_append - write one new K/V row per sequence into the ring cache.
  *
  *   k_ring[b, :, pos[b] mod W, :] = k_new[b, :, :]   (and the same for v)

@@ -55,6 +55,9 @@ def load():
     lib.swa_prefill_dilated.restype = i
     lib.swa_prefill_global.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i, vp, sz, i, vp]
     lib.swa_prefill_global.restype = i
+    lib.swa_prefill_dilated_global.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, i, vp,
+                                               sz, i, vp]
+    lib.swa_prefill_dilated_global.restype = i
     lib.swa_cache_append.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.swa_cache_append.restype = i
     lib.swa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
@@ -166,10 +169,11 @@ def prefill_dilated(q, k, v, W, dilation, mode=CAUSAL, scale=None, out=None, str
 
 
 def prefill_global(q, k, v, W, global_pos, mode=CAUSAL, scale=None, out=None, workspace=None,
-                   stream=None):
+                   stream=None, dilation=1):
     """Windowed attention plus global tokens at the positions `global_pos`
     (device int32 [G], strictly increasing): they attend to every key and
-    every row attends to them (j <= i when causal).  Returns out [B, Hq, T, d]."""
+    every row attends to them (j <= i when causal).  With dilation > 1 the
+    window is the dilated one of `prefill_dilated`.  Returns out [B, Hq, T, d]."""
     import torch
     _check(q, "q", 4)
     _check(k, "k", 4, q.dtype)
@@ -189,12 +193,14 @@ def prefill_global(q, k, v, W, global_pos, mode=CAUSAL, scale=None, out=None, wo
     G = global_pos.shape[0]
     if workspace is None:
         workspace = global_workspace(T, B * Hq, G, d, q.device)
-    st = load().swa_prefill_global(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), T,
-                                   int(W), B * Hq, B * Hkv, d, int(mode), float(scale),
-                                   global_pos.data_ptr() if G else None, G, workspace.data_ptr(),
-                                   workspace.numel() * workspace.element_size(), _dtype_code(q),
-                                   _stream(stream))
-    _raise("swa_prefill_global", st)
+    st = load().swa_prefill_dilated_global(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                           out.data_ptr(), T, int(W), B * Hq, B * Hkv, d,
+                                           int(mode), float(scale), int(dilation),
+                                           global_pos.data_ptr() if G else None, G,
+                                           workspace.data_ptr(),
+                                           workspace.numel() * workspace.element_size(),
+                                           _dtype_code(q), _stream(stream))
+    _raise("swa_prefill_dilated_global", st)
     return out
 
 

@@ -68,22 +68,27 @@ int swa_prefill_dilated(const void* q, const void* k, const void* v, void* out, 
   return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH;
 }
 
-int swa_prefill_global(const void* q, const void* k, const void* v, void* out, int T, int W,
-                       int Hq, int Hkv, int d, int mode, float scale, const int32_t* global_pos,
-                       int G, void* workspace, size_t workspace_bytes, int dtype, void* stream) {
-  if (G == 0)
-    return swa_prefill(q, k, v, out, T, W, Hq, Hkv, d, mode, scale, dtype, stream);
+// Window (dilated when dilation > 1) plus global tokens: the window pass
+// visits the global keys, then the global rows are computed over every key.
+static int prefill_global_impl(const void* q, const void* k, const void* v, void* out, int T,
+                               int W, int Hq, int Hkv, int d, int mode, float scale,
+                               int dilation, const int32_t* global_pos, int G, void* workspace,
+                               size_t workspace_bytes, int dtype, void* stream) {
   if (!q || !k || !v || !out || !global_pos) return SWA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(global_pos))
     return SWA_ERR_INVALID_ARG;
-  if (T <= 0 || W <= 0 || Hq <= 0 || Hkv <= 0 || G < 0) return SWA_ERR_INVALID_ARG;
+  if (T <= 0 || W <= 0 || Hq <= 0 || Hkv <= 0 || G < 0 || dilation <= 0) return SWA_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return SWA_ERR_INVALID_ARG;
   if (!isfinite(scale)) return SWA_ERR_INVALID_ARG;
   if (!supported_d(d) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
   if (mode != SWA_CAUSAL && mode != SWA_SYMMETRIC) return SWA_ERR_UNSUPPORTED;
-  // global keys are gathered with 32-bit byte offsets into a head's K/V
+  // global keys are gathered with 32-bit byte offsets into a head's K/V, and
+  // a tile's 64 rows, dilation rows apart, likewise
   if ((long long)T * d * elem_bytes(dtype) > 2147483647LL) return SWA_ERR_UNSUPPORTED;
+  if ((long long)dilation * d * elem_bytes(dtype) * 64 > 2147483647LL) return SWA_ERR_UNSUPPORTED;
   if ((long long)((T + 15) / 16) * Hq > kMaxGrid) return SWA_ERR_UNSUPPORTED;
+  const long long class_rows = (T + (long long)dilation - 1) / dilation;
+  if ((class_rows + 127) / 128 * Hq * (long long)dilation > kMaxGrid) return SWA_ERR_UNSUPPORTED;
   const int S = swa::global_splits(G, Hq, T);
   if ((long long)G * Hq * S > kMaxGrid) return SWA_ERR_UNSUPPORTED;
   const int S1 = swa::global_rows_mfma_splits(T);
@@ -93,9 +98,9 @@ int swa_prefill_global(const void* q, const void* k, const void* v, void* out, i
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = (dtype == SWA_BF16)
                      ? swa::launch_prefill_global_window_bf16(q, k, v, out, T, W, Hq, Hkv, d, mode,
-                                                              scale, global_pos, G, s)
+                                                              scale, global_pos, G, dilation, s)
                      : swa::launch_prefill_global_window_f32(q, k, v, out, T, W, Hq, Hkv, d, mode,
-                                                             scale, global_pos, G, s);
+                                                             scale, global_pos, G, dilation, s);
   if (e != hipSuccess) return SWA_ERR_LAUNCH;
   float* ws = static_cast<float*>(workspace);
   if (dtype == SWA_BF16) {  // the global rows on the matrix cores, then their merge
@@ -108,6 +113,29 @@ int swa_prefill_global(const void* q, const void* k, const void* v, void* out, i
                                 s);
   }
   return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH;
+}
+
+int swa_prefill_global(const void* q, const void* k, const void* v, void* out, int T, int W,
+                       int Hq, int Hkv, int d, int mode, float scale, const int32_t* global_pos,
+                       int G, void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  if (G == 0)
+    return swa_prefill(q, k, v, out, T, W, Hq, Hkv, d, mode, scale, dtype, stream);
+  return prefill_global_impl(q, k, v, out, T, W, Hq, Hkv, d, mode, scale, 1, global_pos, G,
+                             workspace, workspace_bytes, dtype, stream);
+}
+
+int swa_prefill_dilated_global(const void* q, const void* k, const void* v, void* out, int T,
+                               int W, int Hq, int Hkv, int d, int mode, float scale, int dilation,
+                               const int32_t* global_pos, int G, void* workspace,
+                               size_t workspace_bytes, int dtype, void* stream) {
+  if (G == 0)
+    return swa_prefill_dilated(q, k, v, out, T, W, Hq, Hkv, d, mode, scale, dilation, dtype,
+                               stream);
+  if (dilation == 1)
+    return swa_prefill_global(q, k, v, out, T, W, Hq, Hkv, d, mode, scale, global_pos, G,
+                              workspace, workspace_bytes, dtype, stream);
+  return prefill_global_impl(q, k, v, out, T, W, Hq, Hkv, d, mode, scale, dilation, global_pos, G,
+                             workspace, workspace_bytes, dtype, stream);
 }
 
 int swa_cache_append(void* k_ring, void* v_ring, const int32_t* pos, const void* k_new,

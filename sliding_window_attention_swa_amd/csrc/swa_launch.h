@@ -26,17 +26,17 @@ hipError_t launch_prefill_dilated_f32(const void* q, const void* k, const void* 
                                       int T, int W, int Hq, int Hkv, int d, int mode, float scale,
                                       int dil, hipStream_t stream);
 
-// Window plus global keys for every row (the global rows are left for
-// launch_global_rows).
+// Window (dilated when dil > 1) plus global keys for every row (the global
+// rows are left for the global-row pass).
 hipError_t launch_prefill_global_window_bf16(const void* q, const void* k, const void* v,
                                              void* out, int T, int W, int Hq, int Hkv, int d,
                                              int mode, float scale, const int32_t* gpos, int ngl,
-                                             hipStream_t stream);
+                                             int dil, hipStream_t stream);
 
 hipError_t launch_prefill_global_window_f32(const void* q, const void* k, const void* v,
                                             void* out, int T, int W, int Hq, int Hkv, int d,
                                             int mode, float scale, const int32_t* gpos, int ngl,
-                                            hipStream_t stream);
+                                            int dil, hipStream_t stream);
 
 // Decode with n_sink attention-sink slots beside the ring.  Workspace:
 // B * Hq * (decode_splits(B, Hq, W) + 1) partial records of d + 2 floats.

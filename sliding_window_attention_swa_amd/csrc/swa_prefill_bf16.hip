@@ -119,13 +119,13 @@ constexpr int kWavesPerSimd = D == 128 ? 2 : (D == 64 ? 3 : 5);
 // the global-key modes carry one more tile body; at d = 32 it needs the
 // registers of four waves per SIMD rather than five
 template <int D, int MODE>
-constexpr int kWavesFor = (MODE == 5 || MODE == 6) && D == 32 ? 4 : kWavesPerSimd<D>;
+constexpr int kWavesFor = MODE >= 5 && D == 32 ? 4 : kWavesPerSimd<D>;
 
 // MODE: 0 causal, 1 symmetric, 2 causal chunk continuing a ring cache (Tseq
 // is then the chunk length; kring/vring/pos/hkv_seq are used by MODE 2 only),
-// 3 causal dilated, 4 symmetric dilated (dil is used by MODES 3 and 4 only),
+// 3 causal dilated, 4 symmetric dilated (dil is used by MODES 3, 4, 7, 8),
 // 5 causal and 6 symmetric window plus the ngl global keys at gpos (MODES 5
-// and 6 only).
+// to 8), 7 causal and 8 symmetric dilated window plus global keys.
 template <int D, int MODE>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(kWavesFor<D, MODE>, kWavesFor<D, MODE>)))
@@ -135,10 +135,10 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
                          const __bf16* __restrict__ kring, const __bf16* __restrict__ vring,
                          const int32_t* __restrict__ pos, int hkv_seq, int dil,
                          const int32_t* __restrict__ gpos, int ngl) {
-  constexpr bool kCausal = MODE != 1 && MODE != 4 && MODE != 6;
+  constexpr bool kCausal = MODE != 1 && MODE != 4 && MODE != 6 && MODE != 8;
   constexpr bool kChunk = MODE == 2;
-  constexpr bool kDil = MODE == 3 || MODE == 4;
-  constexpr bool kGlobal = MODE == 5 || MODE == 6;
+  constexpr bool kDil = MODE == 3 || MODE == 4 || MODE == 7 || MODE == 8;
+  constexpr bool kGlobal = MODE >= 5;
   using Gm = Geo<D>;
   constexpr int ROWB = Gm::ROWB, TILEB = Gm::TILEB, KS = Gm::KS;
   constexpr int MD = Gm::MD, NLD = Gm::NLD;
@@ -182,6 +182,9 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   const __bf16* qh = q + (size_t)h * Tseq * D + (size_t)cls * D;
   const __bf16* kh = k + (size_t)kvh * Tseq * D + (size_t)cls * D;
   const __bf16* vh = v + (size_t)kvh * Tseq * D + (size_t)cls * D;
+  // global keys sit at sequence positions (outside any residue class)
+  const __bf16* kg = k + (size_t)kvh * Tseq * D;
+  const __bf16* vg = v + (size_t)kvh * Tseq * D;
   // a dilated class may be shorter than the longest one (or empty): a query
   // block past its end has nothing to do (uniform over the workgroup)
   if constexpr (kDil) {
@@ -270,13 +273,13 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
         // as the K/V tiles: written after the barrier that frees the stage)
         if (tid < kBN) lds_gp[(kt - kt0) & 1][tid] = gpos[min(t0 + tid, ngl - 1)];
         const __amdgpu_buffer_rsrc_t rk =
-            __builtin_amdgcn_make_buffer_rsrc((void*)kh, 0, T * ROWB, kBufferFlags);
+            __builtin_amdgcn_make_buffer_rsrc((void*)kg, 0, Tseq * ROWB, kBufferFlags);
         const __amdgpu_buffer_rsrc_t rv =
-            __builtin_amdgcn_make_buffer_rsrc((void*)vh, 0, T * ROWB, kBufferFlags);
+            __builtin_amdgcn_make_buffer_rsrc((void*)vg, 0, Tseq * ROWB, kBufferFlags);
 #pragma unroll
         for (int j = 0; j < NLD; ++j) {
           const int wbase = (j * kThreads + wave * 64) * 16;
-          const int gp = min(max(gpos[min(t0 + src_row[j], ngl - 1)], 0), T - 1);
+          const int gp = min(max(gpos[min(t0 + src_row[j], ngl - 1)], 0), Tseq - 1);
           const int off = gp * ROWB + src_off[j];
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass mishandles this builtin
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(Kdst + wbase), 16, off, 0, 0, 0);
@@ -598,6 +601,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   // computed.
   auto global_tile = [&](const char* Ks, const char* Vs, int t0, const int* gp_tile) __attribute__((always_inline)) {
     uint32_t okbits = 0;
+    const int rpos = kDil ? cls + dil * qi : qi;  // this lane's row as a sequence position
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       const int4 gp4 = *reinterpret_cast<const int4*>(gp_tile + 8 * g + 4 * half);
@@ -606,9 +610,15 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
       for (int e = 0; e < 4; ++e) {
         const int idx = t0 + 8 * g + 4 * half + e;
         const int gp = gpv[e];
-        const int diff = qi - gp;
-        const bool in_window = kCausal ? (diff >= 0 && diff < W) : (diff >= -hw && diff <= hw);
-        bool ok = idx < ngl && gp >= 0 && gp < T && !in_window;
+        const int diff = rpos - gp;
+        bool in_window;
+        if constexpr (kDil) {  // on the row's grid, within the window's offsets
+          const int m = diff / dil;
+          in_window = diff == m * dil && (kCausal ? (m >= 0 && m < W) : (m >= -hw && m <= hw));
+        } else {
+          in_window = kCausal ? (diff >= 0 && diff < W) : (diff >= -hw && diff <= hw);
+        }
+        bool ok = idx < ngl && gp >= 0 && gp < Tseq && !in_window;
         if (kCausal) ok = ok && diff >= 0;
         okbits |= (uint32_t)ok << (4 * g + e);
       }
@@ -944,7 +954,8 @@ hipError_t launch(const void* q, const void* k, const void* v, void* out, int T,
 // of the class's rows); the longest class has ceil(T / dil) rows.
 template <int D, int MODE>
 hipError_t launch_dilated(const void* q, const void* k, const void* v, void* out, int T, int W,
-                          int Hq, int Hkv, float scale, int dil, hipStream_t stream) {
+                          int Hq, int Hkv, float scale, int dil, hipStream_t stream,
+                          const int32_t* gpos = nullptr, int ngl = 0) {
   const int n_qtiles = ((T + dil - 1) / dil + kBM - 1) / kBM;
   const long long nwg = (long long)n_qtiles * Hq * dil;
   float c;
@@ -955,7 +966,7 @@ hipError_t launch_dilated(const void* q, const void* k, const void* v, void* out
                      static_cast<const __bf16*>(v), static_cast<__bf16*>(out), T, W, Hq, Hkv, c,
                      qsign, n_qtiles, static_cast<const __bf16*>(nullptr),
                      static_cast<const __bf16*>(nullptr), static_cast<const int32_t*>(nullptr), 1,
-                     dil, static_cast<const int32_t*>(nullptr), 0);
+                     dil, gpos, ngl);
   return hipGetLastError();
 }
 
@@ -1240,7 +1251,17 @@ hipError_t launch_prefill_chunk_bf16(const void* q, const void* k, const void* v
 hipError_t launch_prefill_global_window_bf16(const void* q, const void* k, const void* v,
                                              void* out, int T, int W, int Hq, int Hkv, int d,
                                              int mode, float scale, const int32_t* gpos, int ngl,
-                                             hipStream_t stream) {
+                                             int dil, hipStream_t stream) {
+  if (dil > 1) {  // dilated window plus global keys
+    if (mode == 0) {
+      if (d == 32) return launch_dilated<32, 7>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream, gpos, ngl);
+      if (d == 64) return launch_dilated<64, 7>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream, gpos, ngl);
+      return launch_dilated<128, 7>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream, gpos, ngl);
+    }
+    if (d == 32) return launch_dilated<32, 8>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream, gpos, ngl);
+    if (d == 64) return launch_dilated<64, 8>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream, gpos, ngl);
+    return launch_dilated<128, 8>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream, gpos, ngl);
+  }
   if (mode == 0) {
     if (d == 32) return launch_global<32, 5>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, stream);
     if (d == 64) return launch_global<64, 5>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, stream);

@@ -17,9 +17,9 @@
 // every dil-th key, j = i - m * dil for m in the plain window's offsets.
 //
 // Global tokens (MODES 5 causal, 6 symmetric; aivaro section 4.3): after its
-// window the row also takes each global key outside the window (not after
-// the row when causal).  The global rows themselves are written afterwards
-// by the full-row pass.
+// window (dilated when dil > 1) the row also takes each global key outside
+// the window (not after the row when causal).  The global rows themselves
+// are written afterwards by the full-row pass.
 
 #include "swa_device.h"
 #include "swa_launch.h"
@@ -33,7 +33,7 @@ constexpr int kLanesPerRow = 16;
 // MODE: 0 causal, 1 symmetric, 2 causal chunk continuing a ring cache
 // (kring/vring/pos/hkv_seq are used by MODE 2 only), 5 causal and 6
 // symmetric window plus the ngl global keys at gpos.  dil: key stride of a
-// dilated window in MODES 0 and 1 (1 otherwise).
+// dilated window in MODES 0, 1, 5 and 6 (1 otherwise).
 template <int D, int MODE>
 __global__ __launch_bounds__(256) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
@@ -123,7 +123,10 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
     for (int t = 0; t < ngl; ++t) {
       const int gp = gpos[t];
       const int diff = i - gp;
-      const bool in_window = kCausal ? (diff >= 0 && diff < W) : (diff >= -(W / 2) && diff <= W / 2);
+      // in the (dilated) window: on the row's grid, within the window's offsets
+      const int m = diff / dil;
+      const bool in_window = diff == m * dil &&
+                             (kCausal ? (m >= 0 && m < W) : (m >= -(W / 2) && m <= W / 2));
       if (gp < 0 || gp >= T || in_window || (kCausal && diff < 0)) continue;
       visit(kh + (size_t)gp * D, vh + (size_t)gp * D);
     }
@@ -165,7 +168,7 @@ hipError_t launch_chunk(const void* q, const void* k, const void* v, const void*
 
 template <int D, int MODE>
 hipError_t launch_global(const void* q, const void* k, const void* v, void* out, int T, int W,
-                         int Hq, int Hkv, float scale, const int32_t* gpos, int ngl,
+                         int Hq, int Hkv, float scale, const int32_t* gpos, int ngl, int dil,
                          hipStream_t stream) {
   const int n_rowblocks = (T + kRowsPerBlock - 1) / kRowsPerBlock;
   const long long nwg = (long long)n_rowblocks * Hq;
@@ -174,7 +177,7 @@ hipError_t launch_global(const void* q, const void* k, const void* v, void* out,
                      static_cast<const float*>(k), static_cast<const float*>(v),
                      static_cast<float*>(out), T, W, Hq, Hkv, scale, n_rowblocks,
                      static_cast<const float*>(nullptr), static_cast<const float*>(nullptr),
-                     static_cast<const int32_t*>(nullptr), 1, 1, gpos, ngl);
+                     static_cast<const int32_t*>(nullptr), 1, dil, gpos, ngl);
   return hipGetLastError();
 }
 
@@ -183,15 +186,15 @@ hipError_t launch_global(const void* q, const void* k, const void* v, void* out,
 hipError_t launch_prefill_global_window_f32(const void* q, const void* k, const void* v,
                                             void* out, int T, int W, int Hq, int Hkv, int d,
                                             int mode, float scale, const int32_t* gpos, int ngl,
-                                            hipStream_t stream) {
+                                            int dil, hipStream_t stream) {
   if (mode == 0) {
-    if (d == 32) return launch_global<32, 5>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, stream);
-    if (d == 64) return launch_global<64, 5>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, stream);
-    return launch_global<128, 5>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, stream);
+    if (d == 32) return launch_global<32, 5>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, dil, stream);
+    if (d == 64) return launch_global<64, 5>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, dil, stream);
+    return launch_global<128, 5>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, dil, stream);
   }
-  if (d == 32) return launch_global<32, 6>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, stream);
-  if (d == 64) return launch_global<64, 6>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, stream);
-  return launch_global<128, 6>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, stream);
+  if (d == 32) return launch_global<32, 6>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, dil, stream);
+  if (d == 64) return launch_global<64, 6>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, dil, stream);
+  return launch_global<128, 6>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, dil, stream);
 }
 
 hipError_t launch_prefill_chunk_f32(const void* q, const void* k, const void* v,

@@ -45,6 +45,10 @@ WORKLOADS = {
     8: dict(name="Longformer symmetric prefill + 8 global tokens", kind="prefill", B=4, Hq=12,
             Hkv=12, T=4096, W=512, d=64, dtype=BF16, mode=SYMMETRIC,
             global_pos=[0, 1, 2, 3, 4, 5, 6, 7]),
+    # both together, as Longformer combines them (aivaro sections 4.2, 4.3)
+    9: dict(name="Longformer dilated symmetric prefill + 8 global tokens", kind="prefill", B=4,
+            Hq=12, Hkv=12, T=4096, W=512, d=64, dtype=BF16, mode=SYMMETRIC, dilation=2,
+            global_pos=[0, 1, 2, 3, 4, 5, 6, 7]),
     # serving-style chunked prefill: 4 sequences, each continuing with a
     # 2048-token chunk after at least W tokens are already in its ring
     6: dict(name="Mistral-7B chunked prefill", kind="chunk", B=4, Hq=32, Hkv=8, n=2048,

@@ -38,6 +38,7 @@ def test_header_declares_the_entry_points():
         "swa_prefill", "swa_cache_append", "swa_decode", "swa_decode_workspace_bytes",
         "swa_status_string", "swa_cache_append_chunk", "swa_prefill_chunk",
         "swa_prefill_dilated", "swa_prefill_global", "swa_prefill_global_workspace_bytes",
+        "swa_prefill_dilated_global",
         "swa_decode_sinks", "swa_decode_sinks_workspace_bytes", "swa_calib_mfma_bf16",
         "swa_calib_stream_read"])
 
@@ -111,6 +112,29 @@ def test_global_workspace_bytes(lib):
         n = f(T, Hq, G, d)
         assert n > 0 and n % (4 * (d + 2) * G * Hq) == 0
         assert 1 <= n // (4 * (d + 2) * G * Hq) <= max(1, (T + 63) // 64)
+
+
+def dilated_global(lib, q=P, k=P, v=P, out=P, T=64, W=8, Hq=4, Hkv=2, d=64, mode=1, scale=0.125,
+                   dil=2, gpos=P, G=3, ws=P, ws_bytes=1 << 30, dtype=1):
+    return lib.swa_prefill_dilated_global(q, k, v, out, T, W, Hq, Hkv, d, mode, scale, dil, gpos,
+                                          G, ws, ws_bytes, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(gpos=None), INVALID), (dict(gpos=MIS), INVALID),
+    (dict(G=-1), INVALID), (dict(T=0), INVALID), (dict(Hq=6, Hkv=4), INVALID),
+    (dict(dil=0), INVALID), (dict(dil=-2), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(d=40), UNSUPPORTED), (dict(mode=2), UNSUPPORTED), (dict(dtype=3), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(ws=MIS), WORKSPACE), (dict(ws_bytes=16), WORKSPACE),
+    (dict(dil=2**20, d=128), UNSUPPORTED),  # a tile's rows beyond 32-bit byte offsets
+    (dict(T=2**24, d=128), UNSUPPORTED),
+    # G = 0 is swa_prefill_dilated (its checks), dilation 1 is swa_prefill_global
+    (dict(G=0, gpos=None, ws=None, ws_bytes=0, dil=0), INVALID),
+    (dict(G=0, gpos=None, ws=None, ws_bytes=0, d=48), UNSUPPORTED),
+    (dict(dil=1, ws=None), WORKSPACE), (dict(dil=1, mode=5), UNSUPPORTED),
+])
+def test_prefill_dilated_global_rejects(lib, kw, status):
+    assert dilated_global(lib, **kw) == status
 
 
 def test_prefill_global_without_globals_is_prefill_validation(lib):

@@ -36,6 +36,15 @@ def test_global_pairs_are_the_mask_count(T, W, mode, gpos):
     assert bench.global_pairs(T, W, mode, gpos) == int(oracle.global_mask(T, W, mode, gpos).sum())
 
 
+@pytest.mark.parametrize("T,W,mode,gpos,dil", [(50, 7, 1, [0], 2), (50, 7, 0, [0, 3, 49], 3),
+                                               (61, 9, 1, list(range(0, 61, 5)), 4),
+                                               (40, 100, 0, [10, 20], 2), (33, 1, 0, [32], 5),
+                                               (33, 4, 1, [], 3), (8, 2, 1, [3], 2)])
+def test_dilated_global_pairs_are_the_mask_count(T, W, mode, gpos, dil):
+    assert bench.global_pairs(T, W, mode, gpos, dil) == int(
+        oracle.global_mask(T, W, mode, gpos, dil).sum())
+
+
 def test_prefill_and_decode_work_of_the_workloads():
     flops, bytes_ = bench.prefill_work()
     assert flops == 962106228736  # 4 * 128 * 58,722,304 pairs * 32 heads
