@@ -3,6 +3,8 @@ fp64 oracle.
 
 * A 2^20-token causal prefill (W=4096, d=64): sampled rows at the start, on
   tile and block boundaries and at the very end.
+* 2^20 tokens with global tokens: global rows over every key (8192 key
+  splits merged) and the rows beside them.
 * Positions near 2^31 - 1: ring append, decode, multi-token append and a
   chunked prefill whose chunk ends at position 2^31 - 2; decode with sinks far
   into the sequence.
@@ -45,6 +47,26 @@ def test_million_token_prefill_sampled(swa):
         ref = oracle.attention_rows(q.values, k.values, v.values, W, 0, 1 / math.sqrt(d), 0, h, rows)
         got = out[0, h, torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
         assert_parity(got, ref, "bf16", "T=2^20 head %d" % h)
+
+
+def test_million_token_global_rows(swa):
+    """2^20 tokens, symmetric W=512, d=64, global tokens at the start, the
+    middle and the end: each global row attends to all 2^20 keys (8192 key
+    splits of the matrix-core rows pass, merged), and rows next to them see
+    their window plus the global keys."""
+    T, W, d = 2**20, 512, 64
+    gpos = np.array([0, 1000, 2**19, T - 1], dtype=np.int32)
+    print("global rows T=%d W=%d d=%d G=%d" % (T, W, d, len(gpos)), flush=True)
+    q, k, v = si.prefill_inputs(9, B=1, Hq=2, Hkv=1, T=T, d=d)
+    out = swa.prefill_global(to_device(q), to_device(k), to_device(v), W,
+                             torch.from_numpy(gpos).cuda(), mode=si.SYMMETRIC)
+    torch.cuda.synchronize()
+    rows = np.array(list(gpos) + [1, 999, 1001, 2**19 + 300, T - 2], dtype=np.int64)
+    for h in range(2):
+        ref = oracle.attention_global_rows(q.values, k.values, v.values, W, si.SYMMETRIC,
+                                           1 / math.sqrt(d), gpos, 0, h, rows)
+        got = out[0, h, torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+        assert_parity(got, ref, "bf16", "T=2^20 global rows head %d" % h)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
