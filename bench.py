@@ -148,7 +148,7 @@ def summarize_pmc(paths):
     return 0
 
 
-N_XCD, N_SIMD = 8, 1024  # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+N_XCD, N_CU, N_SIMD = 8, 256, 1024  # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
 MFMA_FLOP_PER_SIMD_CYCLE = 1024  # v_mfma_f32_32x32x16_bf16: 32768 FLOP in 32 cycles
 
 
@@ -206,6 +206,12 @@ def summarize_counters(paths):
         if g("SQ_LDS_BANK_CONFLICT") is not None:
             print("  LDS bank-conflict cycles: %.3g (%.2f%% of SIMD cycles)"
                   % (g("SQ_LDS_BANK_CONFLICT"), 100.0 * g("SQ_LDS_BANK_CONFLICT") / (cycles * N_SIMD)))
+        if g("SQ_LDS_IDX_ACTIVE") is not None:
+            print("  LDS busy (indexed access): %.1f%% of CU cycles"
+                  % (100.0 * g("SQ_LDS_IDX_ACTIVE") / (cycles * N_CU)))
+        if g("SQ_INSTS_LDS_LOAD_BANDWIDTH") is not None:
+            nbytes = 64.0 * g("SQ_INSTS_LDS_LOAD_BANDWIDTH")
+            print("  LDS bytes read %.4g = %.1f B per CU cycle" % (nbytes, nbytes / (cycles * N_CU)))
     return 0
 
 
