@@ -49,7 +49,8 @@ Readings of points the pages leave open (each also listed in the design doc):
     number inside the undilated window;
   * global tokens (aivaro section 4.3): added to the window as whole rows and
     columns of the mask; in the causal mode the added pairs keep j <= i, so
-    global tokens at the first positions are attention sinks;
+    global tokens at the first positions are attention sinks; together with
+    a dilation the window part is the dilated one (the union of the masks);
   * decode with sinks: the first S positions are kept in sink slots beside
     the ring and the query sees them together with its window, each
     position once.
