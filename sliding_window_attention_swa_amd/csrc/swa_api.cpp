@@ -109,8 +109,7 @@ static int prefill_global_impl(const void* q, const void* k, const void* v, void
     e = swa::launch_global_combine(ws, out, global_pos, G, T, Hq, Hkv, d,
                                    swa::global_rows_mfma_splits(T), dtype, s);
   } else {
-    e = swa::launch_global_rows(q, k, v, global_pos, out, G, T, Hq, Hkv, d, mode, scale, dtype, ws,
-                                s);
+    e = swa::launch_global_rows_f32(q, k, v, global_pos, out, G, T, Hq, Hkv, d, mode, scale, ws, s);
   }
   return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH;
 }

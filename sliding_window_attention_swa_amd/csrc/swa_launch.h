@@ -57,15 +57,15 @@ hipError_t launch_global_rows_mfma_bf16(const void* q, const void* k, const void
 hipError_t launch_global_combine(float* workspace, void* out, const int32_t* gpos, int ngl, int T,
                                  int Hq, int Hkv, int d, int S, int dtype, hipStream_t stream);
 
-// Number of key chunks the global-row pass splits each row into.
+// Number of key chunks the fp32 global-row pass splits each row into.
 int global_splits(int G, int Hq, int T);
 
-// The rows of the global tokens: each attends to every key (every earlier
-// key when causal).  Workspace: G * Hq * global_splits(G, Hq, T) partial
-// records of d + 2 floats.
-hipError_t launch_global_rows(const void* q, const void* k, const void* v, const int32_t* gpos,
-                              void* out, int ngl, int T, int Hq, int Hkv, int d, int mode,
-                              float scale, int dtype, float* workspace, hipStream_t stream);
+// The rows of the global tokens in fp32: each attends to every key (every
+// earlier key when causal).  Workspace: G * Hq * global_splits(G, Hq, T)
+// partial records of d + 2 floats.
+hipError_t launch_global_rows_f32(const void* q, const void* k, const void* v, const int32_t* gpos,
+                                  void* out, int ngl, int T, int Hq, int Hkv, int d, int mode,
+                                  float scale, float* workspace, hipStream_t stream);
 
 // Chunk of n tokens per sequence against its ring plus itself (causal).
 hipError_t launch_prefill_chunk_bf16(const void* q, const void* k, const void* v,

@@ -970,7 +970,8 @@ hipError_t launch_dilated(const void* q, const void* k, const void* v, void* out
   return hipGetLastError();
 }
 
-// Window plus global keys (the global rows are written by a later pass).
+// Window plus global keys (the global rows are written by global_rows_kernel
+// and the merge).
 template <int D, int MODE>
 hipError_t launch_global(const void* q, const void* k, const void* v, void* out, int T, int W,
                          int Hq, int Hkv, float scale, const int32_t* gpos, int ngl,

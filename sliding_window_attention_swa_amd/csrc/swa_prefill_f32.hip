@@ -19,7 +19,7 @@
 // Global tokens (MODES 5 causal, 6 symmetric; aivaro section 4.3): after its
 // window (dilated when dil > 1) the row also takes each global key outside
 // the window (not after the row when causal).  The global rows themselves
-// are written afterwards by the full-row pass.
+// are written afterwards by the split-K pass of swa_ring.hip.
 
 #include "swa_device.h"
 #include "swa_launch.h"

@@ -25,13 +25,15 @@
 //     through LDS; a small second kernel merges the splits with the usual
 //     log-sum-exp rule and writes the output.
 //
-// The same two kernels also write the rows of global tokens (aivaro answer
-// 629, section 4.3: a global token attends to every token): with GR != 0 a
-// workgroup takes NQ (global row t, query head) pairs of one KV head, so
-// they share every K/V read; the query of a pair is row gpos[t] of the
-// prefill queries, and the linear K/V of the sequence serve as a ring of T
-// slots of which gpos[t] + 1 (causal, GR = 1) or all T (symmetric, GR = 2)
-// are valid.
+// In fp32 the same two kernels also write the rows of global tokens (aivaro
+// answer 629, section 4.3: a global token attends to every token): with
+// GR != 0 a workgroup takes NQ (global row t, query head) pairs of one KV
+// head, so they share every K/V read; the query of a pair is row gpos[t] of
+// the prefill queries, and the linear K/V of the sequence serve as a ring of
+// T slots of which gpos[t] + 1 (causal, GR = 1) or all T (symmetric, GR = 2)
+// are valid.  In bf16 those rows are computed on the matrix cores
+// (swa_prefill_bf16.hip) in the same partial layout, and the merge kernel's
+// GR = 1 instantiation writes them (launch_global_combine).
 
 #include "swa_device.h"
 #include "swa_launch.h"
@@ -677,15 +679,10 @@ hipError_t launch_decode(const void* q, const void* k_ring, const void* v_ring,
   return launch_decode_e<float, 0>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, d, scale, workspace, stream);
 }
 
-hipError_t launch_global_rows(const void* q, const void* k, const void* v, const int32_t* gpos,
-                              void* out, int ngl, int T, int Hq, int Hkv, int d, int mode,
-                              float scale, int dtype, float* workspace, hipStream_t stream) {
+hipError_t launch_global_rows_f32(const void* q, const void* k, const void* v, const int32_t* gpos,
+                                  void* out, int ngl, int T, int Hq, int Hkv, int d, int mode,
+                                  float scale, float* workspace, hipStream_t stream) {
   // ngl "sequences" (the global rows), each against the whole K/V as a ring of T slots
-  if (dtype == 1) {
-    if (mode == 0)
-      return launch_decode_e<__bf16, 1>(q, k, v, gpos, out, ngl, Hq, Hkv, T, d, scale, workspace, stream);
-    return launch_decode_e<__bf16, 2>(q, k, v, gpos, out, ngl, Hq, Hkv, T, d, scale, workspace, stream);
-  }
   if (mode == 0)
     return launch_decode_e<float, 1>(q, k, v, gpos, out, ngl, Hq, Hkv, T, d, scale, workspace, stream);
   return launch_decode_e<float, 2>(q, k, v, gpos, out, ngl, Hq, Hkv, T, d, scale, workspace, stream);
