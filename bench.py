@@ -148,6 +148,63 @@ def summarize_pmc(paths):
     return 0
 
 
+# the HBM-bound prefill configurations whose traffic --pmc-small measures,
+# in dispatch order, with the kernel each one runs
+SMALL_TRAFFIC = ((2, "prefill_short_kernel"), (5, "prefill_bf16_kernel"))
+
+
+def pmc_small():
+    """Counter workload for the HBM-bound prefill configurations: the
+    calibration copy, then TinyMistral and Longformer once each, every one
+    after a 1 GiB write that evicts the L2s and the Infinity Cache."""
+    import torch
+    import sliding_window_attention_swa_amd as swa
+    dev = torch.device("cuda:0")
+    swa.load()
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    for wl, _ in SMALL_TRAFFIC:
+        c = si.WORKLOADS[wl]
+        q, k, v = (si.to_torch(t, dev) for t in si.prefill_inputs(wl))
+        out = torch.empty_like(q)
+        flush.fill_(1.0)
+        torch.cuda.synchronize()
+        swa.prefill(q, k, v, c["W"], mode=c["mode"], out=out)
+        torch.cuda.synchronize()
+        del q, k, v, out
+    print("pmc small workload done", flush=True)
+    return 0
+
+
+def summarize_pmc_small(paths):
+    """HBM bytes of each --pmc-small configuration (counters scaled by the
+    calibration copy) against its algorithmic Q + K + V read and O write."""
+    import csv
+    per, copy = {}, {}
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            name, ctr, val = r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
+            if "copyBuffer" in name:
+                copy[ctr] = max(copy.get(ctr, 0.0), val)
+            for wl, pat in SMALL_TRAFFIC:
+                if pat in name:
+                    per[(wl, ctr)] = per.get((wl, ctr), 0.0) + val
+    for wl, _ in SMALL_TRAFFIC:
+        c = si.WORKLOADS[wl]
+        rd = 2 * c["T"] * c["d"] * c["B"] * (c["Hq"] + 2 * c["Hkv"])
+        wr = 2 * c["T"] * c["d"] * c["B"] * c["Hq"]
+        got = {}
+        for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+            if ctr in copy and (wl, ctr) in per:
+                got[ctr] = per[(wl, ctr)] * COPY_BYTES / copy[ctr]
+        print("%s: read %s bytes (algorithmic %d), written %s bytes (algorithmic %d)" % (
+            c["name"], "%.0f" % got["FETCH_SIZE"] if "FETCH_SIZE" in got else "-", rd,
+            "%.0f" % got["WRITE_SIZE"] if "WRITE_SIZE" in got else "-", wr))
+    return 0
+
+
 N_XCD, N_CU, N_SIMD = 8, 256, 1024  # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
 MFMA_FLOP_PER_SIMD_CYCLE = 1024  # v_mfma_f32_32x32x16_bf16: 32768 FLOP in 32 cycles
 
@@ -502,6 +559,12 @@ def main():
     ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
                     help="turn rocprofv3 MFMA / instruction counter CSVs of a --pmc-workload run "
                          "into utilisation figures")
+    ap.add_argument("--pmc-small", action="store_true",
+                    help="instead of the benchmark line: the counter workload of the HBM-bound "
+                         "prefill configurations (run under rocprofv3 --pmc)")
+    ap.add_argument("--summarize-pmc-small", nargs="+", metavar="CSV",
+                    help="HBM bytes of the --pmc-small configurations from FETCH_SIZE / "
+                         "WRITE_SIZE counter CSVs")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measurement of the box's sustained matrix and read rates "
                          "after the timed steps")
@@ -516,6 +579,10 @@ def main():
         return summarize_pmc(args.summarize_pmc)
     if args.summarize_counters:
         return summarize_counters(args.summarize_counters)
+    if args.summarize_pmc_small:
+        return summarize_pmc_small(args.summarize_pmc_small)
+    if args.pmc_small:
+        return pmc_small()
     if args.all_configs or args.peaks:
         return all_configs(max(args.steps, 20), peaks_only=args.peaks)
 

@@ -109,3 +109,27 @@ def test_counter_summary_arithmetic(tmp_path, capsys):
     assert "clock 1800 MHz" in out
     assert "MFMA busy: 50.0%" in out
     assert "1.000 x the in-window FLOPs" in out
+
+
+def test_small_traffic_summary(tmp_path, capsys):
+    """Counters that read exactly the algorithmic bytes (with FETCH_SIZE
+    reading half the bytes, as the calibration copy shows) are reported as
+    such."""
+    rows = [("__amd_rocclr_copyBuffer", "FETCH_SIZE", bench.COPY_BYTES / 2048),
+            ("__amd_rocclr_copyBuffer", "WRITE_SIZE", bench.COPY_BYTES / 1024)]
+    for wl, pat in bench.SMALL_TRAFFIC:
+        c = si.WORKLOADS[wl]
+        rd = 2 * c["T"] * c["d"] * c["B"] * (c["Hq"] + 2 * c["Hkv"])
+        wr = 2 * c["T"] * c["d"] * c["B"] * c["Hq"]
+        rows += [("swa::%s<...>" % pat, "FETCH_SIZE", rd / 2048), ("swa::%s<...>" % pat, "WRITE_SIZE", wr / 1024)]
+    f = tmp_path / "c.csv"
+    with open(f, "w") as fh:
+        fh.write('"Kernel_Name","Counter_Name","Counter_Value"\n')
+        for n, ctr, v in rows:
+            fh.write('"%s","%s",%r\n' % (n, ctr, v))
+    assert bench.summarize_pmc_small([str(f)]) == 0
+    out = capsys.readouterr().out.splitlines()
+    assert len(out) == len(bench.SMALL_TRAFFIC)
+    for line in out:
+        nums = [int(x) for x in line.replace("(", " ").replace(")", " ").replace(",", " ").split() if x.isdigit()]
+        assert nums[0] == nums[1] and nums[2] == nums[3], line
