@@ -730,14 +730,24 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
 // operand reads and LDS swizzle as the tiled kernel above.
 template <int MODE>
 constexpr int kShortOff = MODE == 0 ? 32 : 16;
+// query heads of a KV group per short-window workgroup (at most): two
+// measured best (TinyMistral 22.3 -> 20.2 us warm, 37 -> 33 us from HBM; four:
+// 20.6 / 32.5 us)
+#ifndef SWA_SHORT_GROUP
+#define SWA_SHORT_GROUP 2
+#endif
 
 bool short_window(int W, int mode) { return mode == 0 ? W <= 33 : (W >> 1) <= 16; }
 
 // The occupancy target keeps the matrix results in ordinary registers (with
 // one wave per workgroup the compiler otherwise keeps them in accumulation
 // registers and copies them out).
-template <int D, int MODE>
-__global__ __launch_bounds__(64)
+//
+// NW > 1 (grouped query heads): a workgroup is NW waves, the same 32 rows of
+// NW query heads of one KV group; the key block is loaded once into LDS, each
+// wave issuing 1/NW of the direct loads, and one barrier makes it visible.
+template <int D, int MODE, int NW = 1>
+__global__ __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>)))
 void prefill_short_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
@@ -746,7 +756,8 @@ void prefill_short_kernel(
   using Gm = Geo<D>;
   constexpr int ROWB = Gm::ROWB, KS = Gm::KS, MD = Gm::MD;
   constexpr int BLOCKB = 64 * ROWB;      // 64 key rows
-  constexpr int NL = BLOCKB / (64 * 16);  // direct loads per lane per block
+  constexpr int NL = BLOCKB / (64 * 16);  // direct loads per lane per block (one wave)
+  static_assert(NL % NW == 0, "the block's loads split evenly over the waves");
   __shared__ __attribute__((aligned(1024))) char lds_k[BLOCKB];
   __shared__ __attribute__((aligned(1024))) char lds_v[BLOCKB];
 
@@ -754,13 +765,15 @@ void prefill_short_kernel(
   int id = blockIdx.x;
   const int nwg = gridDim.x;
   if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
-  const int hg = id % G;
-  const int rest = id / G;
+  const int ng = G / NW;  // workgroups per (KV head, row block)
+  const int hg = (id % ng) * NW + (NW > 1 ? (int)(threadIdx.x >> 6) : 0);
+  const int rest = id / ng;
   const int wt = rest % n_wtiles;
   const int kvh = rest / n_wtiles;
   const int h = kvh * G + hg;
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = NW > 1 ? (int)(threadIdx.x >> 6) : 0;
   const int half = lane >> 5;
   const int qw0 = wt * 32;
   const int qi = qw0 + (lane & 31);
@@ -779,7 +792,8 @@ void prefill_short_kernel(
     const __amdgpu_buffer_rsrc_t rv =
         __builtin_amdgcn_make_buffer_rsrc((void*)vh, 0, T * ROWB, kBufferFlags);
 #pragma unroll
-    for (int j = 0; j < NL; ++j) {
+    for (int jj = 0; jj < NL / NW; ++jj) {
+      const int j = wave * (NL / NW) + jj;
       const int o = (64 * j + lane) * 16;
       const int row = o / ROWB;
       const int src = min(max(kb0 + row, 0), T - 1);
@@ -804,7 +818,8 @@ void prefill_short_kernel(
     r.w ^= qsign;
     qf[ks] = __builtin_bit_cast(bf16x8, r);
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the block is in LDS (one wave: no barrier)
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's part of the block is in LDS
+  if constexpr (NW > 1) __syncthreads();  // and every other wave's part
 
   // ---- S^T = K Q^T for the 64 keys (two 32-key blocks), masked
   const int kr = lane & 31;
@@ -911,11 +926,27 @@ template <int D, int MODE>
 hipError_t launch_short(const void* q, const void* k, const void* v, void* out, int T, int W,
                         int Hq, int Hkv, float c, uint32_t qsign, hipStream_t stream) {
   const int n_wtiles = (T + 31) / 32;
-  const long long nwg = (long long)n_wtiles * Hq;
-  hipLaunchKernelGGL((prefill_short_kernel<D, MODE>), dim3((unsigned)nwg), dim3(64), 0, stream,
-                     static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
-                     static_cast<const __bf16*>(v), static_cast<__bf16*>(out), T, W, Hq, Hkv, c,
-                     qsign, n_wtiles);
+  const int G = Hq / Hkv;
+#define SWA_SHORT(NW)                                                                              \
+  hipLaunchKernelGGL((prefill_short_kernel<D, MODE, NW>), dim3((unsigned)((long long)n_wtiles * (Hq / NW))), \
+                     dim3(64 * NW), 0, stream, static_cast<const __bf16*>(q),                     \
+                     static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),                 \
+                     static_cast<__bf16*>(out), T, W, Hq, Hkv, c, qsign, n_wtiles)
+  // query heads of a KV group share the key block where the group allows
+  if constexpr (SWA_SHORT_GROUP >= 4) {
+    if (G % 4 == 0) {
+      SWA_SHORT(4);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (SWA_SHORT_GROUP >= 2) {
+    if (G % 2 == 0) {
+      SWA_SHORT(2);
+      return hipGetLastError();
+    }
+  }
+  SWA_SHORT(1);
+#undef SWA_SHORT
   return hipGetLastError();
 }
 

@@ -79,6 +79,13 @@ SMALL = [
     (1, 97, 33, 1, 2, 2, 32),
     (1, 300, 34, 1, 2, 1, 128),
     (1, 300, 35, 1, 4, 2, 64),
+    # short windows with the query heads of a KV group sharing the key block:
+    # groups of 4 (one workgroup), 8 (two), 3 (one head per workgroup), 2
+    (0, 300, 20, 1, 8, 2, 64),
+    (1, 257, 20, 2, 8, 1, 128),
+    (0, 100, 33, 1, 6, 2, 32),
+    (1, 65, 10, 1, 4, 2, 128),
+    (0, 31, 5, 1, 16, 4, 64),
 ]
 
 
