@@ -94,6 +94,22 @@ def test_positions_outside_the_sequence_are_ignored(swa):
     assert_parity(to_f64(out), ref, "bf16", "global with out-of-range positions")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_every_token_global_is_full_attention(swa, dtype, mode):
+    """All T positions global: every row is a global row, i.e. full attention
+    (causal or bidirectional), whatever the window."""
+    T, W, d = 200, 8, 64
+    q, k, v = si.prefill_inputs(8, B=1, Hq=4, Hkv=2, T=T, d=d, dtype=dtype)
+    gpos = np.arange(T, dtype=np.int32)
+    out = swa.prefill_global(to_device(q), to_device(k), to_device(v), W,
+                             torch.from_numpy(gpos).cuda(), mode=mode)
+    torch.cuda.synchronize()
+    ref = oracle.attention_banded(q.values, k.values, v.values, T if mode == 0 else 2 * T, mode,
+                                  1 / math.sqrt(d))
+    assert_parity(to_f64(out), ref, dtype, "every token global")
+
+
 def test_no_global_is_prefill_bit_for_bit(swa):
     q, k, v = (to_device(t) for t in si.prefill_inputs(8, B=1, Hq=4, Hkv=2, T=333, d=64))
     a = swa.prefill(q, k, v, 40, mode=1)
