@@ -21,6 +21,8 @@ Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
                                         flushed; not the benchmark line)
        python bench.py --peaks         (the matrix-core and streaming-read rates the box
                                         sustains, from the library's calibration kernels)
+       python bench.py --cpu-oracle    (the fp64 oracle's speed per configuration on the
+                                        host cores, all threads and one)
 """
 
 import argparse
@@ -310,6 +312,43 @@ def cpu_baseline(pos_np, q_dec, kr, vr, qkv_pre):
     }
 
 
+def cpu_oracle_configs():
+    """The fp64 oracle's own speed on the host cores, per configuration: the
+    banded form on a bounded sample of heads (every row of each) for the
+    prefill configurations and a sample of sequences for the decode, with all
+    BLAS threads and with one.  One JSON line per (configuration, threads)."""
+    import oracle
+    from threadpoolctl import threadpool_info, threadpool_limits
+    all_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    samples = []
+    for wl, heads in ((2, 32), (5, 8), (3, 2)):
+        c = si.WORKLOADS[wl]
+        q, k, v = si.prefill_inputs(wl)
+        hs = [(b, h) for b in range(c["B"]) for h in range(c["Hq"])][:heads]
+        flops = 4 * c["d"] * band_pairs(c["T"], c["W"], c["mode"]) * len(hs)
+        fn = (lambda q=q, k=k, v=v, c=c, hs=hs: oracle.attention_banded(
+            q.values, k.values, v.values, c["W"], c["mode"], 1 / math.sqrt(c["d"]), heads=hs))
+        samples.append((c["name"], "%d of %d heads, every row" % (len(hs), c["B"] * c["Hq"]),
+                        flops, fn))
+    c4 = si.WORKLOADS[4]
+    qd, kr, vr, pos = si.decode_inputs(4)
+    nb = 8
+    rows = int(np.minimum(pos[:nb].astype(np.int64) + 1, c4["W"]).sum())
+    samples.append((c4["name"], "%d of %d sequences" % (nb, c4["B"]), 4 * c4["d"] * rows * c4["Hq"],
+                    lambda: oracle.decode(qd.values[:nb], kr.values[:nb], vr.values[:nb], pos[:nb],
+                                          1 / math.sqrt(c4["d"]))))
+    for name, what, flops, fn in samples:
+        for threads in (all_threads, 1):
+            with threadpool_limits(limits=threads):
+                t0 = time.perf_counter()
+                fn()
+                secs = time.perf_counter() - t0
+            print(json.dumps({"config": name, "kind": "oracle", "sample": what, "threads": threads,
+                              "seconds": round(secs, 3), "gflops": round(flops / secs / 1e9, 2)}),
+                  flush=True)
+    return 0
+
+
 def band_pairs(T, W, mode, dilation=1):
     """(query, key) pairs inside the windows of one head, either mode; with a
     dilation, row i has the window's offsets m with i - m * dilation in
@@ -559,6 +598,9 @@ def main():
     ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
                     help="turn rocprofv3 MFMA / instruction counter CSVs of a --pmc-workload run "
                          "into utilisation figures")
+    ap.add_argument("--cpu-oracle", action="store_true",
+                    help="instead of the benchmark line: the fp64 oracle's speed per "
+                         "configuration on the host cores, all threads and one")
     ap.add_argument("--pmc-small", action="store_true",
                     help="instead of the benchmark line: the counter workload of the HBM-bound "
                          "prefill configurations (run under rocprofv3 --pmc)")
@@ -583,6 +625,8 @@ def main():
         return summarize_pmc_small(args.summarize_pmc_small)
     if args.pmc_small:
         return pmc_small()
+    if args.cpu_oracle:
+        return cpu_oracle_configs()
     if args.all_configs or args.peaks:
         return all_configs(max(args.steps, 20), peaks_only=args.peaks)
 
