@@ -431,7 +431,7 @@ def all_configs(reps, peaks_only=False):
         # every repetition is enqueued before the one host synchronisation, so
         # the device never idles between them; events bracket the kernel alone
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(reps + 3)]
+              for _ in range(reps + 10)]
         for r, (a, b) in enumerate(ev):
             if flushed:
                 flush.fill_(float(r))
@@ -439,7 +439,7 @@ def all_configs(reps, peaks_only=False):
             fn()
             b.record()
         torch.cuda.synchronize()
-        return float(np.median([a.elapsed_time(b) for a, b in ev[3:]]))
+        return float(np.median([a.elapsed_time(b) for a, b in ev[10:]]))
 
     peaks = measured_peaks(swa, dev, timed)
     print(json.dumps(peaks), flush=True)
@@ -628,7 +628,7 @@ def main():
     if args.cpu_oracle:
         return cpu_oracle_configs()
     if args.all_configs or args.peaks:
-        return all_configs(max(args.steps, 20), peaks_only=args.peaks)
+        return all_configs(max(args.steps, 50), peaks_only=args.peaks)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
