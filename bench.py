@@ -91,9 +91,15 @@ def read_traffic(prefix, source):
 
 
 def source_hash(name):
+    """SHA-256 of a kernel source's code: comments and whitespace removed, so
+    that an edit of the comments alone keeps the measured traffic valid."""
     import hashlib
+    import re
     p = os.path.join(ROOT, "sliding_window_attention_swa_amd", "csrc", name)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()
+    text = open(p, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
 
 
 PREFILL_SOURCE = "swa_prefill_bf16.hip"

@@ -1052,6 +1052,8 @@ hipError_t launch_chunk(const void* q, const void* k, const void* v, const void*
 // follow the tiled kernel.  The unnormalised partial (acc, max in log2 units,
 // sum) of each pair goes to the split-K workspace, merged afterwards by the
 // decode kernels' merge pass.
+// keys per split: 128 measured best at Longformer shapes (11.5 us; 256: 12.3,
+// 512: 15.2 us, the merge then costing less)
 #ifndef SWA_GROW_KEYS
 #define SWA_GROW_KEYS 128
 #endif

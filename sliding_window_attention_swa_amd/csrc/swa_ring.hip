@@ -45,6 +45,15 @@ constexpr float kRescaleThreshold = 8.0f;
 constexpr float kNegBig = -1.0e30f;
 constexpr int kDecodeThreads = 256;
 constexpr int kDecodeWaves = kDecodeThreads / 64;
+// Tuning constants (the defaults are the measured choices):
+//   SWA_DECODE_UNROLL   K and V rows in flight per lane
+//   SWA_DECODE_ITEMS    (row, split) items a decode launch aims at before it
+//                       stops splitting the ring
+//   SWA_GLOBAL_ITEMS    the same for the fp32 global-row pass
+//   SWA_GLOBAL_NQ       (global row, head) pairs per workgroup of that pass
+//   SWA_COMBINE_UNROLL  splits in flight in the merge of many-split rows
+//   SWA_GLOBAL_NT       non-temporal loads in the global-row pass (off: the
+//                       window pass has just read those rows)
 #ifndef SWA_DECODE_UNROLL
 #define SWA_DECODE_UNROLL 8
 #endif

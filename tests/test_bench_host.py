@@ -133,3 +133,16 @@ def test_small_traffic_summary(tmp_path, capsys):
     for line in out:
         nums = [int(x) for x in line.replace("(", " ").replace(")", " ").replace(",", " ").split() if x.isdigit()]
         assert nums[0] == nums[1] and nums[2] == nums[3], line
+
+
+def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
+    d = tmp_path / "sliding_window_attention_swa_amd" / "csrc"
+    d.mkdir(parents=True)
+    f = d / "k.hip"
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    f.write_text("int a = 1;  // one\n/* block\n comment */ int b = a + 2;\n")
+    h0 = bench.source_hash("k.hip")
+    f.write_text("int a = 1;  // another comment\n\nint b = a + 2;  /* x */\n")
+    assert bench.source_hash("k.hip") == h0
+    f.write_text("int a = 1;\nint b = a + 3;\n")
+    assert bench.source_hash("k.hip") != h0
