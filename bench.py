@@ -164,7 +164,7 @@ SMALL_TRAFFIC = ((2, "prefill_short_kernel"), (5, "prefill_bf16_kernel"))
 def pmc_small():
     """Counter workload for the HBM-bound prefill configurations: the
     calibration copy, then TinyMistral and Longformer once each, every one
-    after a 1 GiB write that evicts the L2s and the Infinity Cache."""
+    after a 1 GiB read that evicts the L2s and the Infinity Cache."""
     import torch
     import sliding_window_attention_swa_amd as swa
     dev = torch.device("cuda:0")
@@ -172,12 +172,13 @@ def pmc_small():
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     dst.copy_(src)
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)  # read, not written: no dirty lines
+    flush_max = torch.empty((), dtype=torch.int32, device=dev)
     for wl, _ in SMALL_TRAFFIC:
         c = si.WORKLOADS[wl]
         q, k, v = (si.to_torch(t, dev) for t in si.prefill_inputs(wl))
         out = torch.empty_like(q)
-        flush.fill_(1.0)
+        torch.amax(flush, dim=0, out=flush_max)
         torch.cuda.synchronize()
         swa.prefill(q, k, v, c["W"], mode=c["mode"], out=out)
         torch.cuda.synchronize()
@@ -422,7 +423,7 @@ def measured_peaks(swa, dev, timed):
 
 def all_configs(reps, peaks_only=False):
     """Every configuration's kernel time, cache-warm (same inputs every
-    repetition) and flushed (a 1 GiB write between repetitions evicts the L2s
+    repetition) and flushed (a 1 GiB read between repetitions evicts the L2s
     and the Infinity Cache), against its binding roofline.  One JSON line per
     configuration."""
     import torch
@@ -431,7 +432,11 @@ def all_configs(reps, peaks_only=False):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     swa.load()
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    # the flush reads 1 GiB with ordinary (cache-allocating) loads: it evicts
+    # the L2s and the Infinity Cache without leaving dirty lines whose
+    # write-back the timed kernel would pay for
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)  # 1 GiB
+    flush_max = torch.empty((), dtype=torch.int32, device=dev)
 
     def timed(fn, flushed):
         # every repetition is enqueued before the one host synchronisation, so
@@ -440,7 +445,7 @@ def all_configs(reps, peaks_only=False):
               for _ in range(reps + 10)]
         for r, (a, b) in enumerate(ev):
             if flushed:
-                flush.fill_(float(r))
+                torch.amax(flush, dim=0, out=flush_max)
             a.record()
             fn()
             b.record()

@@ -237,7 +237,8 @@ int swa_decode(const void* q, const void* k_ring, const void* v_ring, const int3
  *   k_ring, v_ring  in/out [B, Hkv, W, d].
  *   pos             device int32 [B], the position of each chunk's first token.
  *   k, v            input [B, Hkv, n, d].
- *   B, n, Hkv, W >= 1, d in {32, 64, 128}, dtype in swa_dtype.
+ *   B, n, Hkv, W >= 1, d in {32, 64, 128}, dtype in swa_dtype;
+ *   B * Hkv * min(n, W) * d * element size / 16 < 2^31 (SWA_ERR_UNSUPPORTED).
  */
 int swa_cache_append_chunk(void* k_ring, void* v_ring, const int32_t* pos, const void* k,
                            const void* v, int B, int n, int Hkv, int W, int d, int dtype,

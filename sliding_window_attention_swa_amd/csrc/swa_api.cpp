@@ -163,7 +163,8 @@ int swa_cache_append_chunk(void* k_ring, void* v_ring, const int32_t* pos, const
   if (!supported_d(d) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
   const long long row_bytes = (long long)d * elem_bytes(dtype);
   const long long written = n < W ? n : W;
-  if ((long long)B * Hkv * written * (row_bytes / 16) / 256 + 1 > kMaxGrid) return SWA_ERR_UNSUPPORTED;
+  // one thread per 16 bytes written, indexed in 32 bits
+  if ((long long)B * Hkv * written * (row_bytes / 16) > 2147483647LL) return SWA_ERR_UNSUPPORTED;
   hipError_t e = swa::launch_append_chunk(k_ring, v_ring, pos, k, v, B, n, Hkv, W, (int)row_bytes,
                                           static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH;

@@ -731,8 +731,8 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
 template <int MODE>
 constexpr int kShortOff = MODE == 0 ? 32 : 16;
 // query heads of a KV group per short-window workgroup (at most): two
-// measured best (TinyMistral 22.3 -> 20.2 us warm, 37 -> 33 us from HBM; four:
-// 20.6 / 32.5 us)
+// measured best (TinyMistral 22.3 -> 20.2 us warm, 37 -> 33 us after a cache
+// flush by writing; four: 20.6 / 32.5 us)
 #ifndef SWA_SHORT_GROUP
 #define SWA_SHORT_GROUP 2
 #endif

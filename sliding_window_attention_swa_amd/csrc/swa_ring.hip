@@ -97,22 +97,25 @@ __global__ __launch_bounds__(256) void append_kernel(uint4* __restrict__ k_ring,
 // Append n consecutive tokens per sequence: token i goes to slot
 // (pos + i) mod W.  Only the last min(n, W) tokens are written (n single
 // appends in order would overwrite the earlier ones); they map to distinct
-// slots, so no two threads write the same row.  One thread per 16 bytes.
+// slots, so no two threads write the same row.  One thread per 16 bytes; a
+// row is 2^log_cpr such chunks, and the index space (total < 2^31) is split
+// with a mask, a shift and two 32-bit divisions.
 __global__ __launch_bounds__(256) void append_chunk_kernel(
     uint4* __restrict__ k_ring, uint4* __restrict__ v_ring, const int32_t* __restrict__ pos,
     const uint4* __restrict__ k, const uint4* __restrict__ v, int Hkv, int n, int n0, int W,
-    int cpr, long long total) {
-  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    int log_cpr, unsigned total) {
+  const unsigned idx = blockIdx.x * 256u + threadIdx.x;
   if (idx >= total) return;
-  const int c = (int)(idx % cpr);
-  const long long t = idx / cpr;
-  const int i = n0 + (int)(t % (n - n0));
-  const long long bh = t / (n - n0);
-  const int p = pos[bh / Hkv];
+  const unsigned c = idx & ((1u << log_cpr) - 1u);
+  const unsigned t = idx >> log_cpr;  // (sequence x KV head, token) row
+  const unsigned m = (unsigned)(n - n0);
+  const unsigned bh = t / m;
+  const int i = n0 + (int)(t - bh * m);
+  const int p = pos[bh / (unsigned)Hkv];
   if (p < 0) return;
   const unsigned slot = ((unsigned)p + (unsigned)i) % (unsigned)W;
-  const long long dst = (bh * W + slot) * cpr + c;
-  const long long src = (bh * n + i) * cpr + c;
+  const size_t dst = (((size_t)bh * W + slot) << log_cpr) + c;
+  const size_t src = (((size_t)bh * n + i) << log_cpr) + c;
   k_ring[dst] = k[src];
   v_ring[dst] = v[src];
 }
@@ -603,14 +606,15 @@ hipError_t launch_append(void* k_ring, void* v_ring, const int32_t* pos, const v
 hipError_t launch_append_chunk(void* k_ring, void* v_ring, const int32_t* pos, const void* k,
                                const void* v, int B, int n, int Hkv, int W, int row_bytes,
                                hipStream_t stream) {
-  const int cpr = row_bytes / 16;
+  int log_cpr = 0;  // row_bytes / 16 is a power of two (d in {32, 64, 128})
+  while ((16 << log_cpr) < row_bytes) ++log_cpr;
   const int n0 = n > W ? n - W : 0;
-  const long long total = (long long)B * Hkv * (n - n0) * cpr;
+  const long long total = ((long long)B * Hkv * (n - n0)) << log_cpr;  // < 2^31 (checked)
   const long long blocks = (total + 255) / 256;
   hipLaunchKernelGGL(append_chunk_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      static_cast<uint4*>(k_ring), static_cast<uint4*>(v_ring), pos,
                      static_cast<const uint4*>(k), static_cast<const uint4*>(v), Hkv, n, n0, W,
-                     cpr, total);
+                     log_cpr, (unsigned)total);
   return hipGetLastError();
 }
 

@@ -167,6 +167,7 @@ def append_chunk(lib, kr=P, vr=P, pos=P, k=P, v=P, B=2, n=5, Hkv=2, W=8, d=64, d
     (dict(k=MIS), INVALID), (dict(B=0), INVALID), (dict(n=0), INVALID), (dict(n=-1), INVALID),
     (dict(Hkv=0), INVALID), (dict(W=0), INVALID), (dict(d=8), UNSUPPORTED),
     (dict(dtype=2), UNSUPPORTED),
+    (dict(B=65536, Hkv=1024), UNSUPPORTED),  # 2^31 or more 16-byte chunks to write
 ])
 def test_append_chunk_rejects(lib, kw, status):
     assert append_chunk(lib, **kw) == status
