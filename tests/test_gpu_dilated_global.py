@@ -37,6 +37,8 @@ SMALL = [
     (1, 700, 33, 5, [5, 10, 350, 699], 1, 6, 3, 64),
     (0, 129, 300, 2, [64], 2, 2, 1, 128),                     # window longer than each class
     (1, 64, 1, 4, [0, 63], 1, 2, 1, 64),                      # W = 1: self plus globals
+    (1, 37, 5, 40, [0, 36], 1, 2, 1, 64),                     # dilation > T: one-row classes
+    (0, 50, 9, 49, [3, 49], 1, 4, 2, 128),                    # dilation T - 1
 ]
 
 
