@@ -1,7 +1,7 @@
-"""The GPU runs read the library sources, the tests, the oracle, the input
-generator, bench.py and the committed traffic summary: none of them may be
-excluded from the tree that is sent to the GPU machine (.gpurunignore, tar
-patterns: "./x" anchors at the top, other patterns match at any depth)."""
+"""The GPU tests, smoke() and bench.py read the library sources, the tests,
+the oracle, the input generator and the committed traffic summary: none of
+them may be matched by a pattern of .gpurunignore (tar patterns: "./x"
+anchors at the top, other patterns match at any depth)."""
 
 import fnmatch
 import os
