@@ -19,7 +19,7 @@ bounded sample of the same work.
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
        python bench.py --all-configs   (every configuration vs its roofline, warm and
                                         flushed; not the benchmark line)
-       python bench.py --peaks         (the matrix-core and streaming-read rates the box
+       python bench.py --peaks         (the matrix-core and streaming-read rates this GPU
                                         sustains, from the library's calibration kernels)
        python bench.py --cpu-oracle    (the fp64 oracle's speed per configuration on the
                                         host cores, all threads and one)
@@ -393,7 +393,7 @@ def global_pairs(T, W, mode, gpos, dilation=1):
 
 
 def measured_peaks(swa, dev, timed):
-    """What the box sustains (the library's calibration kernels): bf16 matrix
+    """What this GPU sustains (the library's calibration kernels): bf16 matrix
     TFLOP/s of an MFMA loop on N(0,1) operands (the attention inputs'
     distribution), and GB/s of a non-temporal streaming read of 2 GiB (past
     the Infinity Cache); each the best of three grids."""
@@ -619,11 +619,11 @@ def main():
                     help="HBM bytes of the --pmc-small configurations from FETCH_SIZE / "
                          "WRITE_SIZE counter CSVs")
     ap.add_argument("--no-peaks", action="store_true",
-                    help="skip the measurement of the box's sustained matrix and read rates "
+                    help="skip the measurement of this GPU's sustained matrix and read rates "
                          "after the timed steps")
     ap.add_argument("--peaks", action="store_true",
                     help="instead of the benchmark line: the matrix-core and streaming-read "
-                         "rates the box sustains (the library's calibration kernels)")
+                         "rates this GPU sustains (the library's calibration kernels)")
     ap.add_argument("--all-configs", action="store_true",
                     help="instead of the benchmark line: every configuration, cache-warm and "
                          "flushed, against its roofline (one JSON line each)")

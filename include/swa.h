@@ -312,7 +312,7 @@ size_t swa_decode_workspace_bytes(int B, int Hq, int W, int d);
 
 /*
  * Calibration kernels.  They compute nothing of the attention method: they
- * measure, on the box the attention kernels run on, the two ceilings those
+ * measure, on the GPU the attention kernels run on, the two ceilings those
  * kernels are bound by, so that their throughput can be quoted against what
  * the chip sustains as well as against its published peaks.
  *
