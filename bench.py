@@ -727,7 +727,7 @@ def main():
     traffic = read_traffic("", PREFILL_SOURCE)
     dec_traffic = read_traffic("decode_", DECODE_SOURCE)
     peaks = None
-    if not args.no_peaks:  # after the timed region: what this machine sustains
+    if not args.no_peaks:  # after the timed region: what this GPU sustains
         def timed(fn, flushed):
             ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                   for _ in range(8)]

@@ -1,5 +1,5 @@
 // Calibration kernels: what this chip sustains on the two resources the
-// attention kernels are bound by, measured on the same box as they are.  They
+// attention kernels are bound by, measured on the same GPU as they are.  They
 // compute nothing of the attention method.
 //
 //   * matrix cores: a loop of v_mfma_f32_32x32x16_bf16 on random bf16
