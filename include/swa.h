@@ -61,9 +61,11 @@ extern "C" {
 typedef enum {
   SWA_OK = 0,
   SWA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, Hq % Hkv != 0,
-                               non-finite scale, misaligned pointer */
+                               scale not finite or |scale| > 1024, misaligned
+                               pointer */
   SWA_ERR_UNSUPPORTED = -2, /* d not in {32, 64, 128}, unknown mode or dtype,
-                               launch grid beyond the int32 range */
+                               sequence longer than 2^29, launch grid beyond
+                               the int32 range */
   SWA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
   SWA_ERR_LAUNCH = -4       /* the HIP runtime rejected a kernel launch */
 } swa_status;
@@ -95,7 +97,13 @@ typedef enum { SWA_F32 = 0, SWA_BF16 = 1 } swa_dtype;
  *   q, k, v  input, layouts above, element type `dtype`.
  *   out      output [Hq, T, d] (may not alias q, k or v).
  *   T >= 1, W >= 1, Hq >= 1, Hkv >= 1, Hq % Hkv == 0, d in {32, 64, 128},
- *   mode in swa_mode, scale finite, dtype in swa_dtype.
+ *   mode in swa_mode, |scale| <= 1024 (SWA_ERR_INVALID_ARG otherwise; see
+ *   below), dtype in swa_dtype; T <= 2^29 (SWA_ERR_UNSUPPORTED otherwise).
+ *   W may exceed T: W >= T (causal) or floor(W/2) >= T - 1 (symmetric) is full
+ *   attention.
+ * Scale bound (every entry point): the softmax exponent scale*log2(e)*(s - m)
+ * is formed in fp32 as s*c - m*c, whose rounding grows with |s * c|; up to
+ * |scale| = 1024 it stays below 0.01 for scores up to 100 in magnitude.
  * Returns SWA_OK or a negative swa_status.
  */
 int swa_prefill(const void* q, const void* k, const void* v, void* out, int T, int W, int Hq,
@@ -267,8 +275,8 @@ int swa_cache_append_chunk(void* k_ring, void* v_ring, const int32_t* pos, const
  *   pos             device int32 [B], the position of each chunk's first token
  *                   (the number of tokens appended before it).
  *   out             output [B, Hq, n, d] (may not alias any input).
- *   B, n, W, Hq, Hkv >= 1, Hq % Hkv == 0, d in {32, 64, 128}, scale finite,
- *   dtype in swa_dtype, W * d * element size < 2^31.
+ *   B, n, W, Hq, Hkv >= 1, Hq % Hkv == 0, d in {32, 64, 128}, |scale| <= 1024,
+ *   dtype in swa_dtype, W * d * element size < 2^31, n <= 2^29 (SWA_ERR_UNSUPPORTED).
  */
 int swa_prefill_chunk(const void* q, const void* k, const void* v, const void* k_ring,
                       const void* v_ring, const int32_t* pos, void* out, int B, int n, int W,
@@ -309,36 +317,6 @@ size_t swa_decode_sinks_workspace_bytes(int B, int Hq, int W, int d);
 
 /* Workspace bytes swa_decode needs for these sizes (0 for invalid sizes). */
 size_t swa_decode_workspace_bytes(int B, int Hq, int W, int d);
-
-/*
- * Calibration kernels.  They compute nothing of the attention method: they
- * measure, on the GPU the attention kernels run on, the two ceilings those
- * kernels are bound by, so that their throughput can be quoted against what
- * the chip sustains as well as against its published peaks.
- *
- * swa_calib_mfma_bf16 - n_wg workgroups of four waves; each wave runs
- * iters x 16 v_mfma_f32_32x32x16_bf16 (32,768 FLOPs each) on operands taken
- * from `operands` (device, bf16 bits, operand_bytes a multiple of 16, at
- * least 16; random data gives the chip's power-limited rate, which is what
- * attention operands see), rotating four A and four B fragments per lane
- * over four accumulator chains.  Total FLOPs = n_wg * 4 * iters * 16 * 32768.
- *   sink   output float [n_wg * 256] (per-lane sums, keeps the work live).
- *   Errors: SWA_ERR_INVALID_ARG for null or unaligned pointers, bad sizes,
- *   n_wg outside [1, 2^20], iters < 0; SWA_ERR_LAUNCH on launch failure.
- *
- * swa_calib_stream_read - reads `bytes` (a multiple of 16) from device memory
- * `src` with 16-byte non-temporal loads: workgroup w of n_wg (256 lanes,
- * eight loads in flight per lane) reads the w-th contiguous chunk.  Use a
- * buffer larger than the 256 MB Infinity Cache to measure HBM.
- *   sink   output uint32 [n_wg * 256] (XOR of what each lane read).
- *   Errors as above (n_wg >= 1).
- *
- * Both are asynchronous on `stream`; time them with events on that stream.
- */
-int swa_calib_mfma_bf16(const void* operands, size_t operand_bytes, float* sink, int n_wg,
-                        int iters, void* stream);
-int swa_calib_stream_read(const void* src, size_t bytes, unsigned* sink, int n_wg,
-                          void* stream);
 
 /* Static, human-readable text for a swa_status value. */
 const char* swa_status_string(int status);

@@ -23,10 +23,8 @@ SYMMETRIC = 1
 SWA_F32 = 0
 SWA_BF16 = 1
 
-# SWA_LIBRARY may point at another build of the same library (e.g. a tuning
-# variant); by default the in-tree build is used.
-LIB_PATH = os.environ.get("SWA_LIBRARY") or os.path.join(
-    os.path.dirname(os.path.abspath(__file__)), "libswa.so")
+# the in-tree build; no other library is ever loaded
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswa.so")
 
 _lib = None
 
@@ -108,6 +106,15 @@ def _check(t, name, ndim, dtype=None):
         raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
 
 
+def _same_device(**tensors):
+    """Every tensor of one call on the same device (the C ABI sees only
+    pointers and cannot tell)."""
+    devs = {t.device for t in tensors.values() if t is not None}
+    if len(devs) > 1:
+        raise ValueError("tensors on different devices: %s" % ", ".join(
+            "%s=%s" % (n, t.device) for n, t in tensors.items() if t is not None))
+
+
 def _stream(stream):
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -134,6 +141,7 @@ def prefill(q, k, v, W, mode=CAUSAL, scale=None, out=None, stream=None):
     _check(out, "out", 4, q.dtype)
     if tuple(out.shape) != tuple(q.shape):
         raise ValueError("out must have q's shape")
+    _same_device(q=q, k=k, v=v, out=out)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     st = load().swa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), T, int(W),
@@ -159,6 +167,7 @@ def prefill_dilated(q, k, v, W, dilation, mode=CAUSAL, scale=None, out=None, str
     _check(out, "out", 4, q.dtype)
     if tuple(out.shape) != tuple(q.shape):
         raise ValueError("out must have q's shape")
+    _same_device(q=q, k=k, v=v, out=out)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     st = load().swa_prefill_dilated(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), T,
@@ -188,6 +197,7 @@ def prefill_global(q, k, v, W, global_pos, mode=CAUSAL, scale=None, out=None, wo
     _check(out, "out", 4, q.dtype)
     if tuple(out.shape) != tuple(q.shape):
         raise ValueError("out must have q's shape")
+    _same_device(q=q, k=k, v=v, global_pos=global_pos, out=out, workspace=workspace)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     G = global_pos.shape[0]
@@ -216,6 +226,7 @@ def cache_append(k_ring, v_ring, pos, k_new, v_new, stream=None):
     if tuple(v_ring.shape) != tuple(k_ring.shape) or tuple(k_new.shape) != (B, Hkv, d) \
             or tuple(v_new.shape) != (B, Hkv, d) or pos.shape[0] != B:
         raise ValueError("shape mismatch")
+    _same_device(k_ring=k_ring, v_ring=v_ring, pos=pos, k_new=k_new, v_new=v_new)
     st = load().swa_cache_append(k_ring.data_ptr(), v_ring.data_ptr(), pos.data_ptr(),
                                  k_new.data_ptr(), v_new.data_ptr(), B, Hkv, W, d,
                                  _dtype_code(k_ring), _stream(stream))
@@ -227,7 +238,8 @@ def decode_workspace_bytes(B, Hq, W, d):
 
 
 def decode_workspace(B, Hq, W, d, device="cuda"):
-    """A zero-filled decode workspace (reusable across calls without clearing)."""
+    """A decode workspace (reusable across calls without clearing; 16 bytes
+    when the call needs none)."""
     import torch
     return torch.zeros(max(decode_workspace_bytes(B, Hq, W, d), 16), dtype=torch.uint8, device=device)
 
@@ -257,15 +269,21 @@ def decode(q, k_ring, v_ring, pos, scale=None, out=None, workspace=None, stream=
     if out is None:
         out = torch.empty_like(q)
     _check(out, "out", 3, q.dtype)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    _same_device(q=q, k_ring=k_ring, v_ring=v_ring, pos=pos, out=out, workspace=workspace)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = decode_workspace_bytes(B, Hq, W, d)
-    if workspace is None:
-        workspace = decode_workspace(B, Hq, W, d, q.device)
+    if need == 0:  # one split: the kernel writes out itself and reads no workspace
+        ws_ptr, ws_bytes = None, 0
+    else:
+        if workspace is None:
+            workspace = decode_workspace(B, Hq, W, d, q.device)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     st = load().swa_decode(q.data_ptr(), k_ring.data_ptr(), v_ring.data_ptr(), pos.data_ptr(),
                            out.data_ptr(), B, Hq, Hkv, W, d, float(scale), _dtype_code(q),
-                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                           _stream(stream))
+                           ws_ptr, ws_bytes, _stream(stream))
     _raise("swa_decode", st)
     return out
 
@@ -284,6 +302,7 @@ def cache_append_chunk(k_ring, v_ring, pos, k, v, stream=None):
     if tuple(v_ring.shape) != tuple(k_ring.shape) or tuple(k.shape) != (B, Hkv, n, d) \
             or tuple(v.shape) != tuple(k.shape) or pos.shape[0] != B:
         raise ValueError("shape mismatch")
+    _same_device(k_ring=k_ring, v_ring=v_ring, pos=pos, k=k, v=v)
     st = load().swa_cache_append_chunk(k_ring.data_ptr(), v_ring.data_ptr(), pos.data_ptr(),
                                        k.data_ptr(), v.data_ptr(), B, n, Hkv, W, d,
                                        _dtype_code(k_ring), _stream(stream))
@@ -313,6 +332,7 @@ def prefill_chunk(q, k, v, k_ring, v_ring, pos, scale=None, out=None, stream=Non
     _check(out, "out", 4, q.dtype)
     if tuple(out.shape) != tuple(q.shape):
         raise ValueError("out must have q's shape")
+    _same_device(q=q, k=k, v=v, k_ring=k_ring, v_ring=v_ring, pos=pos, out=out)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     st = load().swa_prefill_chunk(q.data_ptr(), k.data_ptr(), v.data_ptr(), k_ring.data_ptr(),
@@ -350,6 +370,10 @@ def decode_sinks(q, k_ring, v_ring, k_sink, v_sink, pos, scale=None, out=None, w
     if out is None:
         out = torch.empty_like(q)
     _check(out, "out", 3, q.dtype)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    _same_device(q=q, k_ring=k_ring, v_ring=v_ring, k_sink=k_sink, v_sink=v_sink, pos=pos,
+                 out=out, workspace=workspace)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if workspace is None:

@@ -30,10 +30,10 @@ SOURCES = ["swa_prefill_bf16.hip", "swa_prefill_f32.hip", "swa_ring.hip", "swa_c
            "swa_api.cpp"]
 
 
-def _compile(src, csrc=CSRC, build_dir=BUILD, defines=()):
+def _compile(src, build_dir):
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-D" + d for d in defines] + [
-        "-I", os.path.join(ROOT, "include"), "-c", os.path.join(csrc, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + [
+        "-I", os.path.join(ROOT, "include"), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the device-only feature flag: drop that note
     noise = "'-packed-fp32-ops' is not a recognized feature for this target"
@@ -45,13 +45,13 @@ def _compile(src, csrc=CSRC, build_dir=BUILD, defines=()):
     return obj
 
 
-def build(verbose=True, csrc=CSRC, out=LIB, defines=()):
-    """Compile every source in `csrc` and link `out` (default: the in-tree
-    libswa.so).  `defines` are extra -D macros."""
-    build_dir = os.path.join(BUILD, os.path.basename(out) + ".d")
+def build(verbose=True):
+    """Compile every source in csrc/ and link the in-tree libswa.so."""
+    out = LIB
+    build_dir = os.path.join(BUILD, "libswa.so.d")
     os.makedirs(build_dir, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, csrc, build_dir, defines), SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, build_dir), SOURCES))
     tmp = out + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include "swa.h"
+#include "swa_calib.h"
 #include "swa_launch.h"
 
 namespace {
@@ -22,6 +23,27 @@ int elem_bytes(int dtype) { return dtype == SWA_BF16 ? 2 : 4; }
 
 constexpr long long kMaxGrid = 2147483647LL;
 
+// Longest sequence (and chunk) a prefill call takes: row and key indices, and
+// the ends of a block's key range (row + 127 + W / 2 after the clamp below),
+// stay inside int32.
+constexpr int kMaxSeq = 1 << 29;
+
+// |scale| above this is rejected.  The kernels form the softmax exponent
+// scale * log2(e) * (s - m) as one fp32 fused multiply-add, s * c - m * c,
+// whose rounding is about |s * c| * 2^-24: at |scale| <= 1024 it stays below
+// 0.01 (a bf16-level error in the probability) for scores up to 100 in
+// magnitude, and the starting reference -1e30 * c stays finite.  Attention
+// scales are 1/sqrt(d) <= 1; a softmax at |scale| = 1024 is already a hard
+// maximum for scores that differ by more than a few hundredths.
+constexpr float kMaxScale = 1024.0f;
+
+bool scale_ok(float scale) { return isfinite(scale) && fabsf(scale) <= kMaxScale; }
+
+// A window wider than the sequence sees every key it can: W >= T (causal) and
+// floor(W / 2) >= T - 1 (symmetric) are both full attention, also on a
+// dilation grid, so W is clamped to 2T before launch (exact).
+int clamp_window(int W, int T) { return (long long)W > 2LL * T ? 2 * T : W; }
+
 }  // namespace
 
 extern "C" {
@@ -32,11 +54,13 @@ int swa_prefill(const void* q, const void* k, const void* v, void* out, int T, i
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SWA_ERR_INVALID_ARG;
   if (T <= 0 || W <= 0 || Hq <= 0 || Hkv <= 0) return SWA_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return SWA_ERR_INVALID_ARG;
-  if (!isfinite(scale)) return SWA_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return SWA_ERR_INVALID_ARG;
   if (!supported_d(d) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
   if (mode != SWA_CAUSAL && mode != SWA_SYMMETRIC) return SWA_ERR_UNSUPPORTED;
+  if (T > kMaxSeq) return SWA_ERR_UNSUPPORTED;
   // workgroup count (16-row blocks for fp32 is the larger) must fit the grid
   if ((long long)((T + 15) / 16) * Hq > kMaxGrid) return SWA_ERR_UNSUPPORTED;
+  W = clamp_window(W, T);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = (dtype == SWA_BF16)
                      ? swa::launch_prefill_bf16(q, k, v, out, T, W, Hq, Hkv, d, mode, scale, s)
@@ -51,15 +75,17 @@ int swa_prefill_dilated(const void* q, const void* k, const void* v, void* out, 
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SWA_ERR_INVALID_ARG;
   if (T <= 0 || W <= 0 || Hq <= 0 || Hkv <= 0 || dilation <= 0) return SWA_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return SWA_ERR_INVALID_ARG;
-  if (!isfinite(scale)) return SWA_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return SWA_ERR_INVALID_ARG;
   if (!supported_d(d) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
   if (mode != SWA_CAUSAL && mode != SWA_SYMMETRIC) return SWA_ERR_UNSUPPORTED;
+  if (T > kMaxSeq) return SWA_ERR_UNSUPPORTED;
   // a tile's 64 rows, dilation rows apart, are addressed with 32-bit byte offsets
   if ((long long)dilation * d * elem_bytes(dtype) * 64 > 2147483647LL) return SWA_ERR_UNSUPPORTED;
   // workgroup counts: 16-row blocks (fp32); 128-row blocks of each residue class (bf16)
   if ((long long)((T + 15) / 16) * Hq > kMaxGrid) return SWA_ERR_UNSUPPORTED;
   const long long class_rows = (T + (long long)dilation - 1) / dilation;
   if ((class_rows + 127) / 128 * Hq * (long long)dilation > kMaxGrid) return SWA_ERR_UNSUPPORTED;
+  W = clamp_window(W, T);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e =
       (dtype == SWA_BF16)
@@ -79,7 +105,7 @@ static int prefill_global_impl(const void* q, const void* k, const void* v, void
     return SWA_ERR_INVALID_ARG;
   if (T <= 0 || W <= 0 || Hq <= 0 || Hkv <= 0 || G < 0 || dilation <= 0) return SWA_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return SWA_ERR_INVALID_ARG;
-  if (!isfinite(scale)) return SWA_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return SWA_ERR_INVALID_ARG;
   if (!supported_d(d) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
   if (mode != SWA_CAUSAL && mode != SWA_SYMMETRIC) return SWA_ERR_UNSUPPORTED;
   // global keys are gathered with 32-bit byte offsets into a head's K/V, and
@@ -95,6 +121,7 @@ static int prefill_global_impl(const void* q, const void* k, const void* v, void
   if ((long long)Hkv * ((G * (Hq / Hkv) + 31) / 32) * S1 > kMaxGrid) return SWA_ERR_UNSUPPORTED;
   const size_t need = swa_prefill_global_workspace_bytes(T, Hq, G, d);
   if (!workspace || !aligned16(workspace) || workspace_bytes < need) return SWA_ERR_WORKSPACE;
+  W = clamp_window(W, T);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = (dtype == SWA_BF16)
                      ? swa::launch_prefill_global_window_bf16(q, k, v, out, T, W, Hq, Hkv, d, mode,
@@ -179,8 +206,9 @@ int swa_prefill_chunk(const void* q, const void* k, const void* v, const void* k
     return SWA_ERR_INVALID_ARG;
   if (B <= 0 || n <= 0 || W <= 0 || Hq <= 0 || Hkv <= 0) return SWA_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return SWA_ERR_INVALID_ARG;
-  if (!isfinite(scale)) return SWA_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return SWA_ERR_INVALID_ARG;
   if (!supported_d(d) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
+  if (n > kMaxSeq) return SWA_ERR_UNSUPPORTED;
   // ring rows are addressed with 32-bit byte offsets
   if ((long long)W * d * elem_bytes(dtype) > 2147483647LL) return SWA_ERR_UNSUPPORTED;
   // folded head counts and the workgroup count (16-row blocks for fp32) fit int32
@@ -208,6 +236,7 @@ size_t swa_prefill_global_workspace_bytes(int T, int Hq, int G, int d) {
 size_t swa_decode_workspace_bytes(int B, int Hq, int W, int d) {
   if (B <= 0 || Hq <= 0 || W <= 0 || !supported_d(d)) return 0;
   const int S = swa::decode_splits(B, Hq, W);
+  if (S == 1) return 0;  // one split writes the output itself: no partials
   return (size_t)B * Hq * S * (size_t)(d + 2) * sizeof(float);
 }
 
@@ -220,10 +249,11 @@ int swa_decode(const void* q, const void* k_ring, const void* v_ring, const int3
     return SWA_ERR_INVALID_ARG;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || W <= 0) return SWA_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return SWA_ERR_INVALID_ARG;
-  if (!isfinite(scale)) return SWA_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return SWA_ERR_INVALID_ARG;
   if (!supported_d(d) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
   const size_t need = swa_decode_workspace_bytes(B, Hq, W, d);
-  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return SWA_ERR_WORKSPACE;
+  if (need > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need))
+    return SWA_ERR_WORKSPACE;
   const int S = swa::decode_splits(B, Hq, W);
   if ((long long)B * Hq * S > kMaxGrid) return SWA_ERR_UNSUPPORTED;
   hipError_t e = swa::launch_decode(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, d, scale, dtype,
@@ -251,7 +281,7 @@ int swa_decode_sinks(const void* q, const void* k_ring, const void* v_ring, cons
     return SWA_ERR_INVALID_ARG;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || W <= 0 || n_sink < 0) return SWA_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return SWA_ERR_INVALID_ARG;
-  if (!isfinite(scale)) return SWA_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return SWA_ERR_INVALID_ARG;
   if (!supported_d(d) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
   const size_t need = swa_decode_sinks_workspace_bytes(B, Hq, W, d);
   if (!workspace || !aligned16(workspace) || workspace_bytes < need) return SWA_ERR_WORKSPACE;

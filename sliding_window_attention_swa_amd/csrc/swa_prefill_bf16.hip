@@ -75,12 +75,8 @@ namespace {
 // regions A and B (spread evenly over the region's products): 80 measured
 // 0.6-2% faster than 56 on the Mistral-7B prefill (two boxes, alternated
 // builds; 64, 72 and 96 also tried)
-#ifndef SWA_VALU_A
-#define SWA_VALU_A 80
-#endif
-#ifndef SWA_VALU_B
-#define SWA_VALU_B 80
-#endif
+constexpr int kValuA = 80;
+constexpr int kValuB = 80;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;   // query rows per workgroup
@@ -327,7 +323,9 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     }
     const int last = T - 1 - kbase;  // last valid row of this tile
     const int RSB = RS * 2;           // bytes between consecutive rows
-    const int bytes = kDil ? min(last, kBN - 1) * RSB + ROWB : (last + 1) * ROWB;
+    // the resource starts at the tile and ends after its last valid row
+    // (at most 64 rows: the size stays far inside int32 at any T)
+    const int bytes = min(last, kBN - 1) * RSB + ROWB;
     const __amdgpu_buffer_rsrc_t rk =
         __builtin_amdgcn_make_buffer_rsrc((void*)(kh + (size_t)kbase * RS), 0, bytes, kBufferFlags);
     const __amdgpu_buffer_rsrc_t rv =
@@ -371,7 +369,10 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   f32x16 o[MD];
 #pragma unroll
   for (int md = 0; md < MD; ++md) o[md] = f32x16{};
-  float m_ref = kNoMax;  // raw-score reference maximum of this lane's row
+  // raw-score reference maximum of this lane's row; it starts so low that the
+  // first visited keys raise it, yet -m_ref * c stays finite (c <= 1478 for
+  // every scale the library accepts), so a masked score gives exp2(-inf) = 0
+  float m_ref = kNoMax;
   float l_part = 0.f;    // this lane's share of the row sum
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -497,7 +498,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
 #pragma unroll
     for (int i = 0; i < KS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, SWA_VALU_A / KS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kValuA / KS, 0);
       if (i < KS / 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -517,7 +518,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
 #pragma unroll
     for (int i = 0; i < 2 * MD; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, SWA_VALU_B / (2 * MD), 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kValuB / (2 * MD), 0);
       if (i < 2 * MD - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -743,9 +744,7 @@ constexpr int kShortOff = MODE == 0 ? 32 : 16;
 // query heads of a KV group per short-window workgroup (at most): two
 // measured best (TinyMistral 22.3 -> 20.2 us warm, 37 -> 33 us after a cache
 // flush by writing; four: 20.6 / 32.5 us)
-#ifndef SWA_SHORT_GROUP
-#define SWA_SHORT_GROUP 2
-#endif
+constexpr int kShortGroup = 2;
 
 bool short_window(int W, int mode) { return mode == 0 ? W <= 33 : (W >> 1) <= 16; }
 
@@ -790,24 +789,28 @@ void prefill_short_kernel(
   const int kb0 = qw0 - kShortOff<MODE>;  // key of LDS row 0 (may be negative)
 
   const __bf16* qh = q + (size_t)h * T * D;
-  const __bf16* kh = k + (size_t)kvh * T * D;
-  const __bf16* vh = v + (size_t)kvh * T * D;
 
   // ---- the key block, rows clamped into [0, T) (out-of-range rows hold
   // finite data and are masked below); load j of a lane fills LDS bytes
-  // [(64*j + lane)*16, +16)
+  // [(64*j + lane)*16, +16).  The resource starts at the block's first row
+  // inside the sequence (blo) and covers at most its 64 rows, so offsets stay
+  // small at any T.
   {
+    const int blo = max(kb0, 0);
+    const int bhi = min(kb0 + 63, T - 1);
+    const __bf16* kblk = k + ((size_t)kvh * T + blo) * D;
+    const __bf16* vblk = v + ((size_t)kvh * T + blo) * D;
     const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void*)kh, 0, T * ROWB, kBufferFlags);
+        __builtin_amdgcn_make_buffer_rsrc((void*)kblk, 0, (bhi - blo + 1) * ROWB, kBufferFlags);
     const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc((void*)vh, 0, T * ROWB, kBufferFlags);
+        __builtin_amdgcn_make_buffer_rsrc((void*)vblk, 0, (bhi - blo + 1) * ROWB, kBufferFlags);
 #pragma unroll
     for (int jj = 0; jj < NL / NW; ++jj) {
       const int j = wave * (NL / NW) + jj;
       const int o = (64 * j + lane) * 16;
       const int row = o / ROWB;
-      const int src = min(max(kb0 + row, 0), T - 1);
-      const int off = src * ROWB + ((((o % ROWB) / 16) ^ swz<D>(row)) * 16);
+      const int src = min(max(kb0 + row, blo), bhi);
+      const int off = (src - blo) * ROWB + ((((o % ROWB) / 16) ^ swz<D>(row)) * 16);
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass mishandles this builtin
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(lds_k + 64 * j * 16), 16, off, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(lds_v + 64 * j * 16), 16, off, 0, 0, 0);
@@ -943,13 +946,13 @@ hipError_t launch_short(const void* q, const void* k, const void* v, void* out, 
                      static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),                 \
                      static_cast<__bf16*>(out), T, W, Hq, Hkv, c, qsign, n_wtiles)
   // query heads of a KV group share the key block where the group allows
-  if constexpr (SWA_SHORT_GROUP >= 4) {
+  if constexpr (kShortGroup >= 4) {
     if (G % 4 == 0) {
       SWA_SHORT(4);
       return hipGetLastError();
     }
   }
-  if constexpr (SWA_SHORT_GROUP >= 2) {
+  if constexpr (kShortGroup >= 2) {
     if (G % 2 == 0) {
       SWA_SHORT(2);
       return hipGetLastError();
@@ -1064,10 +1067,7 @@ hipError_t launch_chunk(const void* q, const void* k, const void* v, const void*
 // decode kernels' merge pass.
 // keys per split: 128 measured best at Longformer shapes (11.5 us; 256: 12.3,
 // 512: 15.2 us, the merge then costing less)
-#ifndef SWA_GROW_KEYS
-#define SWA_GROW_KEYS 128
-#endif
-constexpr int kGRowKeys = SWA_GROW_KEYS;
+constexpr int kGRowKeys = 128;
 
 template <int D, int MODE>
 __global__ __launch_bounds__(64)

@@ -45,34 +45,21 @@ constexpr float kRescaleThreshold = 8.0f;
 constexpr float kNegBig = -1.0e30f;
 constexpr int kDecodeThreads = 256;
 constexpr int kDecodeWaves = kDecodeThreads / 64;
-// Tuning constants (the defaults are the measured choices):
-//   SWA_DECODE_UNROLL   K and V rows in flight per lane
-//   SWA_DECODE_ITEMS    (row, split) items a decode launch aims at before it
-//                       stops splitting the ring
-//   SWA_GLOBAL_ITEMS    the same for the fp32 global-row pass
-//   SWA_GLOBAL_NQ       (global row, head) pairs per workgroup of that pass
-//   SWA_COMBINE_UNROLL  splits in flight in the merge of many-split rows
-//   SWA_GLOBAL_NT       non-temporal loads in the global-row pass (off: the
-//                       window pass has just read those rows)
-#ifndef SWA_DECODE_UNROLL
-#define SWA_DECODE_UNROLL 8
-#endif
-#ifndef SWA_DECODE_ITEMS
-#define SWA_DECODE_ITEMS 2048
-#endif
-#ifndef SWA_GLOBAL_ITEMS
-#define SWA_GLOBAL_ITEMS 2048
-#endif
-#ifndef SWA_GLOBAL_NQ
-#define SWA_GLOBAL_NQ 4
-#endif
-#ifndef SWA_COMBINE_UNROLL
-#define SWA_COMBINE_UNROLL 8
-#endif
-#ifndef SWA_GLOBAL_NT
-#define SWA_GLOBAL_NT 0
-#endif
-constexpr int kUnroll = SWA_DECODE_UNROLL;  // K and V rows in flight per lane
+// Measured choices:
+//   kUnroll         K and V rows in flight per lane
+//   kDecodeItems    (row, split) items a decode launch aims at before it
+//                   stops splitting the ring
+//   kGlobalItems    the same for the fp32 global-row pass
+//   kGlobalNQ       (global row, head) pairs per workgroup of that pass
+//   kCombineUnroll  splits in flight in the merge of many-split rows
+//   kGlobalNT       non-temporal loads in the global-row pass (off: the
+//                   window pass has just read those rows)
+constexpr int kUnroll = 8;
+constexpr int kDecodeItems = 2048;
+constexpr int kGlobalItems = 2048;
+constexpr int kGlobalNQ = 4;
+constexpr int kCombineUnroll = 8;
+constexpr bool kGlobalNT = false;
 
 // ------------------------------------------------------------------ append
 
@@ -292,7 +279,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
       const int r = base + (u * kDecodeWaves + wave) * RPW + rg;
       valid[u] = r < s1;
       if (valid[u]) {
-        if constexpr (kRows<GR> && !SWA_GLOBAL_NT) {  // rows the windowed pass just read
+        if constexpr (kRows<GR> && !kGlobalNT) {  // rows the windowed pass just read
           kraw[u] = *reinterpret_cast<const uint4*>(kb + (size_t)r * D);
           vraw[u] = *reinterpret_cast<const uint4*>(vb + (size_t)r * D);
         } else {
@@ -481,9 +468,9 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
   float M = m[0];
   float a = 0.f, L = 0.f;
   if constexpr (kRows<GR>) {  // many splits: several in flight at once
-#pragma unroll SWA_COMBINE_UNROLL
+#pragma unroll kCombineUnroll
     for (int s = 1; s < S; ++s) M = fmaxf(M, m[s]);
-#pragma unroll SWA_COMBINE_UNROLL
+#pragma unroll kCombineUnroll
     for (int s = 0; s < S; ++s) {
       const float w = __builtin_amdgcn_exp2f(m[s] - M);
       L = fmaf(w, l[s], L);
@@ -518,9 +505,12 @@ hipError_t launch_decode_t(const void* q, const void* k_ring, const void* v_ring
   const int n_pairs = kRows<GR> ? B * G : 0;
   const int n_hchunks = kRows<GR> ? (n_pairs + NQ - 1) / NQ : G / NQ;
   const size_t rows = (size_t)B * Hq * (GR == 3 ? S + 1 : S);
-  float* ws_acc = workspace;
-  float* ws_m = ws_acc + rows * D;
-  float* ws_l = ws_m + rows;
+  // a plain decode of one split writes the output itself: no workspace (it
+  // may be null then)
+  const bool partials = GR != 0 || S > 1;
+  float* ws_acc = partials ? workspace : nullptr;
+  float* ws_m = partials ? ws_acc + rows * D : nullptr;
+  float* ws_l = partials ? ws_m + rows : nullptr;
   const long long nwg = (long long)(kRows<GR> ? 1 : B) * Hkv * n_hchunks * S;
   hipLaunchKernelGGL((decode_split_kernel<E, D, NQ, GR>), dim3((unsigned)nwg), dim3(kDecodeThreads), 0,
                      stream, static_cast<const E*>(q), static_cast<const E*>(k_ring),
@@ -539,8 +529,8 @@ hipError_t launch_decode_d(const void* q, const void* k_ring, const void* v_ring
                            const int32_t* pos, void* out, int B, int Hq, int Hkv, int W,
                            float scale, float* workspace, hipStream_t stream) {
   const int G = Hq / Hkv;
-  if constexpr (kRows<GR>)  // global rows: SWA_GLOBAL_NQ pairs per workgroup
-    return launch_decode_t<E, D, SWA_GLOBAL_NQ, GR>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
+  if constexpr (kRows<GR>)  // global rows: kGlobalNQ pairs per workgroup
+    return launch_decode_t<E, D, kGlobalNQ, GR>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
   if (G % 4 == 0)
     return launch_decode_t<E, D, 4, GR>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
   if (G % 2 == 0)
@@ -619,11 +609,11 @@ hipError_t launch_append_chunk(void* k_ring, void* v_ring, const int32_t* pos, c
 }
 
 int decode_splits(int B, int Hq, int W) {
-  // Split each ring only as far as needed for ~SWA_DECODE_ITEMS (sequence,
+  // Split each ring only as far as needed for ~kDecodeItems (sequence,
   // query head, split) items, enough work to fill the 256 CUs; a single
   // split needs no merge pass.  Never split below 64 slots.
   const long long heads = (long long)B * Hq;
-  long long want = (SWA_DECODE_ITEMS + heads - 1) / heads;
+  long long want = (kDecodeItems + heads - 1) / heads;
   if (want < 1) want = 1;
   const long long cap = (W + 63) / 64;
   return (int)(want < cap ? want : cap);
@@ -671,14 +661,14 @@ hipError_t launch_global_combine(float* workspace, void* out, const int32_t* gpo
 }
 
 int global_splits(int G, int Hq, int T) {
-  // ~SWA_GLOBAL_ITEMS (row, head, split) items, never below 64 keys.  The
+  // ~kGlobalItems (row, head, split) items, never below 64 keys.  The
   // pass is bound by its vector arithmetic (one dot product, exponential
   // and d FMAs per key and pair), not by memory: finer splits (8192 items)
   // or 8 pairs per workgroup (registers for one wave per SIMD) measured
   // slower.  Its loads are ordinary (cached) ones: the windowed pass has just
   // read the same K/V.
   const long long rows = (long long)G * Hq;
-  long long want = (SWA_GLOBAL_ITEMS + rows - 1) / rows;
+  long long want = (kGlobalItems + rows - 1) / rows;
   if (want < 1) want = 1;
   const long long cap = (T + 63) / 64;
   return (int)(want < cap ? want : cap);

@@ -12,7 +12,7 @@ import pytest
 import sliding_window_attention_swa_amd as swa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "swa.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("swa.h", "swa_calib.h")]
 
 OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
 P = 0x10000  # aligned, never dereferenced
@@ -27,20 +27,24 @@ def lib():
     return swa.load()
 
 
-def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(swa_[a-z0-9_]+)\s*\(", text)))
+def declared_functions(headers=None):
+    names = set()
+    for path in headers or HEADERS:
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(swa_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
-def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted([
+def test_headers_declare_the_entry_points():
+    assert declared_functions(HEADERS[:1]) == sorted([
         "swa_prefill", "swa_cache_append", "swa_decode", "swa_decode_workspace_bytes",
         "swa_status_string", "swa_cache_append_chunk", "swa_prefill_chunk",
         "swa_prefill_dilated", "swa_prefill_global", "swa_prefill_global_workspace_bytes",
         "swa_prefill_dilated_global",
-        "swa_decode_sinks", "swa_decode_sinks_workspace_bytes", "swa_calib_mfma_bf16",
-        "swa_calib_stream_read"])
+        "swa_decode_sinks", "swa_decode_sinks_workspace_bytes"])
+    # the calibration kernels compute nothing of the method: a header of their own
+    assert declared_functions(HEADERS[1:]) == ["swa_calib_mfma_bf16", "swa_calib_stream_read"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -62,6 +66,11 @@ def prefill(lib, q=P, k=P, v=P, out=P, T=16, W=4, Hq=4, Hkv=2, d=64, mode=0, sca
     (dict(d=48), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(mode=2), UNSUPPORTED),
     (dict(dtype=2), UNSUPPORTED), (dict(dtype=-1), UNSUPPORTED),
     (dict(T=2**30, Hq=2**10, Hkv=1), UNSUPPORTED),
+    # sequences past 2^29 rows (the int32 index range of a block's key span)
+    (dict(T=2**29 + 1, Hq=1, Hkv=1), UNSUPPORTED), (dict(T=2**31 - 1, Hq=1, Hkv=1), UNSUPPORTED),
+    # |scale| past 1024 (the fp32 exponent s * c - m * c keeps its precision)
+    (dict(scale=1024.5), INVALID), (dict(scale=-2000.0), INVALID), (dict(scale=1e9), INVALID),
+    (dict(scale=-3e38), INVALID),
 ])
 def test_prefill_rejects(lib, kw, status):
     assert prefill(lib, **kw) == status
@@ -194,8 +203,9 @@ def test_prefill_chunk_rejects(lib, kw, status):
     assert prefill_chunk(lib, **kw) == status
 
 
-def decode(lib, q=P, kr=P, vr=P, pos=P, out=P, B=2, Hq=8, Hkv=2, W=64, d=64, scale=0.125,
+def decode(lib, q=P, kr=P, vr=P, pos=P, out=P, B=2, Hq=8, Hkv=2, W=4096, d=64, scale=0.125,
            dtype=1, ws=P, ws_bytes=None):
+    # the default sizes split the ring, so a workspace is required
     if ws_bytes is None:
         ws_bytes = lib.swa_decode_workspace_bytes(B, Hq, W, d) if B > 0 and Hq > 0 and W > 0 else 0
     return lib.swa_decode(q, kr, vr, pos, out, B, Hq, Hkv, W, d, scale, dtype, ws, ws_bytes, None)
@@ -234,12 +244,13 @@ def test_decode_sinks_rejects(lib, kw, status):
 def test_decode_sinks_workspace_is_one_split_more_than_decode(lib):
     for B, Hq, W, d in [(64, 32, 4096, 128), (1, 2, 100, 64), (3, 8, 37, 32)]:
         per_split = 4 * (d + 2) * B * Hq
-        assert lib.swa_decode_sinks_workspace_bytes(B, Hq, W, d) == \
-            lib.swa_decode_workspace_bytes(B, Hq, W, d) + per_split
+        # the plain decode keeps no partial record when it has one split
+        splits = max(1, lib.swa_decode_workspace_bytes(B, Hq, W, d) // per_split)
+        assert lib.swa_decode_sinks_workspace_bytes(B, Hq, W, d) == (splits + 1) * per_split
 
 
 def test_decode_rejects_one_byte_short_workspace(lib):
-    need = lib.swa_decode_workspace_bytes(2, 8, 64, 64)
+    need = lib.swa_decode_workspace_bytes(2, 8, 4096, 64)
     assert need > 0
     assert decode(lib, ws_bytes=need - 1) == WORKSPACE
 
@@ -248,12 +259,26 @@ def test_workspace_bytes(lib):
     f = lib.swa_decode_workspace_bytes
     assert f(0, 8, 64, 64) == 0 and f(2, 0, 64, 64) == 0 and f(2, 8, 0, 64) == 0
     assert f(2, 8, 64, 48) == 0
-    for B, Hq, W, d in [(64, 32, 4096, 128), (1, 1, 4, 64), (1, 32, 4096, 128), (3, 5, 100, 32)]:
+    # one split (enough heads to fill the GPU, or a ring of at most 64 slots):
+    # the kernel writes the output itself and needs no workspace (the
+    # Mistral-7B decode: 64 sequences x 32 heads)
+    assert f(64, 32, 4096, 128) == 0 and f(1, 1, 4, 64) == 0 and f(16, 128, 4096, 64) == 0
+    for B, Hq, W, d in [(1, 32, 4096, 128), (3, 5, 100, 32), (2, 8, 4096, 64)]:
         n = f(B, Hq, W, d)
         # whole fp32 partial records (d accumulators + max + sum) per split
         assert n > 0 and n % (4 * (d + 2) * B * Hq) == 0
         splits = n // (4 * (d + 2) * B * Hq)
-        assert 1 <= splits <= max(1, (W + 63) // 64)
+        assert 2 <= splits <= (W + 63) // 64
+
+
+def test_decode_without_workspace_only_when_none_is_needed(lib):
+    # a call that needs partials rejects a missing workspace ...
+    assert lib.swa_decode_workspace_bytes(2, 8, 4096, 64) > 0
+    assert decode(lib, ws=None, ws_bytes=0) == WORKSPACE
+    # ... and one that needs none gets past the workspace check (it then fails
+    # on the head count, so nothing is launched)
+    assert lib.swa_decode_workspace_bytes(64, 32, 4096, 128) == 0
+    assert decode(lib, B=64, Hq=33, Hkv=8, W=4096, d=128, ws=None, ws_bytes=0) == INVALID
 
 
 def calib_mfma(lib, ops=P, nbytes=65536, sink=P, n_wg=8, iters=10):

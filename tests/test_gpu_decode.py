@@ -136,8 +136,11 @@ def test_decode_equals_prefill_rows_gqa(swa):
 
 
 def test_mistral_decode_full(swa):
-    """B=64, 32/8 heads, d=128, W=4096 full rings, positions in [4096, 32768)."""
+    """B=64, 32/8 heads, d=128, W=4096 full rings, positions in [4096, 32768).
+    One split per (sequence, head) fills the GPU here, so the call needs and
+    gets no workspace (a null pointer reaches the C ABI)."""
     cfg = si.WORKLOADS[4]
+    assert swa.decode_workspace_bytes(cfg["B"], cfg["Hq"], cfg["W"], cfg["d"]) == 0
     q, kr, vr, pos = si.decode_inputs(4)
     out = swa.decode(to_device(q), to_device(kr), to_device(vr), torch.from_numpy(pos).cuda())
     torch.cuda.synchronize()
@@ -155,8 +158,9 @@ def test_decode_deterministic(swa):
 
 
 def test_workspace_reused_across_calls_and_shapes(swa):
-    """One zero-filled workspace serves consecutive calls of different sizes
-    (the arrival counters return to zero after every call)."""
+    """One workspace serves consecutive calls of different sizes: every
+    partial the merge reads is written by the same call, so nothing from an
+    earlier call is read and the workspace needs no clearing."""
     ws = swa.decode_workspace(8, 32, 4096, 128)
     for B, W in [(8, 4096), (3, 1000), (8, 4096), (1, 64)]:
         q, kr, vr, pos = si.decode_inputs(4, B=B, W=W, pos_lo=W // 2, pos_hi=3 * W)
@@ -167,3 +171,20 @@ def test_workspace_reused_across_calls_and_shapes(swa):
         assert torch.equal(reused, fresh), (B, W)
         ref = oracle.decode(q.values, kr.values, vr.values, pos, 1 / math.sqrt(128))
         assert_parity(to_f64(reused), ref, "bf16", "reused workspace B=%d W=%d" % (B, W))
+
+
+def test_decode_checks_out_before_launch(swa):
+    """A caller-supplied `out` of the wrong shape, or on another device, is
+    refused by the binding before anything is launched (the C ABI sees only
+    pointers)."""
+    q, kr, vr, pos = si.decode_inputs(4, B=2, W=256, pos_lo=300, pos_hi=900)
+    args = (to_device(q), to_device(kr), to_device(vr), torch.from_numpy(pos).cuda())
+    small = torch.empty((2, 31, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="shape"):
+        swa.decode(*args, out=small)
+    host = torch.empty((2, 32, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        swa.decode(*args, out=host)
+    ks = torch.zeros((2, 8, 4, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="shape"):
+        swa.decode_sinks(args[0], args[1], args[2], ks, ks.clone(), args[3], out=small)

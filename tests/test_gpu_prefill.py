@@ -168,17 +168,45 @@ def test_large_scores_force_rescaling(swa, dtype, scale, mode, T, W, d):
     if dtype == "bf16":
         assert_parity(got, ref, dtype, "large scores scale=%g mode=%d d=%d" % (scale, mode, d))
         return
-    # fp32: the exponent s*c - m*c (c = scale*log2 e) is formed in fp32 from
-    # terms as large as max|s*c|, so each probability carries a relative error
-    # up to about max|s*c| * 2^-23; the output error is bounded by that times
-    # max|v| (first order, both signs of the difference)
+    assert_fp32_exponent_bound(got, ref, q, k, v, scale, "large scores fp32")
+
+
+def assert_fp32_exponent_bound(got, ref, q, k, v, scale, what):
+    """fp32 parity for scores far outside the workloads' scale: the exponent
+    s*c - m*c (c = scale*log2 e) is formed in fp32 from terms as large as
+    max|s*c|, so each probability carries a relative error up to about
+    max|s*c| * 2^-23; the output error is bounded by that times max|v| (first
+    order, both signs of the difference)."""
+    G = q.values.shape[1] // k.values.shape[1]
     sc = np.abs(np.einsum("bhid,bhjd->bhij", q.values.astype(np.float64),
-                          np.repeat(k.values, 2, axis=1).astype(np.float64))).max()
+                          np.repeat(k.values, G, axis=1).astype(np.float64))).max()
     sc *= abs(scale) / np.log(2.0)
     tol = max(FP32_MAX_ABS, 2.0 * sc * 2.0 ** -23 * np.abs(v.values).max())
-    assert np.all(np.isfinite(got))
+    assert np.all(np.isfinite(got)), what
     err = float(np.max(np.abs(got - ref)))
-    assert err <= tol, "large scores fp32: max-abs %.3g > derived bound %.3g" % (err, tol)
+    print("%s: max-abs %.3g (derived bound %.3g)" % (what, err, tol))
+    assert err <= tol, "%s: max-abs %.3g > derived bound %.3g" % (what, err, tol)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("scale", [1000.0, -1024.0])
+@pytest.mark.parametrize("mode,T,W,d", [(0, 300, 100, 128), (1, 260, 90, 64), (0, 200, 20, 32),
+                                        (1, 150, 24, 64)])
+def test_largest_scale_is_a_hard_maximum(swa, dtype, scale, mode, T, W, d):
+    """At the largest scales the library accepts (|scale| <= 1024) the softmax
+    is one-hot on the row's largest (smallest, for a negative scale)
+    in-window score: the first visited keys jump the reference maximum by
+    thousands of log2 units, every later larger score again, and the output
+    row is that key's value row, with nothing non-finite."""
+    print("huge scale", dtype, scale, mode, T, W, d, flush=True)
+    q, k, v = small_inputs(950 + T + d, 1, 2, 1, T, d, dtype)
+    got = to_f64(run(swa, q, k, v, W, mode, scale=scale))
+    ref = oracle.attention_dense(q.values, k.values, v.values, W, mode, scale)
+    what = "scale %g mode=%d W=%d d=%d" % (scale, mode, W, d)
+    if dtype == "bf16":
+        assert_parity(got, ref, dtype, what)
+    else:  # the exponent's fp32 rounding, as for the rescaling test above
+        assert_fp32_exponent_bound(got, ref, q, k, v, scale, what)
 
 
 def test_deterministic(swa):
