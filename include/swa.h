@@ -228,6 +228,27 @@ int swa_decode(const void* q, const void* k_ring, const void* v_ring, const int3
                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * swa_decode_noalloc - swa_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).
+ *
+ * Same computation, arguments, layouts and errors as swa_decode, without the
+ * workspace: when the ring is split, the split partials go to a scratch
+ * array the library holds on each GPU (one copy per device, kept until the
+ * process ends, at most 4 MiB; every call on that device shares it).  The
+ * call allocates nothing and needs no initialisation; partials are written
+ * before the same call reads them.  Calls that overlap in time on one GPU
+ * (other streams, other threads) race on the scratch and give undefined
+ * outputs: serialise them.  A call whose partials would not fit returns
+ * SWA_ERR_UNSUPPORTED (no valid size does today: at most 4096 records of
+ * d + 2 floats); failing to find the scratch's device address returns
+ * SWA_ERR_LAUNCH.
+ */
+int swa_decode_noalloc(const void* q, const void* k_ring, const void* v_ring, const int32_t* pos,
+                       void* out, int B, int Hq, int Hkv, int W, int d, float scale, int dtype,
+                       void* stream);
+
+/*
  * swa_cache_append_chunk - append n consecutive tokens per sequence to the
  * ring cache.
  *

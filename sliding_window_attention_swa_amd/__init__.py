@@ -60,6 +60,8 @@ def load():
     lib.swa_cache_append.restype = i
     lib.swa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     lib.swa_decode.restype = i
+    lib.swa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.swa_decode_noalloc.restype = i
     lib.swa_cache_append_chunk.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
     lib.swa_cache_append_chunk.restype = i
     lib.swa_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
@@ -285,6 +287,35 @@ def decode(q, k_ring, v_ring, pos, scale=None, out=None, workspace=None, stream=
                            out.data_ptr(), B, Hq, Hkv, W, d, float(scale), _dtype_code(q),
                            ws_ptr, ws_bytes, _stream(stream))
     _raise("swa_decode", st)
+    return out
+
+
+def decode_noalloc(q, k_ring, v_ring, pos, scale=None, out=None, stream=None):
+    """decode without a workspace: the library's per-GPU scratch holds the
+    split partials (calls overlapping on one GPU race); returns out
+    [B, Hq, d].  Pass `out` to make the call allocate nothing at all."""
+    import torch
+    _check(q, "q", 3)
+    _check(k_ring, "k_ring", 4, q.dtype)
+    _check(v_ring, "v_ring", 4, q.dtype)
+    _check(pos, "pos", 1, torch.int32)
+    B, Hq, d = q.shape
+    Hkv, W = k_ring.shape[1], k_ring.shape[2]
+    if tuple(k_ring.shape) != (B, Hkv, W, d) or tuple(v_ring.shape) != tuple(k_ring.shape) \
+            or pos.shape[0] != B:
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", 3, q.dtype)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    _same_device(q=q, k_ring=k_ring, v_ring=v_ring, pos=pos, out=out)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = load().swa_decode_noalloc(q.data_ptr(), k_ring.data_ptr(), v_ring.data_ptr(),
+                                   pos.data_ptr(), out.data_ptr(), B, Hq, Hkv, W, d, float(scale),
+                                   _dtype_code(q), _stream(stream))
+    _raise("swa_decode_noalloc", st)
     return out
 
 

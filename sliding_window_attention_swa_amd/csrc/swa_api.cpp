@@ -262,6 +262,29 @@ int swa_decode(const void* q, const void* k_ring, const void* v_ring, const int3
   return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH;
 }
 
+int swa_decode_noalloc(const void* q, const void* k_ring, const void* v_ring, const int32_t* pos,
+                       void* out, int B, int Hq, int Hkv, int W, int d, float scale, int dtype,
+                       void* stream) {
+  if (!q || !k_ring || !v_ring || !pos || !out) return SWA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_ring) || !aligned16(v_ring) || !aligned16(pos) ||
+      !aligned16(out))
+    return SWA_ERR_INVALID_ARG;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || W <= 0) return SWA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return SWA_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return SWA_ERR_INVALID_ARG;
+  if (!supported_d(d) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
+  const size_t need = swa_decode_workspace_bytes(B, Hq, W, d);
+  if (need > swa::kDecodeScratchBytes) return SWA_ERR_UNSUPPORTED;
+  const int S = swa::decode_splits(B, Hq, W);
+  if ((long long)B * Hq * S > kMaxGrid) return SWA_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* ws = nullptr;
+  if (need > 0 && swa::decode_scratch(s, &ws) != hipSuccess) return SWA_ERR_LAUNCH;
+  hipError_t e = swa::launch_decode(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, d, scale, dtype,
+                                    ws, s);
+  return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH;
+}
+
 size_t swa_decode_sinks_workspace_bytes(int B, int Hq, int W, int d) {
   if (B <= 0 || Hq <= 0 || W <= 0 || !supported_d(d)) return 0;
   const int S = swa::decode_splits(B, Hq, W);

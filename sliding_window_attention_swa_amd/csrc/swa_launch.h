@@ -89,6 +89,15 @@ hipError_t launch_append(void* k_ring, void* v_ring, const int32_t* pos, const v
 // Number of slot chunks ("splits") the decode pass divides each ring into.
 int decode_splits(int B, int Hq, int W);
 
+// Size of the library-owned decode scratch (one per GPU): the split partials
+// of any swa_decode call fit (B*Hq*splits < 4096 records of d + 2 <= 130
+// floats whenever the ring is split at all).
+constexpr size_t kDecodeScratchBytes = (size_t)4 << 20;
+
+// Device address of the calling device's scratch (the device of `stream`,
+// or the current one for the null stream), looked up on first use.
+hipError_t decode_scratch(hipStream_t stream, float** ptr);
+
 hipError_t launch_decode(const void* q, const void* k_ring, const void* v_ring,
                          const int32_t* pos, void* out, int B, int Hq, int Hkv, int W, int d,
                          float scale, int dtype, float* workspace, hipStream_t stream);

@@ -35,6 +35,8 @@
 // (swa_prefill_bf16.hip) in the same partial layout, and the merge kernel's
 // GR = 1 instantiation writes them (launch_global_combine).
 
+#include <mutex>
+
 #include "swa_device.h"
 #include "swa_launch.h"
 
@@ -689,6 +691,44 @@ hipError_t launch_global_rows_f32(const void* q, const void* k, const void* v, c
   if (mode == 0)
     return launch_decode_e<float, 1>(q, k, v, gpos, out, ngl, Hq, Hkv, T, d, scale, workspace, stream);
   return launch_decode_e<float, 2>(q, k, v, gpos, out, ngl, Hq, Hkv, T, d, scale, workspace, stream);
+}
+
+// ------------------------------------------------- library-owned scratch
+
+// Split partials of swa_decode_noalloc, for callers that cannot allocate.
+// One copy per GPU (each device holds its own instance of the array, at its
+// own address) lives until the process ends.  Host code never passes the
+// array's name to a kernel or a copy: in host code it is a stand-in, not a
+// device address; the address comes from hipGetSymbolAddress, once per
+// device, with that device current.
+constexpr int kMaxScratchDevices = 64;
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
+namespace {
+std::mutex g_scratch_mu;
+float* g_scratch[kMaxScratchDevices];  // per device; null until first use
+}  // namespace
+
+hipError_t decode_scratch(hipStream_t stream, float** ptr) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return e;
+    if (back != hipSuccess) return back;
+    g_scratch[dev] = static_cast<float*>(p);
+  }
+  *ptr = g_scratch[dev];
+  return hipSuccess;
 }
 
 }  // namespace swa

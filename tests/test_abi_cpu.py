@@ -42,7 +42,7 @@ def test_headers_declare_the_entry_points():
         "swa_status_string", "swa_cache_append_chunk", "swa_prefill_chunk",
         "swa_prefill_dilated", "swa_prefill_global", "swa_prefill_global_workspace_bytes",
         "swa_prefill_dilated_global",
-        "swa_decode_sinks", "swa_decode_sinks_workspace_bytes"])
+        "swa_decode_sinks", "swa_decode_sinks_workspace_bytes", "swa_decode_noalloc"])
     # the calibration kernels compute nothing of the method: a header of their own
     assert declared_functions(HEADERS[1:]) == ["swa_calib_mfma_bf16", "swa_calib_stream_read"]
 
@@ -221,6 +221,33 @@ def decode(lib, q=P, kr=P, vr=P, pos=P, out=P, B=2, Hq=8, Hkv=2, W=4096, d=64, s
 ])
 def test_decode_rejects(lib, kw, status):
     assert decode(lib, **kw) == status
+
+
+def decode_noalloc(lib, q=P, kr=P, vr=P, pos=P, out=P, B=2, Hq=8, Hkv=2, W=4096, d=64,
+                   scale=0.125, dtype=1):
+    return lib.swa_decode_noalloc(q, kr, vr, pos, out, B, Hq, Hkv, W, d, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(kr=None), INVALID), (dict(vr=None), INVALID),
+    (dict(pos=None), INVALID), (dict(out=None), INVALID), (dict(q=MIS), INVALID),
+    (dict(out=MIS), INVALID), (dict(B=0), INVALID), (dict(Hq=0), INVALID), (dict(Hkv=-1), INVALID),
+    (dict(W=0), INVALID), (dict(Hq=6, Hkv=4), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(scale=1025.0), INVALID), (dict(d=16), UNSUPPORTED), (dict(dtype=5), UNSUPPORTED),
+])
+def test_decode_noalloc_rejects(lib, kw, status):
+    assert decode_noalloc(lib, **kw) == status
+
+
+def test_decode_noalloc_scratch_holds_every_split_decode(lib):
+    """The per-GPU scratch (4 MiB) holds the partials of any decode that
+    splits its ring: at most 4096 records of d + 2 floats."""
+    worst = 0
+    for B in (1, 2, 3, 5, 7, 16, 31, 64, 100, 511, 1023, 2047):
+        for Hq in (1, 2, 3, 4, 8):
+            for W in (65, 1000, 4096, 1 << 20):
+                worst = max(worst, lib.swa_decode_workspace_bytes(B, Hq, W, 128))
+    assert 0 < worst <= 4096 * 130 * 4 <= 4 << 20
 
 
 def decode_sinks(lib, q=P, kr=P, vr=P, ks=P, vs=P, S=4, pos=P, out=P, B=2, Hq=8, Hkv=2, W=64,
