@@ -214,7 +214,89 @@ def summarize_pmc_small(paths):
     return 0
 
 
+def pmc_config(wl):
+    """Counter workload of one prefill configuration: its kernel once after a
+    1 GiB read that evicts the L2s and the Infinity Cache, then once warm."""
+    import torch
+    import sliding_window_attention_swa_amd as swa
+    dev = torch.device("cuda:0")
+    swa.load()
+    c = si.WORKLOADS[wl]
+    q, k, v = (si.to_torch(t, dev) for t in si.prefill_inputs(wl))
+    out = torch.empty_like(q)
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    flush_max = torch.empty((), dtype=torch.int32, device=dev)
+    torch.amax(flush, dim=0, out=flush_max)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        swa.prefill_dilated(q, k, v, c["W"], c.get("dilation", 1), mode=c["mode"], out=out)
+        torch.cuda.synchronize()
+    print("pmc workload %d (%s) done" % (wl, c["name"]), flush=True)
+    return 0
+
+
+def summarize_config_counters(paths, wl):
+    """Per-dispatch SQ / TA counters of a --pmc-config run (the first, flushed
+    dispatch of the prefill kernel), with the derived issue and wait figures."""
+    import csv
+    c = si.WORKLOADS[wl]
+    per, dur, first = {}, {}, {}
+    for path in paths:  # one pass per file; a counter taken in several passes counts once
+        rows = [r for r in csv.DictReader(open(path)) if "prefill_" in r["Kernel_Name"]]
+        if not rows:
+            continue
+        d0 = min(int(r["Dispatch_Id"]) for r in rows)
+        mine = {}
+        for r in rows:
+            if int(r["Dispatch_Id"]) != d0:
+                continue
+            first[r["Counter_Name"]] = r["Kernel_Name"].split("(")[0]
+            mine[r["Counter_Name"]] = mine.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            dur[r["Counter_Name"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+        for k, v in mine.items():
+            per.setdefault(k, v)
+    if not per:
+        print("no prefill dispatch in the counter files", file=sys.stderr)
+        return 1
+    g = per.get
+    print("%s: kernel %s" % (c["name"], sorted(set(first.values()))))
+    for k in sorted(per):
+        print("  %-32s %.6g" % (k, per[k]))
+    t = max(dur.values())
+    print("  dispatch (under the profiler) %.1f us" % (t * 1e6))
+    # cycles of one XCD during the dispatch: GRBM_GUI_ACTIVE sums the 8 XCDs
+    # (it also counts the profiler's short window around the dispatch)
+    cycles = g("GRBM_GUI_ACTIVE") / N_XCD if g("GRBM_GUI_ACTIVE") else t * CLOCK_MAX_HZ
+    print("  cycles per XCD %.0f -> clock %.0f MHz during the dispatch" % (cycles, cycles / t / 1e6))
+    if g("SQ_VALU_MFMA_BUSY_CYCLES") is not None:
+        print("  MFMA busy %.1f%% of SIMD cycles"
+              % (100.0 * g("SQ_VALU_MFMA_BUSY_CYCLES") / (cycles * N_SIMD)))
+    if g("SQ_LDS_IDX_ACTIVE") is not None:
+        print("  LDS busy (indexed access) %.1f%% of CU cycles"
+              % (100.0 * g("SQ_LDS_IDX_ACTIVE") / (cycles * N_CU)))
+    if g("SQ_LDS_BANK_CONFLICT") is not None:
+        print("  LDS bank-conflict cycles %.3g" % g("SQ_LDS_BANK_CONFLICT"))
+    if g("SQ_WAVE_CYCLES"):
+        wc = g("SQ_WAVE_CYCLES")
+        for k in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                  "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_VMEM", "SQ_ACTIVE_INST_SCA"):
+            if g(k) is not None:
+                print("  %-22s %.1f%% of wave cycles" % (k, 100.0 * g(k) / wc))
+        if g("SQ_WAVES"):
+            print("  waves %d, average life %.0f cycles" % (g("SQ_WAVES"), wc / g("SQ_WAVES")))
+    if g("SQ_INSTS_VALU") and g("SQ_INSTS_MFMA"):
+        print("  VALU instructions per MFMA %.2f" % (g("SQ_INSTS_VALU") / g("SQ_INSTS_MFMA")))
+    if g("SQ_INSTS_VALU_TRANS_F32"):
+        exps = band_pairs(c["T"], c["W"], c["mode"], c.get("dilation", 1)) * c["Hq"] * c["B"] / 64.0
+        print("  transcendental instructions %.4g = %.3f x one exp per in-window score"
+              % (g("SQ_INSTS_VALU_TRANS_F32"), g("SQ_INSTS_VALU_TRANS_F32") / exps))
+    if g("SQ_LEVEL_WAVES") and g("SQ_BUSY_CYCLES"):
+        print("  waves resident on average %.0f" % (g("SQ_LEVEL_WAVES") / g("SQ_BUSY_CYCLES")))
+    return 0
+
+
 N_XCD, N_CU, N_SIMD = 8, 256, 1024  # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+CLOCK_MAX_HZ = 2.4e9  # MI355X's peak engine clock
 MFMA_FLOP_PER_SIMD_CYCLE = 1024  # v_mfma_f32_32x32x16_bf16: 32768 FLOP in 32 cycles
 
 
@@ -618,6 +700,12 @@ def main():
     ap.add_argument("--summarize-pmc-small", nargs="+", metavar="CSV",
                     help="HBM bytes of the --pmc-small configurations from FETCH_SIZE / "
                          "WRITE_SIZE counter CSVs")
+    ap.add_argument("--pmc-config", type=int, metavar="N",
+                    help="instead of the benchmark line: the counter workload of prefill "
+                         "configuration N (run under rocprofv3 --pmc)")
+    ap.add_argument("--summarize-config-counters", nargs="+", metavar="CSV",
+                    help="SQ counters of a --pmc-config run (with --config N)")
+    ap.add_argument("--config", type=int, default=5, help="configuration of the summary")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measurement of this GPU's sustained matrix and read rates "
                          "after the timed steps")
@@ -636,6 +724,10 @@ def main():
         return summarize_pmc_small(args.summarize_pmc_small)
     if args.pmc_small:
         return pmc_small()
+    if args.pmc_config:
+        return pmc_config(args.pmc_config)
+    if args.summarize_config_counters:
+        return summarize_config_counters(args.summarize_config_counters, args.config)
     if args.cpu_oracle:
         return cpu_oracle_configs()
     if args.all_configs or args.peaks:

@@ -67,6 +67,7 @@
 
 #include "swa_device.h"
 #include "swa_launch.h"
+#include "swa_tile_math.h"
 
 namespace swa {
 namespace {
@@ -81,6 +82,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;   // query rows per workgroup
 constexpr int kBN = 64;            // key rows per tile
+static_assert(kBM == tm::kBM && kBN == tm::kBN, "the tile arithmetic's block and tile sizes");
 // A row's accumulators are rescaled only when one of its probabilities
 // against the current reference maximum reaches 2^28 (a lane's partial block
 // sum reaches 2^32): until then every product term stays far from overflow
@@ -174,7 +176,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   }
   const int h = kvh * G + hg;
   // T rows of stride RS elements: the sequence itself, or one residue class
-  const int T = kDil ? (Tseq - cls + dil - 1) / dil : Tseq;
+  const int T = kDil ? tm::class_rows(Tseq, cls, dil) : Tseq;
   const int RS = kDil ? dil * D : D;
 
   const int tid = threadIdx.x;
@@ -217,27 +219,27 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   const int hw = W >> 1;
   int lo, hi;
   if (kCausal) {
-    lo = max(-pstart, q0 - W + 1);
-    hi = min(T - 1, q0 + kBM - 1);
+    lo = SWA_TM_CAUSAL_BLOCK_LO(q0, W, pstart);
+    hi = SWA_TM_CAUSAL_BLOCK_HI(q0, T);
   } else {
-    lo = max(0, q0 - hw);
-    hi = min(T - 1, q0 + kBM - 1 + hw);
+    lo = SWA_TM_SYM_BLOCK_LO(q0, hw);
+    hi = SWA_TM_SYM_BLOCK_HI(q0, T, hw);
   }
   int kt0;
   if constexpr (kChunk) {
-    kt0 = lo >= 0 ? lo / kBN : -((kBN - 1 - lo) / kBN);  // floor division
+    kt0 = tm::floor_tile(lo);  // floor division
   } else {
     kt0 = lo / kBN;
   }
   const int kt1 = hi / kBN;
   // global modes: the global key tiles follow the window's, as kt1+1 .. kt_end
-  const int kt_end = kGlobal ? kt1 + (ngl + kBN - 1) / kBN : kt1;
+  const int kt_end = kGlobal ? tm::global_tiles_end(kt1, ngl) : kt1;
 
   // this wave's rows and key range
   const bool wave_active = qw0 < T;
-  const int qlast = min(qw0 + 31, T - 1);
-  const int wlo = kCausal ? max(-pstart, qw0 - W + 1) : max(0, qw0 - hw);
-  const int whi = kCausal ? qlast : min(T - 1, qlast + hw);
+  const int qlast = SWA_TM_WAVE_LAST(qw0, T);
+  const int wlo = SWA_TM_WAVE_LO(kCausal, qw0, W, hw, pstart);
+  const int whi = SWA_TM_WAVE_HI(kCausal, qlast, T, hw);
 
   // ---- Q rows as B operands, zero beyond the sequence; a negative scale is
   // folded into Q's sign bits (exact) so that c > 0 below.
@@ -262,10 +264,10 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   int src_off[NLD], src_row[NLD];
 #pragma unroll
   for (int j = 0; j < NLD; ++j) {
-    const int o = (j * kThreads + tid) * 16;
-    const int row = o / ROWB;
+    const int o = tm::load_lds_offset(j, tid, kThreads);
+    const int row = tm::load_row(o, ROWB);
     src_row[j] = row;
-    src_off[j] = (((o % ROWB) / 16) ^ swz<D>(row)) * 16;
+    src_off[j] = (tm::load_chunk(o, ROWB) ^ swz<D>(row)) * 16;
   }
   auto load_tile = [&](char* Kdst, char* Vdst, int kt) __attribute__((always_inline)) {
     const int kbase = kt * kBN;
@@ -277,7 +279,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
         const int t0 = (kt - kt1 - 1) * kBN;
         // the tile's 64 global positions, for the mask (same stage discipline
         // as the K/V tiles: written after the barrier that frees the stage)
-        if (tid < kBN) lds_gp[(kt - kt0) & 1][tid] = gpos[min(t0 + tid, ngl - 1)];
+        if (tid < kBN) lds_gp[(kt - kt0) & 1][tid] = gpos[tm::global_index(t0, tid, ngl)];
         const __amdgpu_buffer_rsrc_t rk =
             __builtin_amdgcn_make_buffer_rsrc((void*)kg, 0, Tseq * ROWB, kBufferFlags);
         const __amdgpu_buffer_rsrc_t rv =
@@ -285,7 +287,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
 #pragma unroll
         for (int j = 0; j < NLD; ++j) {
           const int wbase = (j * kThreads + wave * 64) * 16;
-          const int gp = min(max(gpos[min(t0 + src_row[j], ngl - 1)], 0), Tseq - 1);
+          const int gp = tm::global_src_row(gpos[tm::global_index(t0, src_row[j], ngl)], Tseq);
           const int off = gp * ROWB + src_off[j];
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass mishandles this builtin
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(Kdst + wbase), 16, off, 0, 0, 0);
@@ -309,7 +311,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
 #pragma unroll
         for (int j = 0; j < NLD; ++j) {
           const int wbase = (j * kThreads + wave * 64) * 16;
-          const unsigned slot = (unsigned)max(pstart + kbase + src_row[j], 0) % (unsigned)W;
+          const unsigned slot = tm::ring_slot(pstart, kbase, src_row[j], W);
           const int off = (int)slot * ROWB + src_off[j];
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass mishandles this builtin
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(Kdst + wbase), 16, off, 0, 0, 0);
@@ -321,11 +323,11 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
         return;
       }
     }
-    const int last = T - 1 - kbase;  // last valid row of this tile
-    const int RSB = RS * 2;           // bytes between consecutive rows
+    const int last = tm::tile_last(T, kt);  // last valid row of this tile
+    const int RSB = RS * 2;                  // bytes between consecutive rows
     // the resource starts at the tile and ends after its last valid row
     // (at most 64 rows: the size stays far inside int32 at any T)
-    const int bytes = min(last, kBN - 1) * RSB + ROWB;
+    const int bytes = tm::tile_bytes(last, RSB, ROWB);
     const __amdgpu_buffer_rsrc_t rk =
         __builtin_amdgcn_make_buffer_rsrc((void*)(kh + (size_t)kbase * RS), 0, bytes, kBufferFlags);
     const __amdgpu_buffer_rsrc_t rv =
@@ -333,7 +335,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       const int wbase = (j * kThreads + wave * 64) * 16;
-      const int off = min(src_row[j], last) * RSB + src_off[j];
+      const int off = tm::tile_row_offset(src_row[j], last, RSB) + src_off[j];
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass mishandles this builtin
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(Kdst + wbase), 16, off, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(Vdst + wbase), 16, off, 0, 0, 0);
@@ -462,13 +464,13 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   // end runs the same schedule; key k0 + kc counts for this lane's row when
   // mlo <= kc - 4 * half <= mhi, tested on each score block before its
   // probabilities.
-  auto interior_tile = [&](const char* Ks, const char* Vs, auto masked, int mlo, int mhi) __attribute__((always_inline)) {
+  auto interior_tile = [&](const char* Ks, const char* Vs, auto masked, tm::SymRange mr) __attribute__((always_inline)) {
     constexpr bool kMasked = decltype(masked)::value;
     auto mask_block = [&](f32x16& sb, int mb) __attribute__((always_inline)) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kc = mb * 32 + 8 * (r >> 2) + (r & 3);
-        if (kc < mlo || kc > mhi) sb[r] = -INFINITY;
+        if (!tm::sym_visible(mr, kc)) sb[r] = -INFINITY;
       }
     };
     // S for keys 0..31: all K operands requested up front
@@ -556,14 +558,14 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
       // 0 <= diff <= min(W - 1, qi) with diff = qi - key (keys >= 0; keys < T
       // follow for a row inside the sequence, and rows past T are never
       // stored)
-      const unsigned span = (unsigned)min(W - 1, qi);
+      const unsigned span = tm::causal_edge_span(qi, W);
       const int d0 = qi - k0;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kc = mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);  // key - k0
-          if (!((unsigned)(d0 - kc) <= span)) s[mb][r] = -INFINITY;
+          if (!tm::causal_edge_visible(d0, kc, span)) s[mb][r] = -INFINITY;
         }
       }
     } else {
@@ -575,14 +577,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          const int diff = qi - key;
-          bool ok = key < T;
-          if (kCausal) {
-            ok = ok && diff >= 0 && diff < W && key >= -pstart;
-          } else {
-            ok = ok && diff >= -hw && diff <= hw;
-          }
-          if (!ok) s[mb][r] = -INFINITY;
+          if (!tm::edge_visible(kCausal, qi, key, T, W, pstart)) s[mb][r] = -INFINITY;
         }
       }
     }
@@ -620,17 +615,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int idx = t0 + 8 * g + 4 * half + e;
-        const int gp = gpv[e];
-        const int diff = rpos - gp;
-        bool in_window;
-        if constexpr (kDil) {  // on the row's grid, within the window's offsets
-          const int m = diff / dil;
-          in_window = diff == m * dil && (kCausal ? (m >= 0 && m < W) : (m >= -hw && m <= hw));
-        } else {
-          in_window = kCausal ? (diff >= 0 && diff < W) : (diff >= -hw && diff <= hw);
-        }
-        bool ok = idx < ngl && gp >= 0 && gp < Tseq && !in_window;
-        if (kCausal) ok = ok && diff >= 0;
+        const bool ok = tm::global_counts(kCausal, kDil, rpos, gpv[e], idx, ngl, Tseq, W, dil);
         okbits |= (uint32_t)ok << (4 * g + e);
       }
     }
@@ -667,21 +652,13 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     __syncthreads();
     if (kt < kt_end) load_tile(Kn, Vn, kt + 1);
     const int k0 = kt * kBN;
-    if (!(wave_active && k0 <= whi && k0 + kBN - 1 >= wlo)) return;
-    bool full;
-    if (kCausal) {
-      full = (k0 + kBN - 1 <= qw0) && (k0 >= qlast - W + 1) && (k0 + kBN <= T);
-      if (kChunk) full = full && k0 >= -pstart;
-    } else {
-      full = (k0 >= qlast - hw) && (k0 + kBN - 1 <= qw0 + hw) && (k0 + kBN <= T);
-    }
+    if (!tm::tile_visited(wave_active, wlo, whi, k0)) return;
+    const bool full = tm::tile_full(kCausal, kChunk, k0, qw0, qlast, T, W, pstart);
     if (full) {
-      interior_tile(Ks, Vs, std::false_type{}, 0, 0);
+      interior_tile(Ks, Vs, std::false_type{}, tm::SymRange{0, 0});
     } else if constexpr (!kCausal) {
       // symmetric: keys k0 + kc with qi - hw <= k0 + kc <= min(qi + hw, T - 1)
-      const int mlo = qi - hw - k0 - 4 * half;
-      const int mhi = min(qi + hw, T - 1) - k0 - 4 * half;
-      interior_tile(Ks, Vs, std::true_type{}, mlo, mhi);
+      interior_tile(Ks, Vs, std::true_type{}, tm::sym_range(qi, k0, half, T, W));
     } else {
       edge_tile(Ks, Vs, k0);
     }
@@ -796,8 +773,9 @@ void prefill_short_kernel(
   // inside the sequence (blo) and covers at most its 64 rows, so offsets stay
   // small at any T.
   {
-    const int blo = max(kb0, 0);
-    const int bhi = min(kb0 + 63, T - 1);
+    const tm::ShortBlock sbk = tm::short_block(qw0, kShortOff<MODE>, T);
+    const int blo = sbk.blo;
+    const int bhi = sbk.bhi;
     const __bf16* kblk = k + ((size_t)kvh * T + blo) * D;
     const __bf16* vblk = v + ((size_t)kvh * T + blo) * D;
     const __amdgpu_buffer_rsrc_t rk =
@@ -809,7 +787,7 @@ void prefill_short_kernel(
       const int j = wave * (NL / NW) + jj;
       const int o = (64 * j + lane) * 16;
       const int row = o / ROWB;
-      const int src = min(max(kb0 + row, blo), bhi);
+      const int src = tm::short_src_row(sbk, row);
       const int off = (src - blo) * ROWB + ((((o % ROWB) / 16) ^ swz<D>(row)) * 16);
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass mishandles this builtin
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(lds_k + 64 * j * 16), 16, off, 0, 0, 0);
@@ -854,18 +832,14 @@ void prefill_short_kernel(
   // a row inside the sequence; rows past T are never stored).  A symmetric
   // row far past T gets dlo > dhi: the span wraps and keeps every score of its
   // clamped, finite rows.
-  const int hw = W >> 1;
-  const int dlo = MODE == 0 ? 0 : max(-hw, qi - T + 1);
-  const int dhi = MODE == 0 ? min(W - 1, qi) : min(hw, qi);
-  const unsigned span = (unsigned)(dhi - dlo);
-  const int d0 = qi - kb0 - dlo;  // diff - dlo of key kb0
+  const tm::ShortMask smk = tm::short_mask(MODE == 0, qi, kb0, T, W);
   float mx = -INFINITY;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kc = mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);  // key - kb0
-      if (!((unsigned)(d0 - kc) <= span)) s[mb][r] = -INFINITY;
+      if (!tm::short_visible(smk, kc)) s[mb][r] = -INFINITY;
       mx = fmaxf(mx, s[mb][r]);
     }
   }
@@ -1104,9 +1078,9 @@ void global_rows_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     h = kvh * G + pi % G;
     if (gp < 0 || gp >= T) gp = -1;
   }
-  const int s0 = split * kGRowKeys;
-  const int s1 = min(T, s0 + kGRowKeys);
-  const int lim = gp < 0 ? -1 : min(MODE == 0 ? gp : T - 1, s1 - 1);  // last key of the row
+  const int s0 = tm::grow_split_begin(split, kGRowKeys);
+  const int s1 = tm::grow_split_end(split, kGRowKeys, T);
+  const int lim = tm::grow_row_limit(MODE == 0, gp, T, s1);  // last key of the row
   // the wave stops after the last key any of its rows sees
   int wlim = lim;
 #pragma unroll
@@ -1150,7 +1124,7 @@ void global_rows_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     for (int j = 0; j < NL; ++j) {
       const int o16 = (64 * j + lane) * 16;
       const int row = o16 / ROWB;
-      const int off = min(k0 + row, T - 1) * ROWB + ((((o16 % ROWB) / 16) ^ swz<D>(row)) * 16);
+      const int off = tm::grow_src_row(k0, row, T) * ROWB + ((((o16 % ROWB) / 16) ^ swz<D>(row)) * 16);
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass mishandles this builtin
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(lds_k + 64 * j * 16), 16, off, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(lds_v + 64 * j * 16), 16, off, 0, 0, 0);
