@@ -90,20 +90,23 @@ def read_traffic(prefix, source):
         return None
 
 
-def source_hash(name):
-    """SHA-256 of a kernel source's code: comments and whitespace removed, so
-    that an edit of the comments alone keeps the measured traffic valid."""
+def source_hash(names):
+    """SHA-256 of a kernel's source files' code: comments and whitespace
+    removed, so that an edit of the comments alone keeps the measured figures
+    valid."""
     import hashlib
     import re
-    p = os.path.join(ROOT, "sliding_window_attention_swa_amd", "csrc", name)
-    text = open(p, encoding="utf-8").read()
+    text = ""
+    for name in names:
+        p = os.path.join(ROOT, "sliding_window_attention_swa_amd", "csrc", name)
+        text += open(p, encoding="utf-8").read() + "\n"
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
     return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
 
 
-PREFILL_SOURCE = "swa_prefill_bf16.hip"
-DECODE_SOURCE = "swa_ring.hip"
+PREFILL_SOURCE = ("swa_prefill_bf16.hip", "swa_tile_math.h")
+DECODE_SOURCE = ("swa_ring.hip",)
 
 
 def summarize_pmc(paths):
@@ -250,7 +253,7 @@ def summarize_config_counters(paths, wl):
         for r in rows:
             if int(r["Dispatch_Id"]) != d0:
                 continue
-            first[r["Counter_Name"]] = r["Kernel_Name"].split("(")[0]
+            first[r["Counter_Name"]] = short_kernel_name(r["Kernel_Name"])
             mine[r["Counter_Name"]] = mine.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
             dur[r["Counter_Name"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
         for k, v in mine.items():
@@ -260,6 +263,7 @@ def summarize_config_counters(paths, wl):
         return 1
     g = per.get
     print("%s: kernel %s" % (c["name"], sorted(set(first.values()))))
+    print("counters_kernel_sha256: %s" % source_hash(PREFILL_SOURCE))
     for k in sorted(per):
         print("  %-32s %.6g" % (k, per[k]))
     t = max(dur.values())
@@ -295,6 +299,71 @@ def summarize_config_counters(paths, wl):
     return 0
 
 
+def _short_mangled(name):
+    """name<args> of a mangled kernel of this library: nested length-prefixed
+    identifiers, then template arguments that are integers (Li128E) or the
+    element types bf16 (DF16b) and float (f)."""
+    import re
+    i, parts = 3, []
+    while i < len(name) and name[i].isdigit():
+        n = re.match(r"\d+", name[i:]).group(0)
+        i += len(n)
+        parts.append(name[i:i + int(n)])
+        i += int(n)
+    if not parts:
+        return None
+    args = []
+    if name[i:i + 1] == "I":
+        i += 1
+        while i < len(name) and name[i] != "E":
+            m = re.match(r"L[a-z](-?\d+)E|(DF16b)|([fb])", name[i:])
+            if not m:
+                return None
+            args.append(m.group(1) or {"DF16b": "bf16", "f": "float", "b": "bool"}[m.group(2) or m.group(3)])
+            i += len(m.group(0))
+    return parts[-1] + ("<%s>" % ", ".join(args) if args else "")
+
+
+def short_kernel_name(name):
+    """A kernel's name without namespaces, return type and parameter list
+    (demangled first when the trace left it mangled)."""
+    if name.startswith("_ZN"):
+        name = _short_mangled(name) or name
+    name = name.replace("(anonymous namespace)::", "")
+    name = name.split("(")[0]
+    if name.startswith("void "):
+        name = name[5:]
+    return name.replace("swa::", "").replace("at::native::", "")
+
+
+def summarize_kernel_trace(paths, skip):
+    """Per-kernel durations from a rocprofv3 --kernel-trace CSV of a benchmark
+    run, without the first `skip` dispatches of each kernel (the untimed
+    warm-up steps): the calls the timed region made."""
+    import csv
+    calls = {}
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            name = short_kernel_name(r["Kernel_Name"])
+            t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+            calls.setdefault(name, []).append((t0, (t1 - t0) * 1e-3))
+    rows = []
+    for name, cs in calls.items():
+        cs.sort()
+        us = [u for _, u in cs[skip:]]
+        if us:
+            rows.append((sum(us), name, len(us), sum(us) / len(us), min(us), max(us)))
+    if not rows:
+        print("no kernel dispatches after the warm-ups", file=sys.stderr)
+        return 1
+    total = sum(r[0] for r in rows)
+    print("| kernel | calls | average (us) | min (us) | max (us) | share |")
+    print("|---|---|---|---|---|---|")
+    for tot, name, n, avg, lo, hi in sorted(rows, reverse=True):
+        print("| %s | %d | %.1f | %.1f | %.1f | %.1f%% |" % (name, n, avg, lo, hi, 100.0 * tot / total))
+    return 0
+
+
 N_XCD, N_CU, N_SIMD = 8, 256, 1024  # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
 CLOCK_MAX_HZ = 2.4e9  # MI355X's peak engine clock
 MFMA_FLOP_PER_SIMD_CYCLE = 1024  # v_mfma_f32_32x32x16_bf16: 32768 FLOP in 32 cycles
@@ -318,6 +387,7 @@ def summarize_counters(paths):
     if "prefill" not in dur:
         print("no prefill dispatch in the counter files", file=sys.stderr)
         return 1
+    print("counters_kernel_sha256: %s" % source_hash(PREFILL_SOURCE))
     for kind in ("prefill", "decode"):
         if kind not in dur:
             continue
@@ -706,6 +776,9 @@ def main():
     ap.add_argument("--summarize-config-counters", nargs="+", metavar="CSV",
                     help="SQ counters of a --pmc-config run (with --config N)")
     ap.add_argument("--config", type=int, default=5, help="configuration of the summary")
+    ap.add_argument("--summarize-kernel-trace", nargs="+", metavar="CSV",
+                    help="per-kernel times of a rocprofv3 --kernel-trace run of the benchmark "
+                         "line, without the --warmup steps' dispatches")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measurement of this GPU's sustained matrix and read rates "
                          "after the timed steps")
@@ -728,6 +801,8 @@ def main():
         return pmc_config(args.pmc_config)
     if args.summarize_config_counters:
         return summarize_config_counters(args.summarize_config_counters, args.config)
+    if args.summarize_kernel_trace:
+        return summarize_kernel_trace(args.summarize_kernel_trace, args.warmup)
     if args.cpu_oracle:
         return cpu_oracle_configs()
     if args.all_configs or args.peaks:

@@ -448,6 +448,17 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     p[1] = __builtin_bit_cast(bf16x8, w1);
   };
 
+  // symmetric windows: key k0 + kc (kc = 32 * mb + 8 * (r / 4) + 4 * half +
+  // r % 4 for score register r of block mb) counts for this lane's row when
+  // mlo <= kc - 4 * half <= mhi
+  auto mask_block = [&](f32x16& sb, int mb, const tm::SymRange& mr) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kc = mb * 32 + 8 * (r >> 2) + (r & 3);
+      if (!tm::sym_visible(mr, kc)) sb[r] = -INFINITY;
+    }
+  };
+
   // A tile inside every row's window.  Three regions, each mixing matrix and
   // vector work so that one wave keeps both busy:
   //   A: S of keys 32..63        | probabilities of keys 0..31
@@ -461,18 +472,12 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   // priority).
   //
   // Masked (symmetric windows): a tile crossing a window edge or the sequence
-  // end runs the same schedule; key k0 + kc counts for this lane's row when
-  // mlo <= kc - 4 * half <= mhi, tested on each score block before its
-  // probabilities.
+  // end runs the same schedule, with a mask on each 32-key block that some
+  // rows see only in part (bit b of the mask set: block b); key k0 + kc
+  // counts for this lane's row when mlo <= kc - 4 * half <= mhi, tested on
+  // the block's scores before their probabilities.
   auto interior_tile = [&](const char* Ks, const char* Vs, auto masked, tm::SymRange mr) __attribute__((always_inline)) {
-    constexpr bool kMasked = decltype(masked)::value;
-    auto mask_block = [&](f32x16& sb, int mb) __attribute__((always_inline)) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kc = mb * 32 + 8 * (r >> 2) + (r & 3);
-        if (!tm::sym_visible(mr, kc)) sb[r] = -INFINITY;
-      }
-    };
+    constexpr int kMask = decltype(masked)::value;
     // S for keys 0..31: all K operands requested up front
     bf16x8 ka[KS];
 #pragma unroll
@@ -493,7 +498,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     f32x16 s1 = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], s1, 0, 0, 0);
-    if constexpr (kMasked) mask_block(s0, 0);
+    if constexpr ((kMask & 1) != 0) mask_block(s0, 0, mr);
     probs(s0, -m_ref * c, p0, l0);
     pin(p0, l0);
     __builtin_amdgcn_sched_group_barrier(0x100, KS / 2, 0);
@@ -513,7 +518,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(Vs, md, kk), p0[kk], o[md], 0, 0, 0);
     }
-    if constexpr (kMasked) mask_block(s1, 1);
+    if constexpr ((kMask & 2) != 0) mask_block(s1, 1, mr);
     probs(s1, -m_ref * c, p1, l1);
     pin(p1, l1);
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -541,6 +546,26 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
       if (i < 2 * MD - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // A symmetric tile of whose two 32-key blocks the wave's rows see only one
+  // (block MB): that block alone, masked.
+  auto block_tile = [&](const char* Ks, const char* Vs, auto mbc, tm::SymRange mr) __attribute__((always_inline)) {
+    constexpr int MB = decltype(mbc)::value;
+    f32x16 sb = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(Ks, MB, ks), qf[ks], sb, 0, 0, 0);
+    mask_block(sb, MB, mr);
+    bf16x8 pb[2];
+    float lb;
+    probs(sb, -m_ref * c, pb, lb);
+    if (raise_max(&sb, 1, lb)) probs(sb, -m_ref * c, pb, lb);
+    l_part += lb;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(Vs, md, 2 * MB + kk), pb[kk], o[md], 0, 0, 0);
+    }
   };
 
   // A tile that crosses a window edge or the sequence end: mask, then the
@@ -655,10 +680,28 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     if (!tm::tile_visited(wave_active, wlo, whi, k0)) return;
     const bool full = tm::tile_full(kCausal, kChunk, k0, qw0, qlast, T, W, pstart);
     if (full) {
-      interior_tile(Ks, Vs, std::false_type{}, tm::SymRange{0, 0});
-    } else if constexpr (!kCausal) {
+      interior_tile(Ks, Vs, std::integral_constant<int, 0>{}, tm::SymRange{0, 0});
+    } else if constexpr (!kCausal && !tm::sym_blocks_classified(D)) {
       // symmetric: keys k0 + kc with qi - hw <= k0 + kc <= min(qi + hw, T - 1)
-      interior_tile(Ks, Vs, std::true_type{}, tm::sym_range(qi, k0, half, T, W));
+      interior_tile(Ks, Vs, std::integral_constant<int, 3>{}, tm::sym_range(qi, k0, half, T, W));
+    } else if constexpr (!kCausal) {
+      // symmetric: keys k0 + kc with qi - hw <= k0 + kc <= min(qi + hw, T - 1);
+      // each 32-key block is skipped, taken whole or masked, as the wave's
+      // rows see it (the classes are uniform over the wave)
+      const tm::SymRange mr = tm::sym_range(qi, k0, half, T, W);
+      const int c0 = tm::sym_block_class(k0, qw0, qlast, T, W);
+      const int c1 = tm::sym_block_class(k0 + 32, qw0, qlast, T, W);
+      if (c1 == tm::kSymNone) {
+        block_tile(Ks, Vs, std::integral_constant<int, 0>{}, mr);
+      } else if (c0 == tm::kSymNone) {
+        block_tile(Ks, Vs, std::integral_constant<int, 1>{}, mr);
+      } else if (c0 == tm::kSymAll) {
+        interior_tile(Ks, Vs, std::integral_constant<int, 2>{}, mr);
+      } else if (c1 == tm::kSymAll) {
+        interior_tile(Ks, Vs, std::integral_constant<int, 1>{}, mr);
+      } else {
+        interior_tile(Ks, Vs, std::integral_constant<int, 3>{}, mr);
+      }
     } else {
       edge_tile(Ks, Vs, k0);
     }

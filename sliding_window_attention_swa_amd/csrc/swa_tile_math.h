@@ -119,6 +119,22 @@ SWA_HD SymRange sym_range(int qi, int k0, int half, int T, int W) {
 }
 SWA_HD bool sym_visible(const SymRange& m, int kc) { return !(kc < m.mlo || kc > m.mhi); }
 
+// Symmetric windows: how the wave's rows [qw0, qlast] see the 32-key block
+// starting at key kb.  kSymNone: no row sees any of its keys (the block is
+// skipped); kSymAll: every row sees every key, all inside the sequence (no
+// mask); kSymSome: anything else (masked per score).
+// The kernels classify blocks at head sizes of 64 and more; at 32 the extra
+// tile variants exceed the register budget of five waves per SIMD, and both
+// blocks of an edge tile are masked.
+constexpr int kSymNone = 0, kSymSome = 1, kSymAll = 2;
+constexpr bool sym_blocks_classified(int D) { return D >= 64; }
+SWA_HD int sym_block_class(int kb, int qw0, int qlast, int T, int W) {
+  const int hw = W >> 1;
+  if (kb + 31 < imax(0, qw0 - hw) || kb > imin(T - 1, qlast + hw)) return kSymNone;
+  if (kb >= qlast - hw && kb + 31 <= qw0 + hw && kb + 32 <= T) return kSymAll;
+  return kSymSome;
+}
+
 // Window tile kt of a sequence (or residue class) of T rows, RSB bytes from
 // one row to the next and ROWB bytes per row: the buffer resource starts at
 // the tile's first row and ends after its last valid row (at most 64 rows);

@@ -141,8 +141,73 @@ def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
     f = d / "k.hip"
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     f.write_text("int a = 1;  // one\n/* block\n comment */ int b = a + 2;\n")
-    h0 = bench.source_hash("k.hip")
+    h0 = bench.source_hash(("k.hip",))
     f.write_text("int a = 1;  // another comment\n\nint b = a + 2;  /* x */\n")
-    assert bench.source_hash("k.hip") == h0
+    assert bench.source_hash(("k.hip",)) == h0
     f.write_text("int a = 1;\nint b = a + 3;\n")
-    assert bench.source_hash("k.hip") != h0
+    assert bench.source_hash(("k.hip",)) != h0
+
+
+def test_source_hash_covers_every_file(tmp_path, monkeypatch):
+    """The prefill's figures are tied to the kernel and its index header."""
+    d = tmp_path / "sliding_window_attention_swa_amd" / "csrc"
+    d.mkdir(parents=True)
+    (d / "k.hip").write_text("int a = 1;\n")
+    (d / "h.h").write_text("int b = 2;\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0 = bench.source_hash(("k.hip", "h.h"))
+    (d / "h.h").write_text("int b = 3;\n")
+    assert bench.source_hash(("k.hip", "h.h")) != h0
+    assert "swa_tile_math.h" in bench.PREFILL_SOURCE
+
+
+def test_kernel_trace_summary_drops_the_warmups(tmp_path, capsys):
+    """Three warm-up dispatches of 2000 us, then timed ones of 1000 and
+    1010 us: only the timed ones are averaged."""
+    f = tmp_path / "run_kernel_trace.csv"
+    rows = ["Kernel_Name,Start_Timestamp,End_Timestamp"]
+    t = 0
+    for us in (2000, 2000, 2000, 1000, 1010):
+        rows.append('"void swa::prefill_bf16_kernel<128, 0>(args)",%d,%d' % (t, t + us * 1000))
+        rows.append('"append_kernel(args)",%d,%d' % (t + 3_000_000, t + 3_004_000))
+        t += 10_000_000
+    f.write_text("\n".join(rows) + "\n")
+    assert bench.summarize_kernel_trace([str(f)], 3) == 0
+    out = capsys.readouterr().out
+    line = [l for l in out.splitlines() if "prefill_bf16_kernel" in l][0]
+    cells = [c.strip() for c in line.split("|")]
+    assert cells[2] == "2" and cells[3] == "1005.0" and cells[5] == "1010.0"
+
+
+def test_config_counter_summary_counts_a_repeated_counter_once(tmp_path, capsys):
+    """GRBM_GUI_ACTIVE in each of three passes: the clock comes from one of
+    them (2.0 GHz over a 50 us dispatch), and only the first dispatch of the
+    prefill kernel in a file is read."""
+    cycles = 2.0e9 * 50e-6
+    paths = []
+    for i, extra in enumerate(("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA")):
+        f = tmp_path / ("p%d.csv" % i)
+        lines = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value,Start_Timestamp,End_Timestamp"]
+        for disp, scale in ((7, 1.0), (8, 5.0)):
+            lines.append("%d,prefill_bf16_kernel<64>(x),GRBM_GUI_ACTIVE,%f,0,50000"
+                         % (disp, scale * cycles * bench.N_XCD))
+            lines.append("%d,prefill_bf16_kernel<64>(x),%s,%f,0,50000" % (disp, extra, 100.0 * (i + 1) * scale))
+        f.write_text("\n".join(lines) + "\n")
+        paths.append(str(f))
+    assert bench.summarize_config_counters(paths, 5) == 0
+    out = capsys.readouterr().out
+    assert "clock 2000 MHz" in out
+    assert "VALU instructions per MFMA 0.67" in out
+
+
+def test_short_names_of_mangled_kernels():
+    """Kernel traces may leave this library's kernels mangled (anonymous
+    namespace, bf16 template arguments)."""
+    f = bench.short_kernel_name
+    assert f("_ZN3swa12_GLOBAL__N_119prefill_bf16_kernelILi128ELi0EEEvPKDF16bS3_S3_PDF16bii") == \
+        "prefill_bf16_kernel<128, 0>"
+    assert f("_ZN3swa12_GLOBAL__N_119decode_split_kernelIDF16bLi128ELi4ELi0EEEvPKT_S4_") == \
+        "decode_split_kernel<bf16, 128, 4, 0>"
+    assert f("swa::(anonymous namespace)::append_kernel(HIP_vector_type<unsigned int, 4u>*, int)") == \
+        "append_kernel"
+    assert f("void at::native::fill_kernel<16>(int)") == "fill_kernel<16>"

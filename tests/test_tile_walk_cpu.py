@@ -100,6 +100,16 @@ def test_plain_windows_tiled(walker):
         check(r, expect_rows(oracle.window_mask(T, W, m)), ("tiled", m, T, W, D))
 
 
+def test_symmetric_block_classes_every_alignment(walker):
+    """Symmetric edge tiles skip, take whole or mask each 32-key block: half
+    windows of every residue mod 32 (and both parities of W), sequence ends
+    inside and at block boundaries."""
+    shapes = [(T, W) for T in (96, 129, 300) for W in range(2, 140)]
+    res = run(walker, ["tiled 1 %d %d 1 0 64 0" % (T, W) for T, W in shapes])
+    for (T, W), r in zip(shapes, res):
+        check(r, expect_rows(oracle.window_mask(T, W, SYMMETRIC)), ("sym blocks", T, W))
+
+
 def test_short_window_kernel(walker):
     """The short-window kernel (causal W <= 33, symmetric W/2 <= 16; any W
     is walked): each row's 64-key block holds its whole window."""

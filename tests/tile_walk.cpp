@@ -152,13 +152,27 @@ void walk_tiled(int MODE, int Tseq, int W, int dil, int pstart, int D, const std
             const int k0 = kt * tw::kBN;
             if (!tw::tile_visited(wave_active, wlo, whi, k0)) continue;
             const bool full = tw::tile_full(kCausal, kChunk, k0, qw0, qlast, T, W, pstart);
+            // symmetric edge tiles: the class of each 32-key block, as the
+            // kernel branches on it (a block no row sees is skipped, a block
+            // every row sees is taken unmasked)
+            int cls_blk[2] = {tw::kSymSome, tw::kSymSome};
+            if (!full && !kCausal && tw::sym_blocks_classified(D)) {
+              cls_blk[0] = tw::sym_block_class(k0, qw0, qlast, T, W);
+              cls_blk[1] = tw::sym_block_class(k0 + 32, qw0, qlast, T, W);
+              // a lone block is always masked
+              if (cls_blk[1] == tw::kSymNone && cls_blk[0] != tw::kSymNone) cls_blk[0] = tw::kSymSome;
+              if (cls_blk[0] == tw::kSymNone && cls_blk[1] != tw::kSymNone) cls_blk[1] = tw::kSymSome;
+            }
             for (int mb = 0; mb < 2; ++mb) {
+              if (!full && !kCausal && cls_blk[mb] == tw::kSymNone) continue;  // skipped
               for (int r = 0; r < 16; ++r) {
                 const int kcn = mb * 32 + 8 * (r >> 2) + (r & 3);  // without the half
                 const int kc = kcn + 4 * half;
                 const int key = k0 + kc;
                 bool ok;
                 if (full) {
+                  ok = true;
+                } else if (!kCausal && cls_blk[mb] == tw::kSymAll) {
                   ok = true;
                 } else if (!kCausal) {
                   ok = tw::sym_visible(tw::sym_range(qi, k0, half, T, W), kcn);
