@@ -118,21 +118,25 @@ static int prefill_global_impl(const void* q, const void* k, const void* v, void
   const int S = swa::global_splits(G, Hq, T);
   if ((long long)G * Hq * S > kMaxGrid) return SWA_ERR_UNSUPPORTED;
   const int S1 = swa::global_rows_mfma_splits(T);
-  if ((long long)Hkv * ((G * (Hq / Hkv) + 31) / 32) * S1 > kMaxGrid) return SWA_ERR_UNSUPPORTED;
+  // bf16: the window workgroups and the global-row workgroups (two units
+  // each) share one launch
+  const long long row_units = (long long)Hkv * ((G * (Hq / Hkv) + 31) / 32) * S1;
+  if ((class_rows + 127) / 128 * Hq * (long long)dilation + (row_units + 1) / 2 + 8 > kMaxGrid)
+    return SWA_ERR_UNSUPPORTED;
   const size_t need = swa_prefill_global_workspace_bytes(T, Hq, G, d);
   if (!workspace || !aligned16(workspace) || workspace_bytes < need) return SWA_ERR_WORKSPACE;
   W = clamp_window(W, T);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  float* ws = static_cast<float*>(workspace);
   hipError_t e = (dtype == SWA_BF16)
+                     // the window pass and, in the same launch, the global rows'
+                     // split-K partials on the matrix cores
                      ? swa::launch_prefill_global_window_bf16(q, k, v, out, T, W, Hq, Hkv, d, mode,
-                                                              scale, global_pos, G, dilation, s)
+                                                              scale, global_pos, G, dilation, ws, s)
                      : swa::launch_prefill_global_window_f32(q, k, v, out, T, W, Hq, Hkv, d, mode,
                                                              scale, global_pos, G, dilation, s);
   if (e != hipSuccess) return SWA_ERR_LAUNCH;
-  float* ws = static_cast<float*>(workspace);
-  if (dtype == SWA_BF16) {  // the global rows on the matrix cores, then their merge
-    e = swa::launch_global_rows_mfma_bf16(q, k, v, global_pos, G, T, Hq, Hkv, d, mode, scale, ws, s);
-    if (e != hipSuccess) return SWA_ERR_LAUNCH;
+  if (dtype == SWA_BF16) {  // the merge of the global rows' partials
     e = swa::launch_global_combine(ws, out, global_pos, G, T, Hq, Hkv, d,
                                    swa::global_rows_mfma_splits(T), dtype, s);
   } else {

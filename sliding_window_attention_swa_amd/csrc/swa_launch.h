@@ -31,7 +31,7 @@ hipError_t launch_prefill_dilated_f32(const void* q, const void* k, const void* 
 hipError_t launch_prefill_global_window_bf16(const void* q, const void* k, const void* v,
                                              void* out, int T, int W, int Hq, int Hkv, int d,
                                              int mode, float scale, const int32_t* gpos, int ngl,
-                                             int dil, hipStream_t stream);
+                                             int dil, float* workspace, hipStream_t stream);
 
 hipError_t launch_prefill_global_window_f32(const void* q, const void* k, const void* v,
                                             void* out, int T, int W, int Hq, int Hkv, int d,
@@ -46,14 +46,10 @@ hipError_t launch_decode_sinks(const void* q, const void* k_ring, const void* v_
                                int d, float scale, int dtype, float* workspace,
                                hipStream_t stream);
 
-// The rows of the global tokens on the matrix cores (bf16): split-K partials
-// of global_rows_mfma_splits(T) chunks into the workspace, merged by
-// launch_global_combine.
+// The rows of the global tokens on the matrix cores (bf16) are split-K
+// partials of global_rows_mfma_splits(T) chunks, written to the workspace by
+// launch_prefill_global_window_bf16 and merged by launch_global_combine.
 int global_rows_mfma_splits(int T);
-hipError_t launch_global_rows_mfma_bf16(const void* q, const void* k, const void* v,
-                                        const int32_t* gpos, int ngl, int T, int Hq, int Hkv,
-                                        int d, int mode, float scale, float* workspace,
-                                        hipStream_t stream);
 hipError_t launch_global_combine(float* workspace, void* out, const int32_t* gpos, int ngl, int T,
                                  int Hq, int Hkv, int d, int S, int dtype, hipStream_t stream);
 

@@ -62,8 +62,9 @@
 // mode).  They are visited after the window's tiles, as extra tiles whose
 // rows are gathered from the global positions; a global key already inside a
 // row's window is masked there so that no key counts twice.  The global rows
-// themselves attend to every key: global_rows_kernel below computes their
-// split-K partials afterwards, and the decode kernels' merge writes them.
+// themselves attend to every key: the leading workgroups of the same launch
+// compute their split-K partials (global_rows_unit below), and the decode
+// kernels' merge writes them.
 
 #include "swa_device.h"
 #include "swa_launch.h"
@@ -129,6 +130,195 @@ constexpr int kWavesPerSimd = D == 128 ? 2 : (D == 64 ? 3 : 5);
 template <int D, int MODE>
 constexpr int kWavesFor = MODE >= 5 && D == 32 ? 4 : kWavesPerSimd<D>;
 
+// ---------------------------------------------------------------------------
+// Rows of global tokens on the matrix cores (aivaro answer 629, section 4.3:
+// a global token attends to every token).  One wave (a unit) takes 32 (global row,
+// query head) pairs of one KV head and one split of kGRowKeys keys: the pairs'
+// query rows are gathered as the B operand, 64-key K/V tiles are loaded into
+// LDS, and scores, masking (key <= the row's last key: its own position when
+// causal, T - 1 otherwise), an exact per-tile online softmax and O^T += V^T P^T
+// follow the tiled kernel.  The unnormalised partial (acc, max in log2 units,
+// sum) of each pair goes to the split-K workspace, merged afterwards by the
+// decode kernels' merge pass.  The units run as the leading workgroups of the
+// window pass's launch (two per workgroup, each in one half of its LDS), so
+// that they overlap the window pass instead of following it.
+// keys per split: 128 measured best at Longformer shapes (11.5 us; 256: 12.3,
+// 512: 15.2 us, the merge then costing less)
+constexpr int kGRowKeys = 128;
+
+template <int D, int MODE>
+__device__ __forceinline__ void global_rows_unit(const __bf16* __restrict__ q,
+                                                 const __bf16* __restrict__ k,
+                                                 const __bf16* __restrict__ v,
+                                                 const int32_t* __restrict__ gpos,
+                                                 float* __restrict__ ws_acc, float* __restrict__ ws_m,
+                                                 float* __restrict__ ws_l, int T, int Hq, int Hkv,
+                                                 int ngl, float c, uint32_t qsign, int S,
+                                                 int n_pchunks, int unit, int lane, char* lds_k,
+                                                 char* lds_v) {
+  using Gm = Geo<D>;
+  constexpr int ROWB = Gm::ROWB, KS = Gm::KS, MD = Gm::MD;
+  constexpr int TILEB = kBN * ROWB;
+  constexpr int NL = TILEB / (64 * 16);  // direct loads per lane per tile
+
+  const int G = Hq / Hkv;
+  const int n_pairs = ngl * G;
+  int id = unit;
+  const int split = id % S;
+  id /= S;
+  const int pc = id % n_pchunks;
+  const int kvh = id / n_pchunks;
+  const int half = lane >> 5;
+
+  // this lane's row: pair pi = pc * 32 + lane % 32 (global row pi / G, query
+  // head kvh * G + pi % G); positions outside [0, T) and pairs past the last
+  // are rows without keys
+  const int pi = pc * 32 + (lane & 31);
+  int gp = -1, h = 0;
+  if (pi < n_pairs) {
+    gp = gpos[pi / G];
+    h = kvh * G + pi % G;
+    if (gp < 0 || gp >= T) gp = -1;
+  }
+  const int s0 = tm::grow_split_begin(split, kGRowKeys);
+  const int s1 = tm::grow_split_end(split, kGRowKeys, T);
+  const int lim = tm::grow_row_limit(MODE == 0, gp, T, s1);  // last key of the row
+  // the wave stops after the last key any of its rows sees
+  int wlim = lim;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) wlim = max(wlim, __shfl_xor(wlim, off));
+
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (gp >= 0) w = *reinterpret_cast<const uint4*>(q + ((size_t)h * T + gp) * D + ks * 16 + half * 8);
+    w.x ^= qsign;
+    w.y ^= qsign;
+    w.z ^= qsign;
+    w.w ^= qsign;
+    qf[ks] = __builtin_bit_cast(bf16x8, w);
+  }
+  const __bf16* kh = k + (size_t)kvh * T * D;
+  const __bf16* vh = v + (size_t)kvh * T * D;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)kh, 0, T * ROWB, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)vh, 0, T * ROWB, kBufferFlags);
+
+  const int kr = lane & 31;
+  const int kf = swz<D>(kr);
+  const int tr_s = lane & 15, tr_g = lane >> 4;
+  const int tr_row = 4 * (tr_g >> 1) + (tr_s >> 2);
+  const int tr_c0 = 2 * (tr_g & 1) + ((tr_s & 3) >> 1);
+  const int tr_flo = swz<D>(tr_row), tr_fhi = swz<D>(tr_row + 8);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  f32x16 o[MD];
+#pragma unroll
+  for (int md = 0; md < MD; ++md) o[md] = f32x16{};
+  float m = -INFINITY, l = 0.f;  // raw-score maximum and sum of this lane's row
+
+  for (int k0 = s0; k0 <= wlim; k0 += kBN) {
+    // the tile: rows past T re-read row T - 1 (finite, masked); the previous
+    // tile's LDS reads are complete before it is overwritten
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int o16 = (64 * j + lane) * 16;
+      const int row = o16 / ROWB;
+      const int off = tm::grow_src_row(k0, row, T) * ROWB + ((((o16 % ROWB) / 16) ^ swz<D>(row)) * 16);
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass mishandles this builtin
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(lds_k + 64 * j * 16), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(lds_v + 64 * j * 16), 16, off, 0, 0, 0);
+#else
+      (void)rk, (void)rv, (void)off;
+#endif
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the tile is in LDS (one wave: no barrier)
+
+    f32x16 sb[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      sb[mb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds_k + (mb * 32 + kr) * ROWB + (((2 * ks + half) ^ kf) * 16));
+        sb[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sb[mb], 0, 0, 0);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (key > lim) sb[mb][r] = -INFINITY;
+        mx = fmaxf(mx, sb[mb][r]);
+      }
+    }
+    mx = max_lane_pair(mx);  // lanes l and l^32 hold the same row
+    const float m_new = fmaxf(m, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // a row without keys so far
+    const float alpha = __builtin_amdgcn_exp2f((m - m_use) * c);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[md][r] *= alpha;
+    }
+    const float mc = -m_use * c;
+    bf16x8 p[4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sb[mb][8 * k2 + 2 * e], c, mc));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sb[mb][8 * k2 + 2 * e + 1], c, mc));
+          w[e] = pack_bf16x2(p0, p1);
+          l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[e]), ones, l, false);
+        }
+        p[2 * mb + k2] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+      const int vlo = tr_row * ROWB + (((4 * md + tr_c0) ^ tr_flo) * 16) + (tr_s & 1) * 8;
+      const int vhi = (tr_row + 8) * ROWB + (((4 * md + tr_c0) ^ tr_fhi) * 16) + (tr_s & 1) * 8;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const char* src = lds_v + kk * 16 * ROWB;
+        const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + vlo));
+        const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + vhi));
+        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[kk], o[md], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- the pair's partial (the merge computes sum_s 2^(m_s - M) acc_s / ...)
+  const float l_tot = l + __shfl_xor(l, 32);
+  if (gp >= 0) {
+    const size_t slot = ((size_t)kvh * n_pairs + pi) * S + split;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int dim = 32 * md + 8 * rq + 4 * half;
+        *reinterpret_cast<float4*>(ws_acc + slot * D + dim) =
+            make_float4(o[md][4 * rq], o[md][4 * rq + 1], o[md][4 * rq + 2], o[md][4 * rq + 3]);
+      }
+    }
+    if (half == 0) {
+      ws_m[slot] = m == -INFINITY ? -1.0e30f : m * c;
+      ws_l[slot] = l_tot;
+    }
+  }
+}
+
 // MODE: 0 causal, 1 symmetric, 2 causal chunk continuing a ring cache (Tseq
 // is then the chunk length; kring/vring/pos/hkv_seq are used by MODE 2 only),
 // 3 causal dilated, 4 symmetric dilated (dil is used by MODES 3, 4, 7, 8),
@@ -142,7 +332,9 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
                          int W, int Hq, int Hkv, float c, uint32_t qsign, int n_qtiles,
                          const __bf16* __restrict__ kring, const __bf16* __restrict__ vring,
                          const int32_t* __restrict__ pos, int hkv_seq, int dil,
-                         const int32_t* __restrict__ gpos, int ngl) {
+                         const int32_t* __restrict__ gpos, int ngl,
+                         float* __restrict__ gr_acc, float* __restrict__ gr_m,
+                         float* __restrict__ gr_l, int gr_S, int gr_pchunks, int gr_wgs) {
   constexpr bool kCausal = MODE != 1 && MODE != 4 && MODE != 6 && MODE != 8;
   constexpr bool kChunk = MODE == 2;
   constexpr bool kDil = MODE == 3 || MODE == 4 || MODE == 7 || MODE == 8;
@@ -159,10 +351,25 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   // global modes: the positions of the global key tile held in each stage
   __shared__ __attribute__((aligned(16))) int lds_gp[2][kGlobal ? kBN : 1];
 
+  // global modes: the first gr_wgs workgroups compute the global rows, two
+  // units each (waves 0 and 1, each in its own LDS stage)
+  if constexpr (kGlobal) {
+    if ((int)blockIdx.x < gr_wgs) {
+      const int w = threadIdx.x >> 6;
+      const int unit = (int)tm::grow_unit(blockIdx.x, w);
+      if (w < 2 && unit < Hkv * gr_pchunks * gr_S) {
+        global_rows_unit<D, kCausal ? 0 : 1>(q, k, v, gpos, gr_acc, gr_m, gr_l, Tseq, Hq, Hkv, ngl,
+                                             c, qsign, gr_S, gr_pchunks, unit, threadIdx.x & 63,
+                                             w ? lds_k1 : lds_k0, w ? lds_v1 : lds_v0);
+      }
+      return;
+    }
+  }
+
   // ---- which (query head, query block) this workgroup owns
   const int G = Hq / Hkv;
-  int id = blockIdx.x;
-  const int nwg = gridDim.x;
+  int id = (int)blockIdx.x - gr_wgs;
+  const int nwg = (int)gridDim.x - gr_wgs;
   // consecutive ids go round-robin to the 8 XCDs: give each XCD a contiguous range
   if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
   const int hg = id % G;
@@ -1007,18 +1214,40 @@ hipError_t launch(const void* q, const void* k, const void* v, void* out, int T,
                      static_cast<const __bf16*>(v), static_cast<__bf16*>(out), T, W, Hq, Hkv, c,
                      qsign, n_qtiles, static_cast<const __bf16*>(nullptr),
                      static_cast<const __bf16*>(nullptr), static_cast<const int32_t*>(nullptr), 1,
-                     1, static_cast<const int32_t*>(nullptr), 0);
+                     1, static_cast<const int32_t*>(nullptr), 0, nullptr, nullptr, nullptr, 1, 1, 0);
   return hipGetLastError();
 }
 
 // Dilated windows: one workgroup per (query head, residue class, query block
 // of the class's rows); the longest class has ceil(T / dil) rows.
+// The global-row units of a global-key launch: split-K over kGRowKeys-key
+// chunks of every (KV head, chunk of 32 (global row, query head) pairs); two
+// units per workgroup, a multiple of 8 workgroups so that the window
+// workgroups keep their XCD placement.  Workspace layout: acc, then the
+// maxima, then the sums, as the merge reads them.
+struct GlobalRows {
+  float *acc, *m, *l;
+  int S, pchunks, wgs;
+};
+GlobalRows global_rows_plan(float* ws, int T, int Hq, int Hkv, int ngl, int D) {
+  GlobalRows g;
+  g.S = (T + kGRowKeys - 1) / kGRowKeys;
+  g.pchunks = (ngl * (Hq / Hkv) + 31) / 32;
+  g.wgs = ngl > 0 ? (int)tm::grow_workgroups((long long)Hkv * g.pchunks * g.S) : 0;
+  const size_t rows = (size_t)ngl * Hq * g.S;
+  g.acc = ws;
+  g.m = ws ? ws + rows * D : nullptr;
+  g.l = ws ? g.m + rows : nullptr;
+  return g;
+}
+
 template <int D, int MODE>
 hipError_t launch_dilated(const void* q, const void* k, const void* v, void* out, int T, int W,
                           int Hq, int Hkv, float scale, int dil, hipStream_t stream,
-                          const int32_t* gpos = nullptr, int ngl = 0) {
+                          const int32_t* gpos = nullptr, int ngl = 0, float* ws = nullptr) {
   const int n_qtiles = ((T + dil - 1) / dil + kBM - 1) / kBM;
-  const long long nwg = (long long)n_qtiles * Hq * dil;
+  const GlobalRows gr = global_rows_plan(ws, T, Hq, Hkv, gpos ? ngl : 0, D);
+  const long long nwg = (long long)n_qtiles * Hq * dil + gr.wgs;
   float c;
   uint32_t qsign;
   fold_scale(scale, c, qsign);
@@ -1027,18 +1256,19 @@ hipError_t launch_dilated(const void* q, const void* k, const void* v, void* out
                      static_cast<const __bf16*>(v), static_cast<__bf16*>(out), T, W, Hq, Hkv, c,
                      qsign, n_qtiles, static_cast<const __bf16*>(nullptr),
                      static_cast<const __bf16*>(nullptr), static_cast<const int32_t*>(nullptr), 1,
-                     dil, gpos, ngl);
+                     dil, gpos, ngl, gr.acc, gr.m, gr.l, gr.S, gr.pchunks, gr.wgs);
   return hipGetLastError();
 }
 
-// Window plus global keys (the global rows are written by global_rows_kernel
-// and the merge).
+// Window plus global keys, with the global rows' split-K partials computed in
+// the same launch (the merge writes those rows afterwards).
 template <int D, int MODE>
 hipError_t launch_global(const void* q, const void* k, const void* v, void* out, int T, int W,
-                         int Hq, int Hkv, float scale, const int32_t* gpos, int ngl,
+                         int Hq, int Hkv, float scale, const int32_t* gpos, int ngl, float* ws,
                          hipStream_t stream) {
   const int n_qtiles = (T + kBM - 1) / kBM;
-  const long long nwg = (long long)n_qtiles * Hq;
+  const GlobalRows gr = global_rows_plan(ws, T, Hq, Hkv, ngl, D);
+  const long long nwg = (long long)n_qtiles * Hq + gr.wgs;
   float c;
   uint32_t qsign;
   fold_scale(scale, c, qsign);
@@ -1047,7 +1277,7 @@ hipError_t launch_global(const void* q, const void* k, const void* v, void* out,
                      static_cast<const __bf16*>(v), static_cast<__bf16*>(out), T, W, Hq, Hkv, c,
                      qsign, n_qtiles, static_cast<const __bf16*>(nullptr),
                      static_cast<const __bf16*>(nullptr), static_cast<const int32_t*>(nullptr), 1,
-                     1, gpos, ngl);
+                     1, gpos, ngl, gr.acc, gr.m, gr.l, gr.S, gr.pchunks, gr.wgs);
   return hipGetLastError();
 }
 
@@ -1068,237 +1298,13 @@ hipError_t launch_chunk(const void* q, const void* k, const void* v, const void*
                      static_cast<const __bf16*>(v), static_cast<__bf16*>(out), n, W, Hq * B,
                      Hkv * B, c, qsign, n_qtiles, static_cast<const __bf16*>(k_ring),
                      static_cast<const __bf16*>(v_ring), pos, Hkv, 1,
-                     static_cast<const int32_t*>(nullptr), 0);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// Rows of global tokens on the matrix cores (aivaro answer 629, section 4.3:
-// a global token attends to every token).  One wave takes 32 (global row,
-// query head) pairs of one KV head and one split of kGRowKeys keys: the pairs'
-// query rows are gathered as the B operand, 64-key K/V tiles are loaded into
-// LDS, and scores, masking (key <= the row's last key: its own position when
-// causal, T - 1 otherwise), an exact per-tile online softmax and O^T += V^T P^T
-// follow the tiled kernel.  The unnormalised partial (acc, max in log2 units,
-// sum) of each pair goes to the split-K workspace, merged afterwards by the
-// decode kernels' merge pass.
-// keys per split: 128 measured best at Longformer shapes (11.5 us; 256: 12.3,
-// 512: 15.2 us, the merge then costing less)
-constexpr int kGRowKeys = 128;
-
-template <int D, int MODE>
-__global__ __launch_bounds__(64)
-__attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>)))
-void global_rows_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-                        const __bf16* __restrict__ v, const int32_t* __restrict__ gpos,
-                        float* __restrict__ ws_acc, float* __restrict__ ws_m,
-                        float* __restrict__ ws_l, int T, int Hq, int Hkv, int ngl, float c,
-                        uint32_t qsign, int S, int n_pchunks) {
-  using Gm = Geo<D>;
-  constexpr int ROWB = Gm::ROWB, KS = Gm::KS, MD = Gm::MD;
-  constexpr int TILEB = kBN * ROWB;
-  constexpr int NL = TILEB / (64 * 16);  // direct loads per lane per tile
-  __shared__ __attribute__((aligned(1024))) char lds_k[TILEB];
-  __shared__ __attribute__((aligned(1024))) char lds_v[TILEB];
-
-  const int G = Hq / Hkv;
-  const int n_pairs = ngl * G;
-  int id = blockIdx.x;
-  const int split = id % S;
-  id /= S;
-  const int pc = id % n_pchunks;
-  const int kvh = id / n_pchunks;
-  const int lane = threadIdx.x;
-  const int half = lane >> 5;
-
-  // this lane's row: pair pi = pc * 32 + lane % 32 (global row pi / G, query
-  // head kvh * G + pi % G); positions outside [0, T) and pairs past the last
-  // are rows without keys
-  const int pi = pc * 32 + (lane & 31);
-  int gp = -1, h = 0;
-  if (pi < n_pairs) {
-    gp = gpos[pi / G];
-    h = kvh * G + pi % G;
-    if (gp < 0 || gp >= T) gp = -1;
-  }
-  const int s0 = tm::grow_split_begin(split, kGRowKeys);
-  const int s1 = tm::grow_split_end(split, kGRowKeys, T);
-  const int lim = tm::grow_row_limit(MODE == 0, gp, T, s1);  // last key of the row
-  // the wave stops after the last key any of its rows sees
-  int wlim = lim;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) wlim = max(wlim, __shfl_xor(wlim, off));
-
-  bf16x8 qf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (gp >= 0) w = *reinterpret_cast<const uint4*>(q + ((size_t)h * T + gp) * D + ks * 16 + half * 8);
-    w.x ^= qsign;
-    w.y ^= qsign;
-    w.z ^= qsign;
-    w.w ^= qsign;
-    qf[ks] = __builtin_bit_cast(bf16x8, w);
-  }
-  const __bf16* kh = k + (size_t)kvh * T * D;
-  const __bf16* vh = v + (size_t)kvh * T * D;
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)kh, 0, T * ROWB, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)vh, 0, T * ROWB, kBufferFlags);
-
-  const int kr = lane & 31;
-  const int kf = swz<D>(kr);
-  const int tr_s = lane & 15, tr_g = lane >> 4;
-  const int tr_row = 4 * (tr_g >> 1) + (tr_s >> 2);
-  const int tr_c0 = 2 * (tr_g & 1) + ((tr_s & 3) >> 1);
-  const int tr_flo = swz<D>(tr_row), tr_fhi = swz<D>(tr_row + 8);
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-
-  f32x16 o[MD];
-#pragma unroll
-  for (int md = 0; md < MD; ++md) o[md] = f32x16{};
-  float m = -INFINITY, l = 0.f;  // raw-score maximum and sum of this lane's row
-
-  for (int k0 = s0; k0 <= wlim; k0 += kBN) {
-    // the tile: rows past T re-read row T - 1 (finite, masked); the previous
-    // tile's LDS reads are complete before it is overwritten
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-#pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      const int o16 = (64 * j + lane) * 16;
-      const int row = o16 / ROWB;
-      const int off = tm::grow_src_row(k0, row, T) * ROWB + ((((o16 % ROWB) / 16) ^ swz<D>(row)) * 16);
-#if defined(__HIP_DEVICE_COMPILE__)  // the host pass mishandles this builtin
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(lds_k + 64 * j * 16), 16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(lds_v + 64 * j * 16), 16, off, 0, 0, 0);
-#else
-      (void)rk, (void)rv, (void)off;
-#endif
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the tile is in LDS (one wave: no barrier)
-
-    f32x16 sb[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      sb[mb] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds_k + (mb * 32 + kr) * ROWB + (((2 * ks + half) ^ kf) * 16));
-        sb[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sb[mb], 0, 0, 0);
-      }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (key > lim) sb[mb][r] = -INFINITY;
-        mx = fmaxf(mx, sb[mb][r]);
-      }
-    }
-    mx = max_lane_pair(mx);  // lanes l and l^32 hold the same row
-    const float m_new = fmaxf(m, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // a row without keys so far
-    const float alpha = __builtin_amdgcn_exp2f((m - m_use) * c);
-    m = m_new;
-    l *= alpha;
-#pragma unroll
-    for (int md = 0; md < MD; ++md) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[md][r] *= alpha;
-    }
-    const float mc = -m_use * c;
-    bf16x8 p[4];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sb[mb][8 * k2 + 2 * e], c, mc));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sb[mb][8 * k2 + 2 * e + 1], c, mc));
-          w[e] = pack_bf16x2(p0, p1);
-          l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[e]), ones, l, false);
-        }
-        p[2 * mb + k2] = __builtin_bit_cast(bf16x8, w);
-      }
-    }
-#pragma unroll
-    for (int md = 0; md < MD; ++md) {
-      const int vlo = tr_row * ROWB + (((4 * md + tr_c0) ^ tr_flo) * 16) + (tr_s & 1) * 8;
-      const int vhi = (tr_row + 8) * ROWB + (((4 * md + tr_c0) ^ tr_fhi) * 16) + (tr_s & 1) * 8;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const char* src = lds_v + kk * 16 * ROWB;
-        const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + vlo));
-        const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + vhi));
-        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[kk], o[md], 0, 0, 0);
-      }
-    }
-  }
-
-  // ---- the pair's partial (the merge computes sum_s 2^(m_s - M) acc_s / ...)
-  const float l_tot = l + __shfl_xor(l, 32);
-  if (gp >= 0) {
-    const size_t slot = ((size_t)kvh * n_pairs + pi) * S + split;
-#pragma unroll
-    for (int md = 0; md < MD; ++md) {
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int dim = 32 * md + 8 * rq + 4 * half;
-        *reinterpret_cast<float4*>(ws_acc + slot * D + dim) =
-            make_float4(o[md][4 * rq], o[md][4 * rq + 1], o[md][4 * rq + 2], o[md][4 * rq + 3]);
-      }
-    }
-    if (half == 0) {
-      ws_m[slot] = m == -INFINITY ? -1.0e30f : m * c;
-      ws_l[slot] = l_tot;
-    }
-  }
-}
-
-template <int D, int MODE>
-hipError_t launch_global_rows(const void* q, const void* k, const void* v, const int32_t* gpos,
-                              int ngl, int T, int Hq, int Hkv, float scale, float* workspace,
-                              hipStream_t stream) {
-  const int S = (T + kGRowKeys - 1) / kGRowKeys;
-  const int n_pairs = ngl * (Hq / Hkv);
-  const int n_pchunks = (n_pairs + 31) / 32;
-  const size_t rows = (size_t)ngl * Hq * S;
-  float* ws_acc = workspace;
-  float* ws_m = ws_acc + rows * D;
-  float* ws_l = ws_m + rows;
-  float c;
-  uint32_t qsign;
-  fold_scale(scale, c, qsign);
-  const long long nwg = (long long)Hkv * n_pchunks * S;
-  hipLaunchKernelGGL((global_rows_kernel<D, MODE>), dim3((unsigned)nwg), dim3(64), 0, stream,
-                     static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
-                     static_cast<const __bf16*>(v), gpos, ws_acc, ws_m, ws_l, T, Hq, Hkv, ngl, c,
-                     qsign, S, n_pchunks);
+                     static_cast<const int32_t*>(nullptr), 0, nullptr, nullptr, nullptr, 1, 1, 0);
   return hipGetLastError();
 }
 
 }  // namespace
 
 int global_rows_mfma_splits(int T) { return (T + kGRowKeys - 1) / kGRowKeys; }
-
-hipError_t launch_global_rows_mfma_bf16(const void* q, const void* k, const void* v,
-                                        const int32_t* gpos, int ngl, int T, int Hq, int Hkv,
-                                        int d, int mode, float scale, float* workspace,
-                                        hipStream_t stream) {
-  if (mode == 0) {
-    if (d == 32) return launch_global_rows<32, 0>(q, k, v, gpos, ngl, T, Hq, Hkv, scale, workspace, stream);
-    if (d == 64) return launch_global_rows<64, 0>(q, k, v, gpos, ngl, T, Hq, Hkv, scale, workspace, stream);
-    return launch_global_rows<128, 0>(q, k, v, gpos, ngl, T, Hq, Hkv, scale, workspace, stream);
-  }
-  if (d == 32) return launch_global_rows<32, 1>(q, k, v, gpos, ngl, T, Hq, Hkv, scale, workspace, stream);
-  if (d == 64) return launch_global_rows<64, 1>(q, k, v, gpos, ngl, T, Hq, Hkv, scale, workspace, stream);
-  return launch_global_rows<128, 1>(q, k, v, gpos, ngl, T, Hq, Hkv, scale, workspace, stream);
-}
 
 hipError_t launch_prefill_chunk_bf16(const void* q, const void* k, const void* v,
                                      const void* k_ring, const void* v_ring, const int32_t* pos,
@@ -1312,25 +1318,25 @@ hipError_t launch_prefill_chunk_bf16(const void* q, const void* k, const void* v
 hipError_t launch_prefill_global_window_bf16(const void* q, const void* k, const void* v,
                                              void* out, int T, int W, int Hq, int Hkv, int d,
                                              int mode, float scale, const int32_t* gpos, int ngl,
-                                             int dil, hipStream_t stream) {
+                                             int dil, float* ws, hipStream_t stream) {
   if (dil > 1) {  // dilated window plus global keys
     if (mode == 0) {
-      if (d == 32) return launch_dilated<32, 7>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream, gpos, ngl);
-      if (d == 64) return launch_dilated<64, 7>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream, gpos, ngl);
-      return launch_dilated<128, 7>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream, gpos, ngl);
+      if (d == 32) return launch_dilated<32, 7>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream, gpos, ngl, ws);
+      if (d == 64) return launch_dilated<64, 7>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream, gpos, ngl, ws);
+      return launch_dilated<128, 7>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream, gpos, ngl, ws);
     }
-    if (d == 32) return launch_dilated<32, 8>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream, gpos, ngl);
-    if (d == 64) return launch_dilated<64, 8>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream, gpos, ngl);
-    return launch_dilated<128, 8>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream, gpos, ngl);
+    if (d == 32) return launch_dilated<32, 8>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream, gpos, ngl, ws);
+    if (d == 64) return launch_dilated<64, 8>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream, gpos, ngl, ws);
+    return launch_dilated<128, 8>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream, gpos, ngl, ws);
   }
   if (mode == 0) {
-    if (d == 32) return launch_global<32, 5>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, stream);
-    if (d == 64) return launch_global<64, 5>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, stream);
-    return launch_global<128, 5>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, stream);
+    if (d == 32) return launch_global<32, 5>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, ws, stream);
+    if (d == 64) return launch_global<64, 5>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, ws, stream);
+    return launch_global<128, 5>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, ws, stream);
   }
-  if (d == 32) return launch_global<32, 6>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, stream);
-  if (d == 64) return launch_global<64, 6>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, stream);
-  return launch_global<128, 6>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, stream);
+  if (d == 32) return launch_global<32, 6>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, ws, stream);
+  if (d == 64) return launch_global<64, 6>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, ws, stream);
+  return launch_global<128, 6>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, ws, stream);
 }
 
 hipError_t launch_prefill_dilated_bf16(const void* q, const void* k, const void* v, void* out,

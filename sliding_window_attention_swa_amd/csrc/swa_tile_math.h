@@ -232,6 +232,12 @@ SWA_HD int grow_row_limit(bool causal, int gp, int T, int s1) {
   return gp < 0 ? -1 : imin(causal ? gp : T - 1, s1 - 1);
 }
 SWA_HD int grow_src_row(int k0, int row, int T) { return imin(k0 + row, T - 1); }
+// The units run as the leading workgroups of the window launch, two per
+// workgroup (waves 0 and 1): unit 2 * wg + wave, if below the unit count; the
+// number of such workgroups is rounded up to a multiple of 8 so that the
+// window workgroups after them keep their XCD placement.
+SWA_HD long long grow_workgroups(long long units) { return units > 0 ? ((units + 1) / 2 + 7) / 8 * 8 : 0; }
+SWA_HD long long grow_unit(long long wg, int wave) { return 2 * wg + wave; }
 
 }  // namespace tm
 }  // namespace swa

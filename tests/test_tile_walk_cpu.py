@@ -190,7 +190,7 @@ def test_window_plus_global_tokens(walker, mode, dil):
 
 
 @pytest.mark.parametrize("mode", [CAUSAL, SYMMETRIC])
-def test_global_rows_kernel(walker, mode):
+def test_global_row_units(walker, mode):
     """The global-row pass: split-K over 128-key chunks, each global row counts
     every key (every earlier key when causal), loads clamped inside the
     sequence."""

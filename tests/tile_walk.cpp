@@ -253,7 +253,7 @@ void walk_short(int MODE, int T, int W, int D) {
   emit(keys);
 }
 
-// The global-rows kernel (global_rows_kernel) for one query head: every
+// The global-row units (global_rows_unit) for one query head: every
 // global row, over all splits.
 void walk_grows(int MODE, int T, int D, const std::vector<int>& gpos) {
   const bool causal = MODE == 0;
@@ -261,6 +261,23 @@ void walk_grows(int MODE, int T, int D, const std::vector<int>& gpos) {
   const int kRowKeys = 128;
   const int S = (T + kRowKeys - 1) / kRowKeys;
   const long long head_bytes = (long long)T * ROWB;
+  // the units of one KV head with G global rows (one chunk of 32 pairs per
+  // head here), two per leading workgroup: each exactly once
+  {
+    const long long units = (long long)S * (((long long)gpos.size() + 31) / 32);
+    std::vector<int> seen(units, 0);
+    const long long wgs = tw::grow_workgroups(units);
+    if (units > 0 && (wgs % 8 != 0 || 2 * wgs < units)) std::printf("BAD row workgroups %lld for %lld units\n", wgs, units);
+    for (long long wg = 0; wg < wgs; ++wg) {
+      for (int wave = 0; wave < 2; ++wave) {
+        const long long u = tw::grow_unit(wg, wave);
+        if (u < units) ++seen[u];
+      }
+    }
+    for (long long u = 0; u < units; ++u) {
+      if (seen[u] != 1) std::printf("BAD row unit %lld run %d times\n", u, seen[u]);
+    }
+  }
   Keys keys;
   for (int split = 0; split < S; ++split) {
     const int s0 = tw::grow_split_begin(split, kRowKeys);
