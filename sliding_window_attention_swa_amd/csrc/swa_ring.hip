@@ -180,7 +180,9 @@ __device__ __forceinline__ uint4 stream_load(const E* p) {
 
 // GR: 0 decode, 1 / 2 rows of causal / symmetric global tokens, 3 decode
 // whose every split writes its partial (slot split of S + 1 per row; the
-// last slot holds the attention sinks' partial)
+// last slot holds the attention sinks' partial), 4 decode of one split with
+// the attention sinks before the window (k_sink / v_sink) taken first in the
+// same online softmax, writing the output itself
 template <int GR>
 constexpr bool kRows = GR == 1 || GR == 2;
 
@@ -189,7 +191,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     const E* __restrict__ q, const E* __restrict__ k_ring, const E* __restrict__ v_ring,
     const int32_t* __restrict__ pos, E* __restrict__ out, float* __restrict__ ws_acc,
     float* __restrict__ ws_m, float* __restrict__ ws_l, int Hq, int Hkv, int W, float scale_log2,
-    int S, int chunk, int n_hchunks, int n_pairs) {
+    int S, int chunk, int n_hchunks, int n_pairs, const E* __restrict__ k_sink,
+    const E* __restrict__ v_sink, int n_sink) {
   // GR != 0: pos holds the global positions, W is the sequence length and
   // pair pi = hc * NQ + hq (of n_pairs = global rows * group size) is global
   // row pi / G with query head kvh * G + pi % G
@@ -273,20 +276,22 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
   const E* kb = k_ring + ring_off;
   const E* vb = v_ring + ring_off;
 
-  for (int base = s0; base < s1; base += STEP) {
+  // one workgroup step: rows base .. base + STEP - 1 (those below lim) of the
+  // rows at kbp / vbp
+  auto step = [&](const E* kbp, const E* vbp, int base, int lim) __attribute__((always_inline)) {
     uint4 kraw[kUnroll], vraw[kUnroll];
     bool valid[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int r = base + (u * kDecodeWaves + wave) * RPW + rg;
-      valid[u] = r < s1;
+      valid[u] = r < lim;
       if (valid[u]) {
         if constexpr (kRows<GR> && !kGlobalNT) {  // rows the windowed pass just read
-          kraw[u] = *reinterpret_cast<const uint4*>(kb + (size_t)r * D);
-          vraw[u] = *reinterpret_cast<const uint4*>(vb + (size_t)r * D);
+          kraw[u] = *reinterpret_cast<const uint4*>(kbp + (size_t)r * D);
+          vraw[u] = *reinterpret_cast<const uint4*>(vbp + (size_t)r * D);
         } else {
-          kraw[u] = stream_load(kb + (size_t)r * D);
-          vraw[u] = stream_load(vb + (size_t)r * D);
+          kraw[u] = stream_load(kbp + (size_t)r * D);
+          vraw[u] = stream_load(vbp + (size_t)r * D);
         }
       } else {
         kraw[u] = make_uint4(0, 0, 0, 0);
@@ -335,7 +340,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
         for (int e = 0; e < EPL; ++e) acc[hq][e] = fmaf(pr, vf[u][e], acc[hq][e]);
       }
     }
+  };
+  if constexpr (GR == 4) {  // the sinks before the window, ahead of the ring's rows
+    const int ns = p < 0 ? 0 : min(n_sink, max(0, p - W + 1));
+    const size_t sink_off = ((size_t)b * Hkv + kvh) * (size_t)n_sink * D + li * EPL;
+    for (int base = 0; base < ns; base += STEP) step(k_sink + sink_off, v_sink + sink_off, base, ns);
   }
+  for (int base = s0; base < s1; base += STEP) step(kb, vb, base, s1);
 
   // ---- merge the NSTATE lane-row states of this workgroup
   const int st = wave * RPW + rg;
@@ -374,6 +385,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
       slot = ((size_t)kvh * n_pairs + pi) * S + split;
     } else if constexpr (GR == 3) {  // always a partial; one more slot per row
       slot = ((size_t)b * Hq + h0 + hq) * (S + 1) + split;
+    } else if constexpr (GR == 4) {  // one split, sinks included: the output
+      Elem<E>::store(out + ((size_t)b * Hq + h0 + hq) * D + dim, L > 0.f ? a / L : 0.f);
+      continue;
     } else {
       if (S == 1) {  // no other split to merge with: finish here
         Elem<E>::store(out + ((size_t)b * Hq + h0 + hq) * D + dim, L > 0.f ? a / L : 0.f);
@@ -499,7 +513,9 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
 template <typename E, int D, int NQ, int GR>
 hipError_t launch_decode_t(const void* q, const void* k_ring, const void* v_ring,
                            const int32_t* pos, void* out, int B, int Hq, int Hkv, int W,
-                           float scale, float* workspace, hipStream_t stream) {
+                           float scale, float* workspace, hipStream_t stream,
+                           const void* k_sink = nullptr, const void* v_sink = nullptr,
+                           int n_sink = 0) {
   const int S = kRows<GR> ? global_splits(B, Hq, W) : decode_splits(B, Hq, W);
   const int chunk = (W + S - 1) / S;
   const int G = Hq / Hkv;
@@ -509,7 +525,7 @@ hipError_t launch_decode_t(const void* q, const void* k_ring, const void* v_ring
   const size_t rows = (size_t)B * Hq * (GR == 3 ? S + 1 : S);
   // a plain decode of one split writes the output itself: no workspace (it
   // may be null then)
-  const bool partials = GR != 0 || S > 1;
+  const bool partials = (GR != 0 && GR != 4) || S > 1;
   float* ws_acc = partials ? workspace : nullptr;
   float* ws_m = partials ? ws_acc + rows * D : nullptr;
   float* ws_l = partials ? ws_m + rows : nullptr;
@@ -517,9 +533,10 @@ hipError_t launch_decode_t(const void* q, const void* k_ring, const void* v_ring
   hipLaunchKernelGGL((decode_split_kernel<E, D, NQ, GR>), dim3((unsigned)nwg), dim3(kDecodeThreads), 0,
                      stream, static_cast<const E*>(q), static_cast<const E*>(k_ring),
                      static_cast<const E*>(v_ring), pos, static_cast<E*>(out), ws_acc, ws_m, ws_l,
-                     Hq, Hkv, W, scale * kLog2e, S, chunk, n_hchunks, n_pairs);
+                     Hq, Hkv, W, scale * kLog2e, S, chunk, n_hchunks, n_pairs,
+                     static_cast<const E*>(k_sink), static_cast<const E*>(v_sink), n_sink);
   hipError_t e = hipGetLastError();
-  if (GR == 3) return e;  // the sinks' partial and the merge follow
+  if (GR == 3 || GR == 4) return e;  // GR 3: the sinks' partial and the merge follow
   if (e != hipSuccess || S == 1) return e;
   hipLaunchKernelGGL((decode_combine_kernel<E, D, GR>), dim3((unsigned)((size_t)B * Hq)), dim3(D), 0,
                      stream, ws_acc, ws_m, ws_l, static_cast<E*>(out), S, pos, W, G, n_pairs);
@@ -547,6 +564,13 @@ hipError_t launch_decode_sinks_d(const void* q, const void* k_ring, const void* 
                                  float scale, float* workspace, hipStream_t stream) {
   const int G = Hq / Hkv;
   hipError_t e;
+  if (decode_splits(B, Hq, W) == 1) {  // one split: the sinks join its online softmax
+    if (G % 4 == 0)
+      return launch_decode_t<E, D, 4, 4>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, nullptr, stream, k_sink, v_sink, n_sink);
+    if (G % 2 == 0)
+      return launch_decode_t<E, D, 2, 4>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, nullptr, stream, k_sink, v_sink, n_sink);
+    return launch_decode_t<E, D, 1, 4>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, nullptr, stream, k_sink, v_sink, n_sink);
+  }
   if (G % 4 == 0)
     e = launch_decode_t<E, D, 4, 3>(q, k_ring, v_ring, pos, out, B, Hq, Hkv, W, scale, workspace, stream);
   else if (G % 2 == 0)
