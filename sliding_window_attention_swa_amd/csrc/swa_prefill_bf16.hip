@@ -838,17 +838,36 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   // When at most 32 global keys are left, only the first 32-key block is
   // computed.
   auto global_tile = [&](const char* Ks, const char* Vs, int t0, const int* gp_tile) __attribute__((always_inline)) {
+    // The global positions are the same for every row: when no row of the
+    // wave has one of the tile's keys in its window (and, causal, none is
+    // after a row), every valid key counts for every row and the per-key test
+    // is skipped.  Lane j looks at key t0 + j of the tile.
+    const int gl = gp_tile[lane];
+    const bool gvalid = tm::global_valid(t0 + lane, gl, ngl, Tseq);
+    int gmin = gvalid ? gl : 0x7fffffff, gmax = gvalid ? gl : -0x7fffffff - 1;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      gmin = ::min(gmin, __shfl_xor(gmin, off));
+      gmax = ::max(gmax, __shfl_xor(gmax, off));
+    }
+    const int rlo = kDil ? cls + dil * qw0 : qw0;  // the wave's rows as sequence positions
+    const int rhi = kDil ? cls + dil * qlast : qlast;
+    const int wcls = tm::global_wave_class(kCausal, rlo, rhi, gmin, gmax, W, dil);
     uint32_t okbits = 0;
-    const int rpos = kDil ? cls + dil * qi : qi;  // this lane's row as a sequence position
+    if (wcls == tm::kGlobalAll) {
+      okbits = tm::global_lane_bits(__ballot(gvalid), half);
+    } else if (wcls == tm::kGlobalSome) {
+      const int rpos = kDil ? cls + dil * qi : qi;  // this lane's row as a sequence position
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const int4 gp4 = *reinterpret_cast<const int4*>(gp_tile + 8 * g + 4 * half);
-      const int gpv[4] = {gp4.x, gp4.y, gp4.z, gp4.w};
+      for (int g = 0; g < 8; ++g) {
+        const int4 gp4 = *reinterpret_cast<const int4*>(gp_tile + 8 * g + 4 * half);
+        const int gpv[4] = {gp4.x, gp4.y, gp4.z, gp4.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int idx = t0 + 8 * g + 4 * half + e;
-        const bool ok = tm::global_counts(kCausal, kDil, rpos, gpv[e], idx, ngl, Tseq, W, dil);
-        okbits |= (uint32_t)ok << (4 * g + e);
+        for (int e = 0; e < 4; ++e) {
+          const int idx = t0 + 8 * g + 4 * half + e;
+          const bool ok = tm::global_counts(kCausal, kDil, rpos, gpv[e], idx, ngl, Tseq, W, dil);
+          okbits |= (uint32_t)ok << (4 * g + e);
+        }
       }
     }
     // one 32-key block at a time, and only the blocks holding global keys

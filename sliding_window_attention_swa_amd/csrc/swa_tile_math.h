@@ -176,6 +176,36 @@ SWA_HD bool global_counts(bool causal, bool dilated, int rpos, int gp, int idx, 
   return ok;
 }
 
+// Global key idx of a tile (at position gp) exists: idx < ngl, gp in [0, Tseq).
+SWA_HD bool global_valid(int idx, int gp, int ngl, int Tseq) { return idx < ngl && gp >= 0 && gp < Tseq; }
+
+// A wave's rows at sequence positions [rlo, rhi] (one dilation grid when
+// dilated) against a tile's valid global keys at positions [gmin, gmax]
+// (gmin > gmax: none).  kGlobalAll: no row has any of them in its window and
+// none is after a causal row, so every valid key counts for every row;
+// kGlobalNone: none counts (causal: all after every row); kGlobalSome: test
+// each key with global_counts.
+constexpr int kGlobalSome = 0, kGlobalAll = 1, kGlobalNone = 2;
+SWA_HD int global_wave_class(bool causal, int rlo, int rhi, int gmin, int gmax, int W, int dil) {
+  if (gmin > gmax) return kGlobalNone;
+  if (causal) {
+    if (gmin > rhi) return kGlobalNone;
+    if ((long long)gmax < (long long)rlo - (long long)(W - 1) * dil) return kGlobalAll;
+  } else {
+    const long long reach = (long long)(W >> 1) * dil;
+    if ((long long)gmax < rlo - reach || (long long)gmin > rhi + reach) return kGlobalAll;
+  }
+  return kGlobalSome;
+}
+
+// The lane's 32 key bits (bit 4g + e: key 8g + 4 half + e of the tile) from
+// a mask with bit j for key j of the tile.
+SWA_HD unsigned global_lane_bits(unsigned long long m, int half) {
+  unsigned b = 0;
+  for (int g = 0; g < 8; ++g) b |= (unsigned)((m >> (8 * g + 4 * half)) & 0xFull) << (4 * g);
+  return b;
+}
+
 // LDS placement of a tile load: load j of thread tid fills the 16 bytes at
 // (j * threads + tid) * 16 of the tile; it reads LDS row `row` of the tile,
 // logical 16-byte chunk `chunk` of that row.

@@ -195,14 +195,44 @@ void walk_tiled(int MODE, int Tseq, int W, int dil, int pstart, int D, const std
             for (int kt = kt1 + 1; kt <= kt_end; ++kt) {
               const int t0 = (kt - kt1 - 1) * tw::kBN;
               const int nblk = ngl - t0 > 32 ? 2 : 1;
+              // the wave's class against this tile (lane j looks at key t0 + j)
+              unsigned long long vmask = 0;
+              int gmin = 0x7fffffff, gmax = -0x7fffffff - 1;
+              for (int j = 0; j < 64; ++j) {
+                const int gl = gpos[tw::global_index(t0, j, ngl)];
+                if (tw::global_valid(t0 + j, gl, ngl, Tseq)) {
+                  vmask |= 1ull << j;
+                  gmin = tw::imin(gmin, gl);
+                  gmax = tw::imax(gmax, gl);
+                }
+              }
+              const int rlo = kDil ? cls + dil * qw0 : qw0;
+              const int rhi = kDil ? cls + dil * qlast : qlast;
+              const int wcls = tw::global_wave_class(kCausal, rlo, rhi, gmin, gmax, W, dil);
+              unsigned okbits = 0;
+              if (wcls == tw::kGlobalAll) {
+                okbits = tw::global_lane_bits(vmask, half);
+              } else if (wcls == tw::kGlobalSome) {
+                for (int g = 0; g < 8; ++g) {
+                  for (int e = 0; e < 4; ++e) {
+                    const int kl = 8 * g + 4 * half + e;
+                    const int gp = gpos[tw::global_index(t0, kl, ngl)];
+                    if (tw::global_counts(kCausal, kDil, (int)rpos, gp, t0 + kl, ngl, Tseq, W, dil)) {
+                      okbits |= 1u << (4 * g + e);
+                    }
+                  }
+                }
+              }
               for (int g = 0; g < 4 * nblk; ++g) {
                 for (int e = 0; e < 4; ++e) {
+                  if (!((okbits >> (4 * g + e)) & 1u)) continue;
                   const int kl = 8 * g + 4 * half + e;
-                  const int idx = t0 + kl;
                   const int gp = gpos[tw::global_index(t0, kl, ngl)];
-                  if (tw::global_counts(kCausal, kDil, (int)rpos, gp, idx, ngl, Tseq, W, dil)) {
-                    count(keys, rpos, gp);
+                  // the kernel's per-key test is the reference for the class
+                  if (!tw::global_counts(kCausal, kDil, (int)rpos, gp, t0 + kl, ngl, Tseq, W, dil)) {
+                    std::printf("BAD %lld global key %d counted by the wave class\n", rpos, gp);
                   }
+                  count(keys, rpos, gp);
                 }
               }
             }
