@@ -238,6 +238,30 @@ def pmc_config(wl):
     return 0
 
 
+def trace_global(wl, calls=13):
+    """Kernel-trace workload of a window-plus-global-tokens configuration:
+    `calls` launches of the whole pass (window and global-row launch, then
+    the merge), each after a 1 GiB read that evicts the caches."""
+    import torch
+    import sliding_window_attention_swa_amd as swa
+    dev = torch.device("cuda:0")
+    swa.load()
+    c = si.WORKLOADS[wl]
+    q, k, v = (si.to_torch(t, dev) for t in si.prefill_inputs(wl))
+    out = torch.empty_like(q)
+    gpos = torch.tensor(c["global_pos"], dtype=torch.int32, device=dev)
+    ws = swa.global_workspace(c["T"], c["B"] * c["Hq"], len(c["global_pos"]), c["d"], dev)
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    flush_max = torch.empty((), dtype=torch.int32, device=dev)
+    for _ in range(calls):
+        torch.amax(flush, dim=0, out=flush_max)
+        swa.prefill_global(q, k, v, c["W"], gpos, mode=c["mode"], scale=1.0 / math.sqrt(c["d"]),
+                           out=out, workspace=ws, dilation=c.get("dilation", 1))
+    torch.cuda.synchronize()
+    print("trace workload %d (%s) done" % (wl, c["name"]), flush=True)
+    return 0
+
+
 def summarize_config_counters(paths, wl):
     """Per-dispatch SQ / TA counters of a --pmc-config run (the first, flushed
     dispatch of the prefill kernel), with the derived issue and wait figures."""
@@ -776,6 +800,9 @@ def main():
     ap.add_argument("--summarize-config-counters", nargs="+", metavar="CSV",
                     help="SQ counters of a --pmc-config run (with --config N)")
     ap.add_argument("--config", type=int, default=5, help="configuration of the summary")
+    ap.add_argument("--trace-global", type=int, metavar="N",
+                    help="instead of the benchmark line: 13 flushed calls of the window plus "
+                         "global tokens configuration N (run under rocprofv3 --kernel-trace)")
     ap.add_argument("--summarize-kernel-trace", nargs="+", metavar="CSV",
                     help="per-kernel times of a rocprofv3 --kernel-trace run of the benchmark "
                          "line, without the --warmup steps' dispatches")
@@ -801,6 +828,8 @@ def main():
         return pmc_config(args.pmc_config)
     if args.summarize_config_counters:
         return summarize_config_counters(args.summarize_config_counters, args.config)
+    if args.trace_global:
+        return trace_global(args.trace_global)
     if args.summarize_kernel_trace:
         return summarize_kernel_trace(args.summarize_kernel_trace, args.warmup)
     if args.cpu_oracle:
