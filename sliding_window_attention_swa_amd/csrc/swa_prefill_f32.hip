@@ -1,28 +1,32 @@
-// Sliding-window attention prefill in IEEE fp32 (vector ALU, full-precision
-// products: the fp32 workloads are held to an absolute error of 1e-5).
+// Sliding-window attention prefill in IEEE fp32 (every product and sum in
+// fp32: the fp32 workloads are held to an absolute error of 1e-5).
 //
 // Same definition as the bf16 kernel (robocikowo glossary "Sliding Window
 // Attention", opening definition; Ultralytics glossary, section "Come cresce
 // la finestra con la profondita"): each query row takes the softmax of its
-// in-window logits only.  16 lanes share one query row, each holding d/16
-// dims; a row walks exactly the keys of its own window, one key at a time,
-// with a running maximum and sum.
+// in-window logits only.
+//
+// Plain and dilated windows run on the matrix cores (prefill_f32_mfma_kernel
+// below: v_mfma_f32_32x32x2_f32, the tiled bf16 kernel's decomposition).
+// The chunk and global-token modes keep a vector-ALU kernel in which 16
+// lanes share one query row, each holding d/16 dims, and a row walks exactly
+// the keys of its own window, one key at a time, with a running maximum and
+// sum:
 //
 // Chunked prefill (MODE 2): T is the chunk length and row i is position
 // p + i of its sequence; its keys r = j - p in [max(-p, i-W+1), i] come from
 // ring slot (p + r) mod W when r < 0 (Ultralytics ring-buffer paragraph) and
 // from chunk row r otherwise.
 //
-// Dilated windows (dil > 1; aivaro answer 629, section 4.2): the row takes
-// every dil-th key, j = i - m * dil for m in the plain window's offsets.
-//
-// Global tokens (MODES 5 causal, 6 symmetric; aivaro section 4.3): after its
-// window (dilated when dil > 1) the row also takes each global key outside
-// the window (not after the row when causal).  The global rows themselves
-// are written afterwards by the split-K pass of swa_ring.hip.
+// Global tokens (MODES 5 causal, 6 symmetric; aivaro section 4.3): the row
+// takes its window (dilated when dil > 1: every dil-th key, j = i - m * dil
+// for m in the plain window's offsets; aivaro section 4.2), then each global
+// key outside the window (not after the row when causal).  The global rows
+// themselves are written afterwards by the split-K pass of swa_ring.hip.
 
 #include "swa_device.h"
 #include "swa_launch.h"
+#include "swa_tile_math.h"
 
 namespace swa {
 namespace {
@@ -30,10 +34,10 @@ namespace {
 constexpr int kRowsPerBlock = 16;
 constexpr int kLanesPerRow = 16;
 
-// MODE: 0 causal, 1 symmetric, 2 causal chunk continuing a ring cache
-// (kring/vring/pos/hkv_seq are used by MODE 2 only), 5 causal and 6
-// symmetric window plus the ngl global keys at gpos.  dil: key stride of a
-// dilated window in MODES 0, 1, 5 and 6 (1 otherwise).
+// MODE: 2 causal chunk continuing a ring cache (kring/vring/pos/hkv_seq are
+// used by MODE 2 only), 5 causal and 6 symmetric window plus the ngl global
+// keys at gpos.  dil: key stride of a dilated window in MODES 5 and 6 (1
+// otherwise).
 template <int D, int MODE>
 __global__ __launch_bounds__(256) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
@@ -136,18 +140,291 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
   for (int e = 0; e < DPL; ++e) orow[e] = acc[e] * inv;
 }
 
+// ---------------------------------------------------------------------------
+// Plain and dilated windows on the matrix cores.  The tiled bf16 kernel's
+// decomposition: one workgroup = 128 query rows of one query head (of one
+// residue class mod the dilation, a sequence of its own with row stride
+// dil * d), four waves of 32 rows; 64-key K/V tiles visited only where they
+// meet the block's windows, double-buffered in LDS and filled by direct
+// buffer-to-LDS loads; S^T = K Q^T with one query row per lane.  Products on
+// v_mfma_f32_32x32x2_f32, softmax exact and online per tile (running maximum
+// and sum in fp32, probabilities exp2(s * c - m) with c = scale * log2(e)),
+// O^T += V^T P^T with the fp32 probabilities as they are.
+//
+// The tile's two 32-key blocks are taken one after the other, each with its
+// own online-softmax update.
+//
+// Operand layout.  A 32x32x2 product takes, in lane l, element l / 32 of its
+// step's two-element slice of the reduced dimension.  S^T = K Q^T reduces
+// over dims, assigned to (step, lane half) as d = 8 * (step / 4) + 4 * half +
+// step % 4, so that a lane's operands of four consecutive steps are four
+// consecutive floats: one 16-byte read of its Q row at the start, one of its
+// K row per four steps.  O^T += V^T P^T reduces over keys: step j of a 32-key
+// block takes key 8 * (j / 4) + 4 * half + j % 4, which is exactly score
+// register j of the lane (the result layout of every 32x32 product), so the
+// probabilities are the B operand with no data movement; V^T comes as single
+// floats, V[key][32 * md + l % 32].
+namespace f32m {
+
+constexpr int kBN = tm::kBN;   // keys per tile
+constexpr int kBM = tm::kBM;   // query rows per workgroup
+constexpr int kThreads = 256;  // four waves
+constexpr int kBufferFlags = 0x00020000;  // raw 32-bit buffer access
+
+template <int D>
+struct Geo {
+  static constexpr int ROWB = D * 4;                   // bytes per K/V row in LDS
+  static constexpr int TILEB = kBN * ROWB;             // bytes per tile
+  static constexpr int NLD = TILEB / (kThreads * 16);  // direct loads per thread per tile
+  static constexpr int KQ = D / 8;                     // 16-byte operand groups per lane
+  static constexpr int MD = D / 32;                    // 32-dim output blocks
+};
+
+// XOR swizzle of a K row's 16-byte chunks: the K operand read (16 lanes, 16
+// consecutive rows, one logical chunk) touches every bank group once.  V rows
+// are stored as they are (its single-float reads, 32 consecutive floats of
+// two rows, meet each bank at most twice), so that their addresses differ by
+// constants and need no registers of their own.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  return D == 32 ? ((row >> 1) & 7) : (row & 15);
+}
+
+// Occupancy (waves per SIMD) that the LDS of double-buffered fp32 tiles
+// allows: 128 KB per workgroup at d = 128, 64 KB at d = 64, 32 KB at d = 32.
+template <int D>
+constexpr int kWaves = D == 128 ? 1 : (D == 64 ? 2 : 4);
+
+}  // namespace f32m
+
+template <int D, bool kCausal>
+__global__ __launch_bounds__(f32m::kThreads)
+__attribute__((amdgpu_waves_per_eu(f32m::kWaves<D>, f32m::kWaves<D>)))
+void prefill_f32_mfma_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                             const float* __restrict__ v, float* __restrict__ out, int Tseq,
+                             int W, int Hq, int Hkv, float c, int n_qtiles, int dil) {
+  using namespace f32m;
+  using Gm = Geo<D>;
+  constexpr int ROWB = Gm::ROWB, TILEB = Gm::TILEB, NLD = Gm::NLD, KQ = Gm::KQ, MD = Gm::MD;
+  typedef __attribute__((address_space(3))) void lds_void;
+  __shared__ __attribute__((aligned(1024))) char lds_k0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char lds_v0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char lds_k1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char lds_v1[TILEB];
+
+  // ---- which (query head, residue class, query block) this workgroup owns;
+  // consecutive ids go round-robin to the 8 XCDs: each gets a contiguous range
+  const int G = Hq / Hkv;
+  int id = (int)blockIdx.x;
+  const int nwg = (int)gridDim.x;
+  if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
+  const int hg = id % G;
+  const int rest = id / G;
+  const int qt = rest % n_qtiles;
+  int kvh = rest / n_qtiles;
+  const int cls = kvh % dil;
+  kvh /= dil;
+  const int h = kvh * G + hg;
+  const int T = tm::class_rows(Tseq, cls, dil);  // rows of this residue class
+  const int RS = dil * D;                        // floats between consecutive rows
+  const int q0 = qt * kBM;
+  if (q0 >= T) return;  // a shorter class: nothing to do (uniform over the workgroup)
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int qw0 = q0 + wave * 32;
+  const int qi = qw0 + (lane & 31);  // the query row this lane owns
+
+  const float* qh = q + (size_t)h * Tseq * D + (size_t)cls * D;
+  const float* kh = k + (size_t)kvh * Tseq * D + (size_t)cls * D;
+  const float* vh = v + (size_t)kvh * Tseq * D + (size_t)cls * D;
+
+  const int hw = W >> 1;
+  const int lo = kCausal ? SWA_TM_CAUSAL_BLOCK_LO(q0, W, 0) : SWA_TM_SYM_BLOCK_LO(q0, hw);
+  const int hi = kCausal ? SWA_TM_CAUSAL_BLOCK_HI(q0, T) : SWA_TM_SYM_BLOCK_HI(q0, T, hw);
+  const int kt0 = lo / kBN;
+  const int kt1 = hi / kBN;
+  const bool wave_active = qw0 < T;
+  const int qlast = SWA_TM_WAVE_LAST(qw0, T);
+  const int wlo = SWA_TM_WAVE_LO(kCausal, qw0, W, hw, 0);
+  const int whi = SWA_TM_WAVE_HI(kCausal, qlast, T, hw);
+
+  // ---- the lane's Q row as B operands: group j holds dims 8j + 4*half .. +3
+  float4 qf[KQ];
+#pragma unroll
+  for (int j = 0; j < KQ; ++j) {
+    qf[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (qi < T) qf[j] = *reinterpret_cast<const float4*>(qh + (size_t)qi * RS + 8 * j + 4 * half);
+  }
+
+  // ---- direct tile loads: load j of this thread fills the 16 bytes at LDS
+  // offset (j * kThreads + tid) * 16 (each wave writes 1 KB contiguously) and
+  // fetches the logical chunk the swizzle keeps there; rows past T re-read
+  // row T - 1 (finite, masked)
+  int src_row[NLD], src_koff[NLD];
+#pragma unroll
+  for (int j = 0; j < NLD; ++j) {
+    const int o = tm::load_lds_offset(j, tid, kThreads);
+    const int row = tm::load_row(o, ROWB);
+    src_row[j] = row;
+    src_koff[j] = (tm::load_chunk(o, ROWB) ^ swz<D>(row)) * 16;
+  }
+  auto load_tile = [&](char* Kdst, char* Vdst, int kt) __attribute__((always_inline)) {
+    const int last = tm::tile_last(T, kt);
+    const int RSB = RS * 4;
+    const int bytes = tm::tile_bytes(last, RSB, ROWB);
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kh + (size_t)kt * kBN * RS), 0, bytes, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vh + (size_t)kt * kBN * RS), 0, bytes, kBufferFlags);
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int wbase = (j * kThreads + wave * 64) * 16;
+      const int roff = tm::tile_row_offset(src_row[j], last, RSB);
+      const int koff = roff + src_koff[j];
+      const int voff = roff + tm::load_chunk(tm::load_lds_offset(j, tid, kThreads), ROWB) * 16;
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass mishandles this builtin
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(Kdst + wbase), 16, koff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(Vdst + wbase), 16, voff, 0, 0, 0);
+#else
+      (void)rk, (void)rv, (void)wbase, (void)koff, (void)voff;
+#endif
+    }
+  };
+
+  // per-lane LDS read offsets: K operand group j of LDS row l % 32 (+ the
+  // block's first row; the swizzle repeats every 16 rows), V at row
+  // 4 * half (+ the step's row) and dim l % 32 (+ 32 per output block)
+  int koff[KQ];
+#pragma unroll
+  for (int j = 0; j < KQ; ++j) koff[j] = (lane & 31) * ROWB + (((2 * j + half) ^ swz<D>(lane & 31)) * 16);
+  const int vbase = 4 * half * ROWB + (lane & 31) * 4;
+
+  f32x16 o[MD];
+#pragma unroll
+  for (int md = 0; md < MD; ++md) o[md] = f32x16{};
+  float m = -INFINITY;  // running maximum of the row's scaled scores (log2 units)
+  float l = 0.f;        // this lane's share of the row sum
+
+  // One 32-key block (keys k0 .. k0 + 31, LDS rows kb .. kb + 31 of the
+  // tile): S^T, mask (blocks crossing a window edge or the sequence end),
+  // online softmax, O^T += V^T P^T.  The group barriers interleave each LDS
+  // read with the products it feeds, one group ahead, so that the compiler
+  // does not hoist every read of the block (and spill their registers).
+  auto block = [&](const char* Ks, const char* Vs, int kb, int k0, bool full) __attribute__((always_inline)) {
+    f32x16 sb = f32x16{};
+#pragma unroll
+    for (int j = 0; j < KQ; ++j) {
+      const float4 kq = *reinterpret_cast<const float4*>(Ks + kb * ROWB + koff[j]);
+      sb = __builtin_amdgcn_mfma_f32_32x32x2f32(kq.x, qf[j].x, sb, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_32x32x2f32(kq.y, qf[j].y, sb, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_32x32x2f32(kq.z, qf[j].z, sb, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_32x32x2f32(kq.w, qf[j].w, sb, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int j = 0; j < KQ; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      if (j + 2 < KQ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float t = sb[r] * c;
+      if (!full) {
+        const int key = k0 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (!tm::edge_visible(kCausal, qi, key, T, W, 0)) t = -INFINITY;
+      }
+      sb[r] = t;
+      mx = fmaxf(mx, t);
+    }
+    mx = max_lane_pair(mx);  // lanes l and l^32 hold the same row
+    const float m_new = fmaxf(m, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // a row without keys so far
+    const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[md][r] *= alpha;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sb[r] = __builtin_amdgcn_exp2f(sb[r] - m_use);
+      l += sb[r];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      const int vrow = kb + 8 * (kk >> 2) + (kk & 3);  // + 4 * half, in vbase
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
+        const float va = *reinterpret_cast<const float*>(Vs + vrow * ROWB + 128 * md + vbase);
+        o[md] = __builtin_amdgcn_mfma_f32_32x32x2f32(va, sb[kk], o[md], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * MD, 0);
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      __builtin_amdgcn_sched_group_barrier(0x008, MD, 0);
+      if (kk + 2 < 16) __builtin_amdgcn_sched_group_barrier(0x100, MD, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Wait for this tile's loads (issued during the previous one) and for every
+  // wave to be done with the other stage, refill that stage, consume this one.
+  auto step = [&](const char* Ks, const char* Vs, char* Kn, char* Vn, int kt) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (kt < kt1) load_tile(Kn, Vn, kt + 1);
+    const int k0 = kt * kBN;
+    if (!tm::tile_visited(wave_active, wlo, whi, k0)) return;
+    const bool full = tm::tile_full(kCausal, false, k0, qw0, qlast, T, W, 0);
+    block(Ks, Vs, 0, k0, full);
+    block(Ks, Vs, 32, k0 + 32, full);
+  };
+  load_tile(lds_k0, lds_v0, kt0);
+  for (int kt = kt0; kt <= kt1; kt += 2) {
+    step(lds_k0, lds_v0, lds_k1, lds_v1, kt);
+    if (kt + 1 > kt1) break;
+    step(lds_k1, lds_v1, lds_k0, lds_v0, kt + 1);
+  }
+
+  // ---- epilogue: divide by the row sum and store (the exchange involves
+  // both wave halves, so it precedes the guard)
+  const float l_tot = l + __shfl_xor(l, 32);
+  if (qi < T) {
+    const float inv = 1.0f / l_tot;
+    float* orow = out + (size_t)h * Tseq * D + (size_t)cls * D + (size_t)qi * RS;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        *reinterpret_cast<float4*>(orow + 32 * md + 8 * rq + 4 * half) =
+            make_float4(o[md][4 * rq] * inv, o[md][4 * rq + 1] * inv, o[md][4 * rq + 2] * inv,
+                        o[md][4 * rq + 3] * inv);
+      }
+    }
+  }
+}
+
 template <int D, int MODE>
 hipError_t launch(const void* q, const void* k, const void* v, void* out, int T, int W, int Hq,
                   int Hkv, float scale, int dil, hipStream_t stream) {
-  const int n_rowblocks = (T + kRowsPerBlock - 1) / kRowsPerBlock;
-  const long long nwg = (long long)n_rowblocks * Hq;
-  hipLaunchKernelGGL((prefill_f32_kernel<D, MODE>), dim3((unsigned)nwg),
-                     dim3(kRowsPerBlock * kLanesPerRow), 0,
-                     stream, static_cast<const float*>(q), static_cast<const float*>(k),
-                     static_cast<const float*>(v), static_cast<float*>(out), T, W, Hq, Hkv,
-                     scale, n_rowblocks, static_cast<const float*>(nullptr),
-                     static_cast<const float*>(nullptr), static_cast<const int32_t*>(nullptr), 1,
-                     dil, static_cast<const int32_t*>(nullptr), 0);
+  // residue classes: the longest has ceil(T / dil) rows
+  const int n_qtiles = ((T + dil - 1) / dil + f32m::kBM - 1) / f32m::kBM;
+  const long long nwg = (long long)n_qtiles * Hq * dil;
+  hipLaunchKernelGGL((prefill_f32_mfma_kernel<D, MODE == 0>), dim3((unsigned)nwg),
+                     dim3(f32m::kThreads), 0, stream, static_cast<const float*>(q),
+                     static_cast<const float*>(k), static_cast<const float*>(v),
+                     static_cast<float*>(out), T, W, Hq, Hkv, scale * kLog2e, n_qtiles, dil);
   return hipGetLastError();
 }
 

@@ -224,6 +224,47 @@ def test_scale_argument_and_negative_scale(swa):
         assert_parity(got, ref, "bf16", "scale=%g" % scale)
 
 
+# fp32 on the matrix cores: plain windows spanning many 64-key tiles and
+# 128-row blocks, with ragged tails, every row against the oracle
+F32_TILED = [
+    # (mode, T, W, B, Hq, Hkv, d)
+    (0, 2000, 700, 1, 4, 2, 128),
+    (1, 1500, 600, 1, 2, 2, 64),
+    (0, 1100, 300, 2, 4, 1, 32),
+    (1, 777, 1500, 1, 3, 1, 128),
+    (0, 4100, 4096, 1, 2, 1, 64),
+]
+
+
+@pytest.mark.parametrize("mode,T,W,B,Hq,Hkv,d", F32_TILED)
+def test_prefill_f32_many_tiles(swa, mode, T, W, B, Hq, Hkv, d):
+    print("prefill f32 tiled", dict(mode=mode, T=T, W=W, B=B, Hq=Hq, Hkv=Hkv, d=d), flush=True)
+    q, k, v = small_inputs(1300 + T + W + d, B, Hq, Hkv, T, d, "f32")
+    scale = 1 / math.sqrt(d)
+    got = to_f64(run(swa, q, k, v, W, mode))
+    ref = oracle.attention_banded(q.values, k.values, v.values, W, mode, scale)
+    assert_parity(got, ref, "f32", "prefill f32 mode=%d T=%d W=%d d=%d" % (mode, T, W, d))
+
+
+def test_prefill_f32_mistral_shape_sampled(swa):
+    """Mistral-7B's window and sequence (T=16384, W=4096, d=128) in fp32 with
+    four query heads on one KV head: edge and random rows of every head."""
+    T, W, d, Hq = 16384, 4096, 128, 4
+    scale = 1 / math.sqrt(d)
+    q, k, v = small_inputs(1400, 1, Hq, 1, T, d, "f32")
+    got = to_f64(run(swa, q, k, v, W, 0))
+    rng = np.random.default_rng(1401)
+    edge = [0, 1, 63, 64, 127, 128, W - 2, W - 1, W, W + 1, T // 2, T - 129, T - 128, T - 1]
+    sampled_got, sampled_ref = [], []
+    for h in range(Hq):
+        rows = sorted(set(edge) | set(rng.integers(0, T, 16).tolist()))
+        sampled_ref.append(oracle.attention_rows(q.values, k.values, v.values, W, 0, scale, 0, h,
+                                                 rows))
+        sampled_got.append(got[0, h, rows])
+    assert_parity(np.concatenate(sampled_got), np.concatenate(sampled_ref), "f32",
+                  "fp32 Mistral-shape sampled rows")
+
+
 # ------------------------------------------------------------ full sizes
 
 def test_tinymistral_full(swa):

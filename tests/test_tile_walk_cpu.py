@@ -9,8 +9,8 @@ data (a clamped row), any key counted twice, and per query row the set of
 keys it counts.  Here every row's set is compared with the fp64 oracle's
 mask for that row: the plain causal and symmetric windows, the dilated
 windows (dilation above T included), the chunk continuing a ring, the window
-plus global tokens (also dilated), the short-window kernel and the
-global-row kernel.  No GPU is involved.
+plus global tokens (also dilated), the short-window kernel, the global-row
+kernel and the fp32 matrix-core kernel.  No GPU is involved.
 """
 
 import os
@@ -135,6 +135,22 @@ def test_dilated_windows(walker, mode):
     res = run(walker, ["tiled %d %d %d %d 0 %d 0" % (kmode, T, W, dil, D) for T, W, dil, D in shapes])
     for (T, W, dil, D), r in zip(shapes, res):
         check(r, expect_rows(oracle.dilated_mask(T, W, mode, dil)), ("dilated", mode, T, W, dil))
+
+
+@pytest.mark.parametrize("mode", [CAUSAL, SYMMETRIC])
+def test_fp32_matrix_core_kernel(walker, mode):
+    """The fp32 matrix-core kernel (4-byte rows, plain and dilated windows,
+    edge tiles masked by the direct test): each row counts exactly its
+    window, loads stay inside their tiles and class rows."""
+    shapes = [(T, W, 1, D) for (m, T, W, D) in plain_shapes() if m == mode]
+    for T in (1, 64, 129, 300, 513):
+        for W in (1, 33, 65, 300):
+            for dil in (2, 5, T + 3):
+                shapes.append((T, W, dil, 32 if (T + W) % 3 == 0 else (64 if (T + W) % 3 == 1 else 128)))
+    res = run(walker, ["tiledf32 %d %d %d %d %d" % (mode, T, W, dil, D) for T, W, dil, D in shapes])
+    for (T, W, dil, D), r in zip(shapes, res):
+        want = oracle.window_mask(T, W, mode) if dil == 1 else oracle.dilated_mask(T, W, mode, dil)
+        check(r, expect_rows(want), ("fp32", mode, T, W, dil, D))
 
 
 def chunk_window(n, W, p):

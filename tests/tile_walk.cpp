@@ -1,4 +1,4 @@
-// CPU walk of the bf16 prefill kernels' index arithmetic, built from the same
+// CPU walk of the prefill kernels' index arithmetic, built from the same
 // header the kernels use (swa_tile_math.h).  For each shape read from stdin
 // it replays the kernels' loops over workgroups, waves, lanes and tiles and
 // prints
@@ -13,6 +13,7 @@
 //
 // Input lines (one shape each):
 //   tiled MODE Tseq W dil pstart D G g_1 .. g_G
+//   tiledf32 MODE Tseq W dil D       (the fp32 matrix-core kernel, MODE 0/1)
 //   short MODE T W D
 //   grows MODE T D G g_1 .. g_G
 // MODE of "tiled" is the tiled kernel's: 0 causal, 1 symmetric, 2 causal
@@ -56,8 +57,12 @@ void count(Keys& keys, long long row, long long key) {
   if (!keys[row].insert(key).second) std::printf("DUP %lld %lld\n", row, key);
 }
 
-// The tiled kernel (prefill_bf16_kernel) for one query head.
-void walk_tiled(int MODE, int Tseq, int W, int dil, int pstart, int D, const std::vector<int>& gpos) {
+// The tiled kernel (prefill_bf16_kernel) for one query head; with f32, the
+// fp32 matrix-core kernel (prefill_f32_mfma_kernel): 4-byte elements, plain
+// and dilated windows only, every tile crossing an edge masked by the direct
+// test.
+void walk_tiled(int MODE, int Tseq, int W, int dil, int pstart, int D, const std::vector<int>& gpos,
+                bool f32 = false) {
   const bool kCausal = MODE != 1 && MODE != 4 && MODE != 6 && MODE != 8;
   const bool kChunk = MODE == 2;
   const bool kDil = MODE == 3 || MODE == 4 || MODE == 7 || MODE == 8;
@@ -65,7 +70,7 @@ void walk_tiled(int MODE, int Tseq, int W, int dil, int pstart, int D, const std
   if (!kDil) dil = 1;
   if (!kChunk) pstart = 0;
   const int ngl = kGlobal ? (int)gpos.size() : 0;
-  const int ROWB = D * 2;
+  const int ROWB = D * (f32 ? 4 : 2);
   const int TILEB = tw::kBN * ROWB;
   const int kThreads = 256;
   const int NLD = TILEB / (kThreads * 16);
@@ -156,7 +161,7 @@ void walk_tiled(int MODE, int Tseq, int W, int dil, int pstart, int D, const std
             // kernel branches on it (a block no row sees is skipped, a block
             // every row sees is taken unmasked)
             int cls_blk[2] = {tw::kSymSome, tw::kSymSome};
-            if (!full && !kCausal && tw::sym_blocks_classified(D)) {
+            if (!f32 && !full && !kCausal && tw::sym_blocks_classified(D)) {
               cls_blk[0] = tw::sym_block_class(k0, qw0, qlast, T, W);
               cls_blk[1] = tw::sym_block_class(k0 + 32, qw0, qlast, T, W);
               // a lone block is always masked
@@ -172,6 +177,8 @@ void walk_tiled(int MODE, int Tseq, int W, int dil, int pstart, int D, const std
                 bool ok;
                 if (full) {
                   ok = true;
+                } else if (f32) {
+                  ok = tw::edge_visible(kCausal, qi, key, T, W, 0);
                 } else if (!kCausal && cls_blk[mb] == tw::kSymAll) {
                   ok = true;
                 } else if (!kCausal) {
@@ -346,6 +353,13 @@ int main() {
         if (std::scanf("%d", &g[i]) != 1) return 2;
       swz_check(D);
       walk_tiled(mode, Tseq, W, dil, pstart, D, g);
+    } else if (k == "tiledf32") {
+      int mode, Tseq, W, dil, D;
+      if (std::scanf("%d %d %d %d %d", &mode, &Tseq, &W, &dil, &D) != 5) return 2;
+      if (mode != 0 && mode != 1) return 2;
+      swz_check(D);
+      // the kernel runs dilations > 1 as the residue-class walk of modes 3/4
+      walk_tiled(dil > 1 ? mode + 3 : mode, Tseq, W, dil, 0, D, {}, true);
     } else if (k == "short") {
       int mode, T, W, D;
       if (std::scanf("%d %d %d %d", &mode, &T, &W, &D) != 4) return 2;
