@@ -6,17 +6,12 @@
 // la finestra con la profondita"): each query row takes the softmax of its
 // in-window logits only.
 //
-// Plain and dilated windows run on the matrix cores (prefill_f32_mfma_kernel
-// below: v_mfma_f32_32x32x2_f32, the tiled bf16 kernel's decomposition).
-// The chunk and global-token modes keep a vector-ALU kernel in which 16
-// lanes share one query row, each holding d/16 dims, and a row walks exactly
-// the keys of its own window, one key at a time, with a running maximum and
-// sum:
-//
-// Chunked prefill (MODE 2): T is the chunk length and row i is position
-// p + i of its sequence; its keys r = j - p in [max(-p, i-W+1), i] come from
-// ring slot (p + r) mod W when r < 0 (Ultralytics ring-buffer paragraph) and
-// from chunk row r otherwise.
+// Plain and dilated windows and the chunk continuing a ring cache run on the
+// matrix cores (prefill_f32_mfma_kernel below: v_mfma_f32_32x32x2_f32, the
+// tiled bf16 kernel's decomposition).  The global-token modes keep a
+// vector-ALU kernel in which 16 lanes share one query row, each holding d/16
+// dims, and a row walks exactly the keys of its own window, one key at a
+// time, with a running maximum and sum:
 //
 // Global tokens (MODES 5 causal, 6 symmetric; aivaro section 4.3): the row
 // takes its window (dilated when dil > 1: every dil-th key, j = i - m * dil
@@ -34,19 +29,16 @@ namespace {
 constexpr int kRowsPerBlock = 16;
 constexpr int kLanesPerRow = 16;
 
-// MODE: 2 causal chunk continuing a ring cache (kring/vring/pos/hkv_seq are
-// used by MODE 2 only), 5 causal and 6 symmetric window plus the ngl global
-// keys at gpos.  dil: key stride of a dilated window in MODES 5 and 6 (1
-// otherwise).
+// MODE: 5 causal and 6 symmetric window plus the ngl global keys at gpos.
+// dil: key stride of the (dilated) window.
 template <int D, int MODE>
 __global__ __launch_bounds__(256) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ out, int T, int W, int Hq, int Hkv, float scale, int n_rowblocks,
-    const float* __restrict__ kring, const float* __restrict__ vring,
-    const int32_t* __restrict__ pos, int hkv_seq, int dil, const int32_t* __restrict__ gpos,
-    int ngl) {
+    int dil, const int32_t* __restrict__ gpos, int ngl) {
+  static_assert(MODE == 5 || MODE == 6, "the window plus global tokens");
   constexpr int DPL = D / kLanesPerRow;
-  constexpr bool kCausal = MODE != 1 && MODE != 6;
+  constexpr bool kCausal = MODE == 5;
   const int h = blockIdx.x / n_rowblocks;
   const int i = (blockIdx.x % n_rowblocks) * kRowsPerBlock + threadIdx.x / kLanesPerRow;
   const int c = threadIdx.x % kLanesPerRow;
@@ -55,17 +47,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
   const float* qrow = q + ((size_t)h * T + i) * D + c * DPL;
   const float* kh = k + (size_t)kvh * T * D + c * DPL;
   const float* vh = v + (size_t)kvh * T * D + c * DPL;
-
   float* orow = out + ((size_t)h * T + i) * D + c * DPL;
-  int pstart = 0;  // chunk mode: position of the chunk's first token
-  if constexpr (MODE == 2) {
-    pstart = pos[kvh / hkv_seq];
-    if (pstart < 0) {  // inactive sequence: zero rows
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) orow[e] = 0.f;
-      return;
-    }
-  }
 
   float qv[DPL], acc[DPL];
 #pragma unroll
@@ -74,24 +56,12 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
     acc[e] = 0.f;
   }
   int lo, hi;
-  if (MODE == 2) {
-    lo = max(-pstart, i - W + 1);
-    hi = i;
-  } else if (kCausal) {
+  if (kCausal) {
     lo = i - dil * min(W - 1, i / dil);
     hi = i;
   } else {
     lo = i - dil * min(W / 2, i / dil);
     hi = i + dil * min(W / 2, (T - 1 - i) / dil);
-  }
-  // chunk mode: ring slot of key lo (pstart + lo >= 0), advanced with the key
-  unsigned slot = 0;
-  const float* krh = nullptr;
-  const float* vrh = nullptr;
-  if constexpr (MODE == 2) {
-    slot = (unsigned)(pstart + lo) % (unsigned)W;
-    krh = kring + (size_t)kvh * W * D + c * DPL;
-    vrh = vring + (size_t)kvh * W * D + c * DPL;
   }
   float m = -INFINITY, l = 0.f;
   // one key: score, running maximum and sum, accumulate its value row
@@ -110,30 +80,16 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
     for (int e = 0; e < DPL; ++e) acc[e] = fmaf(p, vr[e], acc[e] * alpha);
     m = m_new;
   };
-  for (int j = lo; j <= hi; j += dil) {
-    const float* kr;
-    const float* vr;
-    if (MODE == 2 && j < 0) {  // a ring position
-      kr = krh + (size_t)slot * D;
-      vr = vrh + (size_t)slot * D;
-      slot = slot + 1 == (unsigned)W ? 0u : slot + 1;
-    } else {
-      kr = kh + (size_t)j * D;
-      vr = vh + (size_t)j * D;
-    }
-    visit(kr, vr);
-  }
-  if constexpr (MODE == 5 || MODE == 6) {
-    for (int t = 0; t < ngl; ++t) {
-      const int gp = gpos[t];
-      const int diff = i - gp;
-      // in the (dilated) window: on the row's grid, within the window's offsets
-      const int m = diff / dil;
-      const bool in_window = diff == m * dil &&
-                             (kCausal ? (m >= 0 && m < W) : (m >= -(W / 2) && m <= W / 2));
-      if (gp < 0 || gp >= T || in_window || (kCausal && diff < 0)) continue;
-      visit(kh + (size_t)gp * D, vh + (size_t)gp * D);
-    }
+  for (int j = lo; j <= hi; j += dil) visit(kh + (size_t)j * D, vh + (size_t)j * D);
+  for (int t = 0; t < ngl; ++t) {
+    const int gp = gpos[t];
+    const int diff = i - gp;
+    // in the (dilated) window: on the row's grid, within the window's offsets
+    const int m = diff / dil;
+    const bool in_window = diff == m * dil &&
+                           (kCausal ? (m >= 0 && m < W) : (m >= -(W / 2) && m <= W / 2));
+    if (gp < 0 || gp >= T || in_window || (kCausal && diff < 0)) continue;
+    visit(kh + (size_t)gp * D, vh + (size_t)gp * D);
   }
   const float inv = 1.0f / l;
 #pragma unroll
@@ -141,7 +97,8 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Plain and dilated windows on the matrix cores.  The tiled bf16 kernel's
+// Plain and dilated windows, and the chunk continuing a ring cache (Ultralytics
+// ring-buffer paragraph), on the matrix cores.  The tiled bf16 kernel's
 // decomposition: one workgroup = 128 query rows of one query head (of one
 // residue class mod the dilation, a sequence of its own with row stride
 // dil * d), four waves of 32 rows; 64-key K/V tiles visited only where they
@@ -149,7 +106,11 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
 // buffer-to-LDS loads; S^T = K Q^T with one query row per lane.  Products on
 // v_mfma_f32_32x32x2_f32, softmax exact and online per tile (running maximum
 // and sum in fp32, probabilities exp2(s * c - m) with c = scale * log2(e)),
-// O^T += V^T P^T with the fp32 probabilities as they are.
+// O^T += V^T P^T with the fp32 probabilities as they are.  The chunk mode
+// (MODE 2) is the causal kernel in key coordinates relative to the chunk's
+// first token at position p, as in the bf16 kernel: key r < 0 is position
+// p + r, read from ring slot (p + r) mod W; tiles are aligned to the chunk
+// start, so a tile is wholly ring or wholly chunk.
 //
 // The tile's two 32-key blocks are taken one after the other, each with its
 // own online-softmax update.
@@ -191,19 +152,28 @@ __device__ __forceinline__ int swz(int row) {
 }
 
 // Occupancy (waves per SIMD) that the LDS of double-buffered fp32 tiles
-// allows: 128 KB per workgroup at d = 128, 64 KB at d = 64, 32 KB at d = 32.
-template <int D>
-constexpr int kWaves = D == 128 ? 1 : (D == 64 ? 2 : 4);
+// allows: 128 KB per workgroup at d = 128, 64 KB at d = 64, 32 KB at d = 32
+// (the chunk mode at d = 32 takes three, whose registers hold its ring
+// addressing without spills).
+template <int D, int MODE>
+constexpr int kWaves = D == 128 ? 1 : (D == 64 ? 2 : (MODE == 2 ? 3 : 4));
 
 }  // namespace f32m
 
-template <int D, bool kCausal>
+// MODE: 0 causal, 1 symmetric (dil: key stride of a dilated window), 2 causal
+// chunk continuing a ring cache (Tseq is then the chunk length; kring, vring,
+// pos and hkv_seq are used by MODE 2 only).
+template <int D, int MODE>
 __global__ __launch_bounds__(f32m::kThreads)
-__attribute__((amdgpu_waves_per_eu(f32m::kWaves<D>, f32m::kWaves<D>)))
+__attribute__((amdgpu_waves_per_eu(f32m::kWaves<D, MODE>, f32m::kWaves<D, MODE>)))
 void prefill_f32_mfma_kernel(const float* __restrict__ q, const float* __restrict__ k,
                              const float* __restrict__ v, float* __restrict__ out, int Tseq,
-                             int W, int Hq, int Hkv, float c, int n_qtiles, int dil) {
+                             int W, int Hq, int Hkv, float c, int n_qtiles, int dil,
+                             const float* __restrict__ kring, const float* __restrict__ vring,
+                             const int32_t* __restrict__ pos, int hkv_seq) {
   using namespace f32m;
+  constexpr bool kCausal = MODE != 1;
+  constexpr bool kChunk = MODE == 2;
   using Gm = Geo<D>;
   constexpr int ROWB = Gm::ROWB, TILEB = Gm::TILEB, NLD = Gm::NLD, KQ = Gm::KQ, MD = Gm::MD;
   typedef __attribute__((address_space(3))) void lds_void;
@@ -241,14 +211,31 @@ void prefill_f32_mfma_kernel(const float* __restrict__ q, const float* __restric
   const float* kh = k + (size_t)kvh * Tseq * D + (size_t)cls * D;
   const float* vh = v + (size_t)kvh * Tseq * D + (size_t)cls * D;
 
+  // chunk mode: position of the chunk's first token; the lowest key is -pstart
+  int pstart = 0;
+  if constexpr (kChunk) {
+    pstart = pos[kvh / hkv_seq];
+    if (pstart < 0) {  // inactive sequence: zero rows (uniform over the workgroup)
+      if (qi < T) {
+        float* orow = out + ((size_t)h * Tseq + qi) * D;
+#pragma unroll
+        for (int md = 0; md < Geo<D>::MD; ++md)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq)
+            *reinterpret_cast<float4*>(orow + 32 * md + 8 * rq + 4 * half) = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      return;
+    }
+  }
+
   const int hw = W >> 1;
-  const int lo = kCausal ? SWA_TM_CAUSAL_BLOCK_LO(q0, W, 0) : SWA_TM_SYM_BLOCK_LO(q0, hw);
+  const int lo = kCausal ? SWA_TM_CAUSAL_BLOCK_LO(q0, W, pstart) : SWA_TM_SYM_BLOCK_LO(q0, hw);
   const int hi = kCausal ? SWA_TM_CAUSAL_BLOCK_HI(q0, T) : SWA_TM_SYM_BLOCK_HI(q0, T, hw);
-  const int kt0 = lo / kBN;
+  const int kt0 = kChunk ? tm::floor_tile(lo) : lo / kBN;
   const int kt1 = hi / kBN;
   const bool wave_active = qw0 < T;
   const int qlast = SWA_TM_WAVE_LAST(qw0, T);
-  const int wlo = SWA_TM_WAVE_LO(kCausal, qw0, W, hw, 0);
+  const int wlo = SWA_TM_WAVE_LO(kCausal, qw0, W, hw, pstart);
   const int whi = SWA_TM_WAVE_HI(kCausal, qlast, T, hw);
 
   // ---- the lane's Q row as B operands: group j holds dims 8j + 4*half .. +3
@@ -272,6 +259,31 @@ void prefill_f32_mfma_kernel(const float* __restrict__ q, const float* __restric
     src_koff[j] = (tm::load_chunk(o, ROWB) ^ swz<D>(row)) * 16;
   }
   auto load_tile = [&](char* Kdst, char* Vdst, int kt) __attribute__((always_inline)) {
+    if constexpr (kChunk) {
+      if (kt < 0) {
+        // a ring tile: key r = kt * kBN + row is position pstart + r, in slot
+        // (pstart + r) mod W; rows before position 0 (never in a window)
+        // re-read position 0, which every sequence with pstart >= 1 has written
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(kring + (size_t)kvh * W * D), 0, W * ROWB, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(vring + (size_t)kvh * W * D), 0, W * ROWB, kBufferFlags);
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) {
+          const int wbase = (j * kThreads + wave * 64) * 16;
+          const int roff = (int)tm::ring_slot(pstart, kt * kBN, src_row[j], W) * ROWB;
+          const int koff = roff + src_koff[j];
+          const int voff = roff + tm::load_chunk(tm::load_lds_offset(j, tid, kThreads), ROWB) * 16;
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass mishandles this builtin
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(Kdst + wbase), 16, koff, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(Vdst + wbase), 16, voff, 0, 0, 0);
+#else
+          (void)rk, (void)rv, (void)wbase, (void)koff, (void)voff;
+#endif
+        }
+        return;
+      }
+    }
     const int last = tm::tile_last(T, kt);
     const int RSB = RS * 4;
     const int bytes = tm::tile_bytes(last, RSB, ROWB);
@@ -337,7 +349,7 @@ void prefill_f32_mfma_kernel(const float* __restrict__ q, const float* __restric
       float t = sb[r] * c;
       if (!full) {
         const int key = k0 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (!tm::edge_visible(kCausal, qi, key, T, W, 0)) t = -INFINITY;
+        if (!tm::edge_visible(kCausal, qi, key, T, W, pstart)) t = -INFINITY;
       }
       sb[r] = t;
       mx = fmaxf(mx, t);
@@ -386,7 +398,7 @@ void prefill_f32_mfma_kernel(const float* __restrict__ q, const float* __restric
     if (kt < kt1) load_tile(Kn, Vn, kt + 1);
     const int k0 = kt * kBN;
     if (!tm::tile_visited(wave_active, wlo, whi, k0)) return;
-    const bool full = tm::tile_full(kCausal, false, k0, qw0, qlast, T, W, 0);
+    const bool full = tm::tile_full(kCausal, kChunk, k0, qw0, qlast, T, W, pstart);
     block(Ks, Vs, 0, k0, full);
     block(Ks, Vs, 32, k0 + 32, full);
   };
@@ -421,10 +433,12 @@ hipError_t launch(const void* q, const void* k, const void* v, void* out, int T,
   // residue classes: the longest has ceil(T / dil) rows
   const int n_qtiles = ((T + dil - 1) / dil + f32m::kBM - 1) / f32m::kBM;
   const long long nwg = (long long)n_qtiles * Hq * dil;
-  hipLaunchKernelGGL((prefill_f32_mfma_kernel<D, MODE == 0>), dim3((unsigned)nwg),
+  hipLaunchKernelGGL((prefill_f32_mfma_kernel<D, MODE>), dim3((unsigned)nwg),
                      dim3(f32m::kThreads), 0, stream, static_cast<const float*>(q),
                      static_cast<const float*>(k), static_cast<const float*>(v),
-                     static_cast<float*>(out), T, W, Hq, Hkv, scale * kLog2e, n_qtiles, dil);
+                     static_cast<float*>(out), T, W, Hq, Hkv, scale * kLog2e, n_qtiles, dil,
+                     static_cast<const float*>(nullptr), static_cast<const float*>(nullptr),
+                     static_cast<const int32_t*>(nullptr), 1);
   return hipGetLastError();
 }
 
@@ -432,14 +446,13 @@ template <int D>
 hipError_t launch_chunk(const void* q, const void* k, const void* v, const void* k_ring,
                         const void* v_ring, const int32_t* pos, void* out, int B, int n, int W,
                         int Hq, int Hkv, float scale, hipStream_t stream) {
-  const int n_rowblocks = (n + kRowsPerBlock - 1) / kRowsPerBlock;
-  const long long nwg = (long long)n_rowblocks * Hq * B;
-  hipLaunchKernelGGL((prefill_f32_kernel<D, 2>), dim3((unsigned)nwg),
-                     dim3(kRowsPerBlock * kLanesPerRow), 0, stream, static_cast<const float*>(q),
-                     static_cast<const float*>(k), static_cast<const float*>(v),
-                     static_cast<float*>(out), n, W, Hq * B, Hkv * B, scale, n_rowblocks,
-                     static_cast<const float*>(k_ring), static_cast<const float*>(v_ring), pos,
-                     Hkv, 1, static_cast<const int32_t*>(nullptr), 0);
+  const int n_qtiles = (n + f32m::kBM - 1) / f32m::kBM;
+  const long long nwg = (long long)n_qtiles * Hq * B;
+  hipLaunchKernelGGL((prefill_f32_mfma_kernel<D, 2>), dim3((unsigned)nwg), dim3(f32m::kThreads), 0,
+                     stream, static_cast<const float*>(q), static_cast<const float*>(k),
+                     static_cast<const float*>(v), static_cast<float*>(out), n, W, Hq * B, Hkv * B,
+                     scale * kLog2e, n_qtiles, 1, static_cast<const float*>(k_ring),
+                     static_cast<const float*>(v_ring), pos, Hkv);
   return hipGetLastError();
 }
 
@@ -452,9 +465,7 @@ hipError_t launch_global(const void* q, const void* k, const void* v, void* out,
   hipLaunchKernelGGL((prefill_f32_kernel<D, MODE>), dim3((unsigned)nwg),
                      dim3(kRowsPerBlock * kLanesPerRow), 0, stream, static_cast<const float*>(q),
                      static_cast<const float*>(k), static_cast<const float*>(v),
-                     static_cast<float*>(out), T, W, Hq, Hkv, scale, n_rowblocks,
-                     static_cast<const float*>(nullptr), static_cast<const float*>(nullptr),
-                     static_cast<const int32_t*>(nullptr), 1, dil, gpos, ngl);
+                     static_cast<float*>(out), T, W, Hq, Hkv, scale, n_rowblocks, dil, gpos, ngl);
   return hipGetLastError();
 }
 

@@ -118,6 +118,23 @@ def test_prefill_chunk_small(swa, dtype, B, Hq, Hkv, n, W, d, pos):
         assert np.all(got[b] == 0.0)
 
 
+def test_prefill_chunk_f32_many_tiles(swa):
+    """fp32 chunks on the matrix cores over many ring and chunk tiles: a
+    2000-slot ring, 600-token chunks at positions far past one ring turn and
+    just after the start, every row against the oracle (unwritten slots
+    poisoned)."""
+    B, Hq, Hkv, n, W, d = 2, 4, 2, 600, 2000, 128
+    q, k, v, kr, vr, _ = si.chunk_inputs(6, B=B, Hq=Hq, Hkv=Hkv, n=n, W=W, d=d, dtype="f32")
+    pos = np.array([5000, 300], dtype=np.int32)
+    kr, vr = poison_unwritten(kr, pos, W), poison_unwritten(vr, pos, W)
+    out = swa.prefill_chunk(to_device(q), to_device(k), to_device(v), to_device(kr),
+                            to_device(vr), torch.from_numpy(pos).cuda())
+    torch.cuda.synchronize()
+    ref = oracle.prefill_chunk(q.values, k.values, v.values, kr.values, vr.values, pos, W,
+                               1 / math.sqrt(d))
+    assert_parity(to_f64(out), ref, "f32", "fp32 chunk over many tiles")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_chunked_serving_equals_prefill(swa, dtype):
     """Feed a T=700 sequence (GQA 8/2, d=64, W=96) in uneven chunks: each

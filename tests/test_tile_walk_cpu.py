@@ -147,7 +147,7 @@ def test_fp32_matrix_core_kernel(walker, mode):
         for W in (1, 33, 65, 300):
             for dil in (2, 5, T + 3):
                 shapes.append((T, W, dil, 32 if (T + W) % 3 == 0 else (64 if (T + W) % 3 == 1 else 128)))
-    res = run(walker, ["tiledf32 %d %d %d %d %d" % (mode, T, W, dil, D) for T, W, dil, D in shapes])
+    res = run(walker, ["tiledf32 %d %d %d %d 0 %d" % (mode, T, W, dil, D) for T, W, dil, D in shapes])
     for (T, W, dil, D), r in zip(shapes, res):
         want = oracle.window_mask(T, W, mode) if dil == 1 else oracle.dilated_mask(T, W, mode, dil)
         check(r, expect_rows(want), ("fp32", mode, T, W, dil, D))
@@ -175,6 +175,10 @@ def test_chunk_continuing_a_ring(walker):
     res = run(walker, ["tiled 2 %d %d 1 %d %d 0" % (n, W, p, D) for n, W, p, D in shapes])
     for (n, W, p, D), r in zip(shapes, res):
         check(r, chunk_window(n, W, p), ("chunk", n, W, p))
+    # the fp32 matrix-core kernel's chunk mode (4-byte rows, direct masks)
+    res = run(walker, ["tiledf32 2 %d %d 1 %d %d" % (n, W, p, D) for n, W, p, D in shapes])
+    for (n, W, p, D), r in zip(shapes, res):
+        check(r, chunk_window(n, W, p), ("chunk fp32", n, W, p))
 
 
 GLOBALS = [[0], [0, 1, 2, 3, 4, 5, 6, 7], [3, 40, 41, 200], [10, 77, 150, 299, 500],

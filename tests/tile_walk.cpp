@@ -13,7 +13,7 @@
 //
 // Input lines (one shape each):
 //   tiled MODE Tseq W dil pstart D G g_1 .. g_G
-//   tiledf32 MODE Tseq W dil D       (the fp32 matrix-core kernel, MODE 0/1)
+//   tiledf32 MODE Tseq W dil pstart D   (the fp32 matrix-core kernel, MODE 0/1/2)
 //   short MODE T W D
 //   grows MODE T D G g_1 .. g_G
 // MODE of "tiled" is the tiled kernel's: 0 causal, 1 symmetric, 2 causal
@@ -59,8 +59,8 @@ void count(Keys& keys, long long row, long long key) {
 
 // The tiled kernel (prefill_bf16_kernel) for one query head; with f32, the
 // fp32 matrix-core kernel (prefill_f32_mfma_kernel): 4-byte elements, plain
-// and dilated windows only, every tile crossing an edge masked by the direct
-// test.
+// and dilated windows and the chunk mode, every tile crossing an edge masked
+// by the direct test.
 void walk_tiled(int MODE, int Tseq, int W, int dil, int pstart, int D, const std::vector<int>& gpos,
                 bool f32 = false) {
   const bool kCausal = MODE != 1 && MODE != 4 && MODE != 6 && MODE != 8;
@@ -178,7 +178,7 @@ void walk_tiled(int MODE, int Tseq, int W, int dil, int pstart, int D, const std
                 if (full) {
                   ok = true;
                 } else if (f32) {
-                  ok = tw::edge_visible(kCausal, qi, key, T, W, 0);
+                  ok = tw::edge_visible(kCausal, qi, key, T, W, pstart);
                 } else if (!kCausal && cls_blk[mb] == tw::kSymAll) {
                   ok = true;
                 } else if (!kCausal) {
@@ -354,12 +354,12 @@ int main() {
       swz_check(D);
       walk_tiled(mode, Tseq, W, dil, pstart, D, g);
     } else if (k == "tiledf32") {
-      int mode, Tseq, W, dil, D;
-      if (std::scanf("%d %d %d %d %d", &mode, &Tseq, &W, &dil, &D) != 5) return 2;
-      if (mode != 0 && mode != 1) return 2;
+      int mode, Tseq, W, dil, pstart, D;
+      if (std::scanf("%d %d %d %d %d %d", &mode, &Tseq, &W, &dil, &pstart, &D) != 6) return 2;
+      if (mode < 0 || mode > 2) return 2;
       swz_check(D);
       // the kernel runs dilations > 1 as the residue-class walk of modes 3/4
-      walk_tiled(dil > 1 ? mode + 3 : mode, Tseq, W, dil, 0, D, {}, true);
+      walk_tiled(mode < 2 && dil > 1 ? mode + 3 : mode, Tseq, W, dil, pstart, D, {}, true);
     } else if (k == "short") {
       int mode, T, W, D;
       if (std::scanf("%d %d %d %d", &mode, &T, &W, &D) != 4) return 2;
