@@ -41,6 +41,7 @@ import swa_inputs as si  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 matrix peak
 METRIC = "SWA prefill in-window TFLOP/s + decode KV-read GB/s, % of MI355X peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_mistral7b_traffic.md")
 COPY_BYTES = 256 << 20  # calibration copy: reads and writes this many bytes
@@ -753,6 +754,40 @@ def all_configs(reps, peaks_only=False):
                     "frac_roofline": round(t_roof / ms, 3),
                     "frac_measured": meas(0, bytes_, ms)}
     print(json.dumps(row), flush=True)
+    del q, k, v, kr, vr, out
+
+    # fp32 inputs (no named configuration is fp32 beyond the 16-token toy):
+    # the Mistral-7B and Longformer prefills and the Mistral-7B chunk in fp32,
+    # against the fp32 matrix-core roofline (4-byte elements)
+    def fp32_row(name, kernel, flops, bytes_, fn):
+        t_roof = max(flops / (PEAK_FP32_MFMA_TFLOPS * 1e12), bytes_ / (PEAK_HBM_GBS * 1e9)) * 1e3
+        bound = "mfma" if flops / PEAK_FP32_MFMA_TFLOPS / 1e12 >= bytes_ / PEAK_HBM_GBS / 1e9 else "hbm"
+        row = {"config": name, "kernel": kernel, "bound": bound, "roofline_ms": round(t_roof, 5),
+               "peak_tflops": PEAK_FP32_MFMA_TFLOPS}
+        for tag, fl in (("warm", False), ("flushed", True)):
+            ms = timed(fn, fl)
+            row[tag] = {"ms": round(ms, 5), "tflops": round(flops / ms / 1e9, 1),
+                        "gbs": round(bytes_ / ms / 1e6, 1), "frac_roofline": round(t_roof / ms, 3)}
+        print(json.dumps(row), flush=True)
+
+    for wl in (3, 5):
+        c = si.WORKLOADS[wl]
+        q, k, v = (si.to_torch(t, dev) for t in si.prefill_inputs(wl, dtype="f32"))
+        out = torch.empty_like(q)
+        fn = lambda: swa.prefill(q, k, v, c["W"], mode=c["mode"], scale=1.0 / math.sqrt(c["d"]),  # noqa: E731
+                                 out=out)
+        flops = 4 * c["d"] * band_pairs(c["T"], c["W"], c["mode"], 1) * c["Hq"] * c["B"]
+        bytes_ = 4 * c["T"] * c["d"] * c["B"] * (2 * c["Hq"] + 2 * c["Hkv"])
+        fp32_row(c["name"] + " in fp32", "prefill_f32", flops, bytes_, fn)
+        del q, k, v, out
+    c = si.WORKLOADS[6]
+    tensors = si.chunk_inputs(6, dtype="f32")
+    q, k, v, kr, vr = (si.to_torch(t, dev) for t in tensors[:5])
+    pos = torch.from_numpy(tensors[5]).to(dev)
+    out = torch.empty_like(q)
+    fn = lambda: swa.prefill_chunk(q, k, v, kr, vr, pos, scale=1.0 / math.sqrt(c["d"]), out=out)  # noqa: E731
+    flops, bytes_ = chunk_work(c, tensors[5])
+    fp32_row(c["name"] + " in fp32", "prefill_chunk_f32", flops, 2 * bytes_, fn)
     return 0
 
 
