@@ -104,8 +104,9 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
 // dil * d), four waves of 32 rows; 64-key K/V tiles visited only where they
 // meet the block's windows, double-buffered in LDS and filled by direct
 // buffer-to-LDS loads; S^T = K Q^T with one query row per lane.  Products on
-// v_mfma_f32_32x32x2_f32, softmax exact and online per tile (running maximum
-// and sum in fp32, probabilities exp2(s * c - m) with c = scale * log2(e)),
+// v_mfma_f32_32x32x2_f32, softmax exact and online per 32-key block (running
+// reference maximum, raised lazily, and sum in fp32, probabilities
+// exp2(s * c - m) with c = scale * log2(e)),
 // O^T += V^T P^T with the fp32 probabilities as they are.  The chunk mode
 // (MODE 2) is the causal kernel in key coordinates relative to the chunk's
 // first token at position p, as in the bf16 kernel: key r < 0 is position
@@ -131,6 +132,9 @@ constexpr int kBN = tm::kBN;   // keys per tile
 constexpr int kBM = tm::kBM;   // query rows per workgroup
 constexpr int kThreads = 256;  // four waves
 constexpr int kBufferFlags = 0x00020000;  // raw 32-bit buffer access
+
+// log2 headroom of a row's probabilities over its reference maximum
+constexpr float kGrow = 64.0f;
 
 template <int D>
 struct Geo {
@@ -355,16 +359,25 @@ void prefill_f32_mfma_kernel(const float* __restrict__ q, const float* __restric
       mx = fmaxf(mx, t);
     }
     mx = max_lane_pair(mx);  // lanes l and l^32 hold the same row
-    const float m_new = fmaxf(m, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // a row without keys so far
-    const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-    m = m_new;
-    l *= alpha;
+    // The reference maximum m is raised only when the block's maximum exceeds
+    // it by more than kGrow (or on the row's first keys), so that the
+    // accumulators are rescaled rarely: probabilities up to 2^kGrow cost no
+    // precision (fp32 is a relative-precision format) and the sums stay far
+    // from overflow; the row's largest probability is at least 1, so nothing
+    // that underflows against m would count next to it.
+    const bool grow = mx > m + kGrow;  // m = -inf: any key of the row
+    if (__ballot(grow)) {
+      const float m_new = grow ? mx : m;
+      const float alpha = __builtin_amdgcn_exp2f(m - (m_new == -INFINITY ? 0.f : m_new));
+      m = m_new;
+      l *= alpha;
 #pragma unroll
-    for (int md = 0; md < MD; ++md) {
+      for (int md = 0; md < MD; ++md) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[md][r] *= alpha;
+        for (int r = 0; r < 16; ++r) o[md][r] *= alpha;
+      }
     }
+    const float m_use = m == -INFINITY ? 0.f : m;  // a row without keys so far
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       sb[r] = __builtin_amdgcn_exp2f(sb[r] - m_use);
