@@ -6,18 +6,11 @@
 // la finestra con la profondita"): each query row takes the softmax of its
 // in-window logits only.
 //
-// Plain and dilated windows and the chunk continuing a ring cache run on the
-// matrix cores (prefill_f32_mfma_kernel below: v_mfma_f32_32x32x2_f32, the
-// tiled bf16 kernel's decomposition).  The global-token modes keep a
-// vector-ALU kernel in which 16 lanes share one query row, each holding d/16
-// dims, and a row walks exactly the keys of its own window, one key at a
-// time, with a running maximum and sum:
-//
-// Global tokens (MODES 5 causal, 6 symmetric; aivaro section 4.3): the row
-// takes its window (dilated when dil > 1: every dil-th key, j = i - m * dil
-// for m in the plain window's offsets; aivaro section 4.2), then each global
-// key outside the window (not after the row when causal).  The global rows
-// themselves are written afterwards by the split-K pass of swa_ring.hip.
+// One kernel on the matrix cores (prefill_f32_mfma_kernel below:
+// v_mfma_f32_32x32x2_f32, the tiled bf16 kernel's decomposition) takes every
+// mode: plain and dilated windows, the chunk continuing a ring cache, and the
+// window plus global tokens (whose global rows the split-K pass of
+// swa_ring.hip writes afterwards).
 
 #include "swa_device.h"
 #include "swa_launch.h"
@@ -26,79 +19,10 @@
 namespace swa {
 namespace {
 
-constexpr int kRowsPerBlock = 16;
-constexpr int kLanesPerRow = 16;
-
-// MODE: 5 causal and 6 symmetric window plus the ngl global keys at gpos.
-// dil: key stride of the (dilated) window.
-template <int D, int MODE>
-__global__ __launch_bounds__(256) void prefill_f32_kernel(
-    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    float* __restrict__ out, int T, int W, int Hq, int Hkv, float scale, int n_rowblocks,
-    int dil, const int32_t* __restrict__ gpos, int ngl) {
-  static_assert(MODE == 5 || MODE == 6, "the window plus global tokens");
-  constexpr int DPL = D / kLanesPerRow;
-  constexpr bool kCausal = MODE == 5;
-  const int h = blockIdx.x / n_rowblocks;
-  const int i = (blockIdx.x % n_rowblocks) * kRowsPerBlock + threadIdx.x / kLanesPerRow;
-  const int c = threadIdx.x % kLanesPerRow;
-  if (i >= T) return;  // whole 16-lane groups leave together
-  const int kvh = h / (Hq / Hkv);
-  const float* qrow = q + ((size_t)h * T + i) * D + c * DPL;
-  const float* kh = k + (size_t)kvh * T * D + c * DPL;
-  const float* vh = v + (size_t)kvh * T * D + c * DPL;
-  float* orow = out + ((size_t)h * T + i) * D + c * DPL;
-
-  float qv[DPL], acc[DPL];
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) {
-    qv[e] = qrow[e];
-    acc[e] = 0.f;
-  }
-  int lo, hi;
-  if (kCausal) {
-    lo = i - dil * min(W - 1, i / dil);
-    hi = i;
-  } else {
-    lo = i - dil * min(W / 2, i / dil);
-    hi = i + dil * min(W / 2, (T - 1 - i) / dil);
-  }
-  float m = -INFINITY, l = 0.f;
-  // one key: score, running maximum and sum, accumulate its value row
-  auto visit = [&](const float* kr, const float* vr) {
-    float s = 0.f;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) s = fmaf(qv[e], kr[e], s);
-#pragma unroll
-    for (int off = kLanesPerRow / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, kLanesPerRow);
-    s *= scale;
-    const float m_new = fmaxf(m, s);
-    const float alpha = expf(m - m_new);  // m = -inf on the first key: 0
-    const float p = expf(s - m_new);
-    l = l * alpha + p;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[e] = fmaf(p, vr[e], acc[e] * alpha);
-    m = m_new;
-  };
-  for (int j = lo; j <= hi; j += dil) visit(kh + (size_t)j * D, vh + (size_t)j * D);
-  for (int t = 0; t < ngl; ++t) {
-    const int gp = gpos[t];
-    const int diff = i - gp;
-    // in the (dilated) window: on the row's grid, within the window's offsets
-    const int m = diff / dil;
-    const bool in_window = diff == m * dil &&
-                           (kCausal ? (m >= 0 && m < W) : (m >= -(W / 2) && m <= W / 2));
-    if (gp < 0 || gp >= T || in_window || (kCausal && diff < 0)) continue;
-    visit(kh + (size_t)gp * D, vh + (size_t)gp * D);
-  }
-  const float inv = 1.0f / l;
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) orow[e] = acc[e] * inv;
-}
-
 // ---------------------------------------------------------------------------
-// Plain and dilated windows, and the chunk continuing a ring cache (Ultralytics
-// ring-buffer paragraph), on the matrix cores.  The tiled bf16 kernel's
+// Plain and dilated windows, the chunk continuing a ring cache (Ultralytics
+// ring-buffer paragraph) and the window plus global tokens (aivaro answer 629,
+// sections 4.2 and 4.3), on the matrix cores.  The tiled bf16 kernel's
 // decomposition: one workgroup = 128 query rows of one query head (of one
 // residue class mod the dilation, a sequence of its own with row stride
 // dil * d), four waves of 32 rows; 64-key K/V tiles visited only where they
@@ -111,7 +35,11 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
 // (MODE 2) is the causal kernel in key coordinates relative to the chunk's
 // first token at position p, as in the bf16 kernel: key r < 0 is position
 // p + r, read from ring slot (p + r) mod W; tiles are aligned to the chunk
-// start, so a tile is wholly ring or wholly chunk.
+// start, so a tile is wholly ring or wholly chunk.  The global-token modes
+// (MODES 5 causal, 6 symmetric, any dilation) visit the global keys after the
+// window's tiles, as extra tiles whose rows are gathered from the global
+// positions; a global key already inside a row's window, or after the row
+// when causal, is masked there.
 //
 // The tile's two 32-key blocks are taken one after the other, each with its
 // own online-softmax update.
@@ -157,16 +85,17 @@ __device__ __forceinline__ int swz(int row) {
 
 // Occupancy (waves per SIMD) that the LDS of double-buffered fp32 tiles
 // allows: 128 KB per workgroup at d = 128, 64 KB at d = 64, 32 KB at d = 32
-// (the chunk mode at d = 32 takes three, whose registers hold its ring
-// addressing without spills).
+// (the chunk and global-token modes at d = 32 take three, whose registers
+// hold their ring or global-key addressing without spills).
 template <int D, int MODE>
-constexpr int kWaves = D == 128 ? 1 : (D == 64 ? 2 : (MODE == 2 ? 3 : 4));
+constexpr int kWaves = D == 128 ? 1 : (D == 64 ? 2 : (MODE == 2 || MODE >= 5 ? 3 : 4));
 
 }  // namespace f32m
 
 // MODE: 0 causal, 1 symmetric (dil: key stride of a dilated window), 2 causal
 // chunk continuing a ring cache (Tseq is then the chunk length; kring, vring,
-// pos and hkv_seq are used by MODE 2 only).
+// pos and hkv_seq are used by MODE 2 only), 5 causal and 6 symmetric window
+// (dilated when dil > 1) plus the ngl global keys at gpos.
 template <int D, int MODE>
 __global__ __launch_bounds__(f32m::kThreads)
 __attribute__((amdgpu_waves_per_eu(f32m::kWaves<D, MODE>, f32m::kWaves<D, MODE>)))
@@ -174,10 +103,12 @@ void prefill_f32_mfma_kernel(const float* __restrict__ q, const float* __restric
                              const float* __restrict__ v, float* __restrict__ out, int Tseq,
                              int W, int Hq, int Hkv, float c, int n_qtiles, int dil,
                              const float* __restrict__ kring, const float* __restrict__ vring,
-                             const int32_t* __restrict__ pos, int hkv_seq) {
+                             const int32_t* __restrict__ pos, int hkv_seq,
+                             const int32_t* __restrict__ gpos, int ngl) {
   using namespace f32m;
-  constexpr bool kCausal = MODE != 1;
+  constexpr bool kCausal = MODE != 1 && MODE != 6;
   constexpr bool kChunk = MODE == 2;
+  constexpr bool kGlobal = MODE >= 5;
   using Gm = Geo<D>;
   constexpr int ROWB = Gm::ROWB, TILEB = Gm::TILEB, NLD = Gm::NLD, KQ = Gm::KQ, MD = Gm::MD;
   typedef __attribute__((address_space(3))) void lds_void;
@@ -185,6 +116,8 @@ void prefill_f32_mfma_kernel(const float* __restrict__ q, const float* __restric
   __shared__ __attribute__((aligned(1024))) char lds_v0[TILEB];
   __shared__ __attribute__((aligned(1024))) char lds_k1[TILEB];
   __shared__ __attribute__((aligned(1024))) char lds_v1[TILEB];
+  // global modes: the positions of the global key tile held in each stage
+  __shared__ __attribute__((aligned(16))) int lds_gp[2][kGlobal ? kBN : 1];
 
   // ---- which (query head, residue class, query block) this workgroup owns;
   // consecutive ids go round-robin to the 8 XCDs: each gets a contiguous range
@@ -214,6 +147,9 @@ void prefill_f32_mfma_kernel(const float* __restrict__ q, const float* __restric
   const float* qh = q + (size_t)h * Tseq * D + (size_t)cls * D;
   const float* kh = k + (size_t)kvh * Tseq * D + (size_t)cls * D;
   const float* vh = v + (size_t)kvh * Tseq * D + (size_t)cls * D;
+  // global keys sit at sequence positions (outside any residue class)
+  const float* kg = k + (size_t)kvh * Tseq * D;
+  const float* vg = v + (size_t)kvh * Tseq * D;
 
   // chunk mode: position of the chunk's first token; the lowest key is -pstart
   int pstart = 0;
@@ -237,6 +173,8 @@ void prefill_f32_mfma_kernel(const float* __restrict__ q, const float* __restric
   const int hi = kCausal ? SWA_TM_CAUSAL_BLOCK_HI(q0, T) : SWA_TM_SYM_BLOCK_HI(q0, T, hw);
   const int kt0 = kChunk ? tm::floor_tile(lo) : lo / kBN;
   const int kt1 = hi / kBN;
+  // global modes: the global key tiles follow the window's, as kt1+1 .. kt_end
+  const int kt_end = kGlobal ? tm::global_tiles_end(kt1, ngl) : kt1;
   const bool wave_active = qw0 < T;
   const int qlast = SWA_TM_WAVE_LAST(qw0, T);
   const int wlo = SWA_TM_WAVE_LO(kCausal, qw0, W, hw, pstart);
@@ -263,6 +201,34 @@ void prefill_f32_mfma_kernel(const float* __restrict__ q, const float* __restric
     src_koff[j] = (tm::load_chunk(o, ROWB) ^ swz<D>(row)) * 16;
   }
   auto load_tile = [&](char* Kdst, char* Vdst, int kt) __attribute__((always_inline)) {
+    if constexpr (kGlobal) {
+      if (kt > kt1) {
+        // a global key tile: row j holds the key at gpos[t0 + j]; rows past
+        // the last global key, and positions outside [0, Tseq), re-read a
+        // valid row (masked); the tile's positions go to LDS for the mask
+        // (written after the barrier that frees the stage)
+        const int t0 = (kt - kt1 - 1) * kBN;
+        if (tid < kBN) lds_gp[(kt - kt0) & 1][tid] = gpos[tm::global_index(t0, tid, ngl)];
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc((void*)kg, 0, Tseq * ROWB, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc((void*)vg, 0, Tseq * ROWB, kBufferFlags);
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) {
+          const int wbase = (j * kThreads + wave * 64) * 16;
+          const int roff = tm::global_src_row(gpos[tm::global_index(t0, src_row[j], ngl)], Tseq) * ROWB;
+          const int koff = roff + src_koff[j];
+          const int voff = roff + tm::load_chunk(tm::load_lds_offset(j, tid, kThreads), ROWB) * 16;
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass mishandles this builtin
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(Kdst + wbase), 16, koff, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(Vdst + wbase), 16, voff, 0, 0, 0);
+#else
+          (void)rk, (void)rv, (void)wbase, (void)koff, (void)voff;
+#endif
+        }
+        return;
+      }
+    }
     if constexpr (kChunk) {
       if (kt < 0) {
         // a ring tile: key r = kt * kBN + row is position pstart + r, in slot
@@ -325,11 +291,14 @@ void prefill_f32_mfma_kernel(const float* __restrict__ q, const float* __restric
   float l = 0.f;        // this lane's share of the row sum
 
   // One 32-key block (keys k0 .. k0 + 31, LDS rows kb .. kb + 31 of the
-  // tile): S^T, mask (blocks crossing a window edge or the sequence end),
-  // online softmax, O^T += V^T P^T.  The group barriers interleave each LDS
+  // tile): S^T, mask (blocks crossing a window edge or the sequence end; in a
+  // global tile, gp holding the block's global positions and k0 the global
+  // index of its first key: the keys that count for the row), online softmax,
+  // O^T += V^T P^T.  The group barriers interleave each LDS
   // read with the products it feeds, one group ahead, so that the compiler
   // does not hoist every read of the block (and spill their registers).
-  auto block = [&](const char* Ks, const char* Vs, int kb, int k0, bool full) __attribute__((always_inline)) {
+  const int rpos = cls + dil * qi;  // this lane's row as a sequence position
+  auto block = [&](const char* Ks, const char* Vs, int kb, int k0, bool full, const int* gp) __attribute__((always_inline)) {
     f32x16 sb = f32x16{};
 #pragma unroll
     for (int j = 0; j < KQ; ++j) {
@@ -347,12 +316,22 @@ void prefill_f32_mfma_kernel(const float* __restrict__ q, const float* __restric
     }
     __builtin_amdgcn_sched_barrier(0);
 
+    int gpv[16];
+    if (kGlobal && gp) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int4 x = *reinterpret_cast<const int4*>(gp + 8 * g + 4 * half);
+        gpv[4 * g] = x.x, gpv[4 * g + 1] = x.y, gpv[4 * g + 2] = x.z, gpv[4 * g + 3] = x.w;
+      }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float t = sb[r] * c;
-      if (!full) {
-        const int key = k0 + 8 * (r >> 2) + 4 * half + (r & 3);
+      const int key = k0 + 8 * (r >> 2) + 4 * half + (r & 3);
+      if (kGlobal && gp) {
+        if (!tm::global_counts(kCausal, dil > 1, rpos, gpv[r], key, ngl, Tseq, W, dil)) t = -INFINITY;
+      } else if (!full) {
         if (!tm::edge_visible(kCausal, qi, key, T, W, pstart)) t = -INFINITY;
       }
       sb[r] = t;
@@ -408,18 +387,33 @@ void prefill_f32_mfma_kernel(const float* __restrict__ q, const float* __restric
   auto step = [&](const char* Ks, const char* Vs, char* Kn, char* Vn, int kt) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    if (kt < kt1) load_tile(Kn, Vn, kt + 1);
+    if (kt < kt_end) load_tile(Kn, Vn, kt + 1);
     const int k0 = kt * kBN;
     if (!tm::tile_visited(wave_active, wlo, whi, k0)) return;
     const bool full = tm::tile_full(kCausal, kChunk, k0, qw0, qlast, T, W, pstart);
-    block(Ks, Vs, 0, k0, full);
-    block(Ks, Vs, 32, k0 + 32, full);
+    block(Ks, Vs, 0, k0, full, nullptr);
+    block(Ks, Vs, 32, k0 + 32, full, nullptr);
   };
   load_tile(lds_k0, lds_v0, kt0);
   for (int kt = kt0; kt <= kt1; kt += 2) {
     step(lds_k0, lds_v0, lds_k1, lds_v1, kt);
     if (kt + 1 > kt1) break;
     step(lds_k1, lds_v1, lds_k0, lds_v0, kt + 1);
+  }
+  // global modes: the global key tiles (tile kt sits in stage (kt - kt0) & 1;
+  // the last window step already requested the first of them); a 32-key
+  // block without global keys is skipped
+  if constexpr (kGlobal) {
+    for (int kt = kt1 + 1; kt <= kt_end; ++kt) {
+      const int st = (kt - kt0) & 1;
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __syncthreads();
+      if (kt < kt_end) load_tile(st ? lds_k0 : lds_k1, st ? lds_v0 : lds_v1, kt + 1);
+      if (!wave_active) continue;
+      const int t0 = (kt - kt1 - 1) * kBN;
+      block(st ? lds_k1 : lds_k0, st ? lds_v1 : lds_v0, 0, t0, false, lds_gp[st]);
+      if (ngl - t0 > 32) block(st ? lds_k1 : lds_k0, st ? lds_v1 : lds_v0, 32, t0 + 32, false, lds_gp[st] + 32);
+    }
   }
 
   // ---- epilogue: divide by the row sum and store (the exchange involves
@@ -442,7 +436,8 @@ void prefill_f32_mfma_kernel(const float* __restrict__ q, const float* __restric
 
 template <int D, int MODE>
 hipError_t launch(const void* q, const void* k, const void* v, void* out, int T, int W, int Hq,
-                  int Hkv, float scale, int dil, hipStream_t stream) {
+                  int Hkv, float scale, int dil, hipStream_t stream,
+                  const int32_t* gpos = nullptr, int ngl = 0) {
   // residue classes: the longest has ceil(T / dil) rows
   const int n_qtiles = ((T + dil - 1) / dil + f32m::kBM - 1) / f32m::kBM;
   const long long nwg = (long long)n_qtiles * Hq * dil;
@@ -451,7 +446,7 @@ hipError_t launch(const void* q, const void* k, const void* v, void* out, int T,
                      static_cast<const float*>(k), static_cast<const float*>(v),
                      static_cast<float*>(out), T, W, Hq, Hkv, scale * kLog2e, n_qtiles, dil,
                      static_cast<const float*>(nullptr), static_cast<const float*>(nullptr),
-                     static_cast<const int32_t*>(nullptr), 1);
+                     static_cast<const int32_t*>(nullptr), 1, gpos, ngl);
   return hipGetLastError();
 }
 
@@ -465,20 +460,7 @@ hipError_t launch_chunk(const void* q, const void* k, const void* v, const void*
                      stream, static_cast<const float*>(q), static_cast<const float*>(k),
                      static_cast<const float*>(v), static_cast<float*>(out), n, W, Hq * B, Hkv * B,
                      scale * kLog2e, n_qtiles, 1, static_cast<const float*>(k_ring),
-                     static_cast<const float*>(v_ring), pos, Hkv);
-  return hipGetLastError();
-}
-
-template <int D, int MODE>
-hipError_t launch_global(const void* q, const void* k, const void* v, void* out, int T, int W,
-                         int Hq, int Hkv, float scale, const int32_t* gpos, int ngl, int dil,
-                         hipStream_t stream) {
-  const int n_rowblocks = (T + kRowsPerBlock - 1) / kRowsPerBlock;
-  const long long nwg = (long long)n_rowblocks * Hq;
-  hipLaunchKernelGGL((prefill_f32_kernel<D, MODE>), dim3((unsigned)nwg),
-                     dim3(kRowsPerBlock * kLanesPerRow), 0, stream, static_cast<const float*>(q),
-                     static_cast<const float*>(k), static_cast<const float*>(v),
-                     static_cast<float*>(out), T, W, Hq, Hkv, scale, n_rowblocks, dil, gpos, ngl);
+                     static_cast<const float*>(v_ring), pos, Hkv, static_cast<const int32_t*>(nullptr), 0);
   return hipGetLastError();
 }
 
@@ -489,13 +471,13 @@ hipError_t launch_prefill_global_window_f32(const void* q, const void* k, const 
                                             int mode, float scale, const int32_t* gpos, int ngl,
                                             int dil, hipStream_t stream) {
   if (mode == 0) {
-    if (d == 32) return launch_global<32, 5>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, dil, stream);
-    if (d == 64) return launch_global<64, 5>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, dil, stream);
-    return launch_global<128, 5>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, dil, stream);
+    if (d == 32) return launch<32, 5>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream, gpos, ngl);
+    if (d == 64) return launch<64, 5>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream, gpos, ngl);
+    return launch<128, 5>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream, gpos, ngl);
   }
-  if (d == 32) return launch_global<32, 6>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, dil, stream);
-  if (d == 64) return launch_global<64, 6>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, dil, stream);
-  return launch_global<128, 6>(q, k, v, out, T, W, Hq, Hkv, scale, gpos, ngl, dil, stream);
+  if (d == 32) return launch<32, 6>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream, gpos, ngl);
+  if (d == 64) return launch<64, 6>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream, gpos, ngl);
+  return launch<128, 6>(q, k, v, out, T, W, Hq, Hkv, scale, dil, stream, gpos, ngl);
 }
 
 hipError_t launch_prefill_chunk_f32(const void* q, const void* k, const void* v,

@@ -110,19 +110,23 @@ def test_every_token_global_is_full_attention(swa, dtype, mode):
     assert_parity(to_f64(out), ref, dtype, "every token global")
 
 
-def test_no_global_is_prefill_bit_for_bit(swa):
-    q, k, v = (to_device(t) for t in si.prefill_inputs(8, B=1, Hq=4, Hkv=2, T=333, d=64))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_no_global_is_prefill_bit_for_bit(swa, dtype):
+    q, k, v = (to_device(t) for t in si.prefill_inputs(8, B=1, Hq=4, Hkv=2, T=333, d=64, dtype=dtype))
     a = swa.prefill(q, k, v, 40, mode=1)
     b = swa.prefill_global(q, k, v, 40, torch.zeros(0, dtype=torch.int32, device="cuda"), mode=1)
     torch.cuda.synchronize()
-    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    bits = torch.int16 if dtype == "bf16" else torch.int32
+    assert torch.equal(a.view(bits), b.view(bits))
 
 
-def test_longformer_global_sampled(swa):
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_longformer_global_sampled(swa, dtype):
     """B=4, T=4096, symmetric W=512, 12 heads, d=64, global tokens 0..7:
-    the global rows and sampled other rows of every sequence vs the oracle."""
+    the global rows and sampled other rows of every sequence vs the oracle
+    (bf16, the workload's type; and the same shapes in fp32)."""
     cfg = si.WORKLOADS[8]
-    q, k, v = si.prefill_inputs(8)
+    q, k, v = si.prefill_inputs(8, dtype=dtype)
     gpos = np.array(cfg["global_pos"], dtype=np.int32)
     out = swa.prefill_global(to_device(q), to_device(k), to_device(v), cfg["W"],
                              torch.from_numpy(gpos).cuda(), mode=cfg["mode"])
@@ -135,4 +139,4 @@ def test_longformer_global_sampled(swa):
         for h in (0, 11):
             ref = oracle.attention_global_rows(q.values, k.values, v.values, cfg["W"], cfg["mode"],
                                                scale, gpos, b, h, rows)
-            assert_parity(got[b, h, rows], ref, "bf16", "longformer global b=%d h=%d" % (b, h))
+            assert_parity(got[b, h, rows], ref, dtype, "longformer global b=%d h=%d" % (b, h))

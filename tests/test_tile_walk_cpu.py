@@ -147,7 +147,7 @@ def test_fp32_matrix_core_kernel(walker, mode):
         for W in (1, 33, 65, 300):
             for dil in (2, 5, T + 3):
                 shapes.append((T, W, dil, 32 if (T + W) % 3 == 0 else (64 if (T + W) % 3 == 1 else 128)))
-    res = run(walker, ["tiledf32 %d %d %d %d 0 %d" % (mode, T, W, dil, D) for T, W, dil, D in shapes])
+    res = run(walker, ["tiledf32 %d %d %d %d 0 %d 0" % (mode, T, W, dil, D) for T, W, dil, D in shapes])
     for (T, W, dil, D), r in zip(shapes, res):
         want = oracle.window_mask(T, W, mode) if dil == 1 else oracle.dilated_mask(T, W, mode, dil)
         check(r, expect_rows(want), ("fp32", mode, T, W, dil, D))
@@ -176,7 +176,7 @@ def test_chunk_continuing_a_ring(walker):
     for (n, W, p, D), r in zip(shapes, res):
         check(r, chunk_window(n, W, p), ("chunk", n, W, p))
     # the fp32 matrix-core kernel's chunk mode (4-byte rows, direct masks)
-    res = run(walker, ["tiledf32 2 %d %d 1 %d %d" % (n, W, p, D) for n, W, p, D in shapes])
+    res = run(walker, ["tiledf32 2 %d %d 1 %d %d 0" % (n, W, p, D) for n, W, p, D in shapes])
     for (n, W, p, D), r in zip(shapes, res):
         check(r, chunk_window(n, W, p), ("chunk fp32", n, W, p))
 
@@ -200,8 +200,12 @@ def test_window_plus_global_tokens(walker, mode, dil):
     kmode = (5 if mode == CAUSAL else 6) if dil == 1 else (7 if mode == CAUSAL else 8)
     lines = ["tiled %d %d %d %d 0 64 %d %s" % (kmode, T, W, dil, len(g), " ".join(map(str, g)))
              for T, W, g in shapes]
+    # the bf16 kernel (d = 64), then the fp32 matrix-core kernel (4-byte rows)
+    fmode = 5 if mode == CAUSAL else 6
+    lines += ["tiledf32 %d %d %d %d 0 %d %d %s" % (fmode, T, W, dil, 32 if T % 2 else 128, len(g),
+                                                  " ".join(map(str, g))) for T, W, g in shapes]
     res = run(walker, lines)
-    for (T, W, g), r in zip(shapes, res):
+    for (T, W, g), r in zip(shapes + shapes, res):
         valid = sorted(p for p in g if 0 <= p < T)
         mask = oracle.global_mask(T, W, mode, valid, dil)
         rows = [i for i in range(T) if i not in set(valid)]

@@ -13,7 +13,8 @@
 //
 // Input lines (one shape each):
 //   tiled MODE Tseq W dil pstart D G g_1 .. g_G
-//   tiledf32 MODE Tseq W dil pstart D   (the fp32 matrix-core kernel, MODE 0/1/2)
+//   tiledf32 MODE Tseq W dil pstart D G g_1 .. g_G   (the fp32 matrix-core
+//                              kernel: MODE 0/1/2/5/6, any dilation)
 //   short MODE T W D
 //   grows MODE T D G g_1 .. g_G
 // MODE of "tiled" is the tiled kernel's: 0 causal, 1 symmetric, 2 causal
@@ -58,9 +59,9 @@ void count(Keys& keys, long long row, long long key) {
 }
 
 // The tiled kernel (prefill_bf16_kernel) for one query head; with f32, the
-// fp32 matrix-core kernel (prefill_f32_mfma_kernel): 4-byte elements, plain
-// and dilated windows and the chunk mode, every tile crossing an edge masked
-// by the direct test.
+// fp32 matrix-core kernel (prefill_f32_mfma_kernel): 4-byte elements, every
+// window tile crossing an edge masked by the direct test (its global tiles
+// count the keys global_counts admits, as the class test of the bf16 kernel).
 void walk_tiled(int MODE, int Tseq, int W, int dil, int pstart, int D, const std::vector<int>& gpos,
                 bool f32 = false) {
   const bool kCausal = MODE != 1 && MODE != 4 && MODE != 6 && MODE != 8;
@@ -354,12 +355,19 @@ int main() {
       swz_check(D);
       walk_tiled(mode, Tseq, W, dil, pstart, D, g);
     } else if (k == "tiledf32") {
-      int mode, Tseq, W, dil, pstart, D;
-      if (std::scanf("%d %d %d %d %d %d", &mode, &Tseq, &W, &dil, &pstart, &D) != 6) return 2;
-      if (mode < 0 || mode > 2) return 2;
+      int mode, Tseq, W, dil, pstart, D, G;
+      if (std::scanf("%d %d %d %d %d %d %d", &mode, &Tseq, &W, &dil, &pstart, &D, &G) != 7) return 2;
+      if (mode != 0 && mode != 1 && mode != 2 && mode != 5 && mode != 6) return 2;
+      std::vector<int> g(G);
+      for (int i = 0; i < G; ++i)
+        if (std::scanf("%d", &g[i]) != 1) return 2;
       swz_check(D);
-      // the kernel runs dilations > 1 as the residue-class walk of modes 3/4
-      walk_tiled(mode < 2 && dil > 1 ? mode + 3 : mode, Tseq, W, dil, pstart, D, {}, true);
+      // the kernel runs dilations > 1 as the residue-class walks of the bf16
+      // kernel's dilated modes (3/4, and 7/8 with global keys)
+      int wmode = mode;
+      if (dil > 1 && mode < 2) wmode = mode + 3;
+      if (dil > 1 && mode >= 5) wmode = mode + 2;
+      walk_tiled(wmode, Tseq, W, dil, pstart, D, g, true);
     } else if (k == "short") {
       int mode, T, W, D;
       if (std::scanf("%d %d %d %d", &mode, &T, &W, &D) != 4) return 2;
