@@ -28,10 +28,10 @@ namespace {
 // dil * d), four waves of 32 rows; 64-key K/V tiles visited only where they
 // meet the block's windows, double-buffered in LDS and filled by direct
 // buffer-to-LDS loads; S^T = K Q^T with one query row per lane.  Products on
-// v_mfma_f32_32x32x2_f32, softmax exact and online per 32-key block (running
-// reference maximum, raised lazily, and sum in fp32, probabilities
-// exp2(s * c - m) with c = scale * log2(e)),
-// O^T += V^T P^T with the fp32 probabilities as they are.  The chunk mode
+// v_mfma_f32_32x32x2_f32; softmax exact and online per 32-key block (a
+// reference maximum raised lazily, sums in fp32, probabilities
+// exp2(s * c - m) with c = scale * log2(e)); O^T += V^T P^T with the fp32
+// probabilities as they are.  The chunk mode
 // (MODE 2) is the causal kernel in key coordinates relative to the chunk's
 // first token at position p, as in the bf16 kernel: key r < 0 is position
 // p + r, read from ring slot (p + r) mod W; tiles are aligned to the chunk
