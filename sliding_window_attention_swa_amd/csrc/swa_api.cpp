@@ -58,7 +58,8 @@ int swa_prefill(const void* q, const void* k, const void* v, void* out, int T, i
   if (!supported_d(d) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
   if (mode != SWA_CAUSAL && mode != SWA_SYMMETRIC) return SWA_ERR_UNSUPPORTED;
   if (T > kMaxSeq) return SWA_ERR_UNSUPPORTED;
-  // workgroup count (16-row blocks for fp32 is the larger) must fit the grid
+  // workgroup count must fit the grid (bounded with 16 rows per workgroup:
+  // every kernel takes at least 32)
   if ((long long)((T + 15) / 16) * Hq > kMaxGrid) return SWA_ERR_UNSUPPORTED;
   W = clamp_window(W, T);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -81,7 +82,8 @@ int swa_prefill_dilated(const void* q, const void* k, const void* v, void* out, 
   if (T > kMaxSeq) return SWA_ERR_UNSUPPORTED;
   // a tile's 64 rows, dilation rows apart, are addressed with 32-bit byte offsets
   if ((long long)dilation * d * elem_bytes(dtype) * 64 > 2147483647LL) return SWA_ERR_UNSUPPORTED;
-  // workgroup counts: 16-row blocks (fp32); 128-row blocks of each residue class (bf16)
+  // workgroup counts: at least 32 rows per workgroup (bounded with 16); 128-row
+  // blocks of each residue class
   if ((long long)((T + 15) / 16) * Hq > kMaxGrid) return SWA_ERR_UNSUPPORTED;
   const long long class_rows = (T + (long long)dilation - 1) / dilation;
   if ((class_rows + 127) / 128 * Hq * (long long)dilation > kMaxGrid) return SWA_ERR_UNSUPPORTED;
@@ -215,7 +217,8 @@ int swa_prefill_chunk(const void* q, const void* k, const void* v, const void* k
   if (n > kMaxSeq) return SWA_ERR_UNSUPPORTED;
   // ring rows are addressed with 32-bit byte offsets
   if ((long long)W * d * elem_bytes(dtype) > 2147483647LL) return SWA_ERR_UNSUPPORTED;
-  // folded head counts and the workgroup count (16-row blocks for fp32) fit int32
+  // folded head counts and the workgroup count (bounded with 16 rows per
+  // workgroup) fit int32
   if ((long long)B * Hq > kMaxGrid) return SWA_ERR_UNSUPPORTED;
   if ((long long)((n + 15) / 16) * Hq * B > kMaxGrid) return SWA_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
