@@ -267,24 +267,29 @@ def test_prefill_f32_mistral_shape_sampled(swa):
 
 # ------------------------------------------------------------ full sizes
 
-def test_tinymistral_full(swa):
-    """B=8, T=2048, W=32, 32/8 heads, d=32, bf16: every row of every head."""
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_tinymistral_full(swa, dtype):
+    """B=8, T=2048, W=32, 32/8 heads, d=32: every row of every head (bf16, the
+    workload's type, on the short-window kernel; the same shapes in fp32 on
+    the fp32 matrix-core kernel)."""
     cfg = si.WORKLOADS[2]
-    q, k, v = si.prefill_inputs(2)
+    q, k, v = si.prefill_inputs(2, dtype=dtype)
     got = to_f64(run(swa, q, k, v, cfg["W"], cfg["mode"]))
     ref = oracle.attention_banded(q.values, k.values, v.values, cfg["W"], cfg["mode"],
                                   1 / math.sqrt(cfg["d"]))
-    assert_parity(got, ref, "bf16", "TinyMistral")
+    assert_parity(got, ref, dtype, "TinyMistral")
 
 
-def test_longformer_full(swa):
-    """B=4, T=4096, W=512 symmetric, 12 heads, d=64, bf16: every row."""
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_longformer_full(swa, dtype):
+    """B=4, T=4096, W=512 symmetric, 12 heads, d=64: every row (bf16, the
+    workload's type; and the same shapes in fp32)."""
     cfg = si.WORKLOADS[5]
-    q, k, v = si.prefill_inputs(5)
+    q, k, v = si.prefill_inputs(5, dtype=dtype)
     got = to_f64(run(swa, q, k, v, cfg["W"], cfg["mode"]))
     ref = oracle.attention_banded(q.values, k.values, v.values, cfg["W"], cfg["mode"],
                                   1 / math.sqrt(cfg["d"]))
-    assert_parity(got, ref, "bf16", "Longformer")
+    assert_parity(got, ref, dtype, "Longformer")
 
 
 def test_mistral_full_sampled(swa):
