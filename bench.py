@@ -107,6 +107,7 @@ def source_hash(names):
 
 
 PREFILL_SOURCE = ("swa_prefill_bf16.hip", "swa_tile_math.h")
+PREFILL_F32_SOURCE = ("swa_prefill_f32.hip", "swa_tile_math.h")
 DECODE_SOURCE = ("swa_ring.hip",)
 
 
@@ -218,15 +219,16 @@ def summarize_pmc_small(paths):
     return 0
 
 
-def pmc_config(wl):
-    """Counter workload of one prefill configuration: its kernel once after a
-    1 GiB read that evicts the L2s and the Infinity Cache, then once warm."""
+def pmc_config(wl, dtype="bf16"):
+    """Counter workload of one prefill configuration (its inputs in `dtype`):
+    its kernel once after a 1 GiB read that evicts the L2s and the Infinity
+    Cache, then once warm."""
     import torch
     import sliding_window_attention_swa_amd as swa
     dev = torch.device("cuda:0")
     swa.load()
     c = si.WORKLOADS[wl]
-    q, k, v = (si.to_torch(t, dev) for t in si.prefill_inputs(wl))
+    q, k, v = (si.to_torch(t, dev) for t in si.prefill_inputs(wl, dtype=dtype))
     out = torch.empty_like(q)
     flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
     flush_max = torch.empty((), dtype=torch.int32, device=dev)
@@ -235,7 +237,7 @@ def pmc_config(wl):
     for _ in range(2):
         swa.prefill_dilated(q, k, v, c["W"], c.get("dilation", 1), mode=c["mode"], out=out)
         torch.cuda.synchronize()
-    print("pmc workload %d (%s) done" % (wl, c["name"]), flush=True)
+    print("pmc workload %d (%s, %s) done" % (wl, c["name"], dtype), flush=True)
     return 0
 
 
@@ -287,8 +289,10 @@ def summarize_config_counters(paths, wl):
         print("no prefill dispatch in the counter files", file=sys.stderr)
         return 1
     g = per.get
-    print("%s: kernel %s" % (c["name"], sorted(set(first.values()))))
-    print("counters_kernel_sha256: %s" % source_hash(PREFILL_SOURCE))
+    kernels = sorted(set(first.values()))
+    f32 = any("f32" in kn for kn in kernels)
+    print("%s: kernel %s" % (c["name"], kernels))
+    print("counters_kernel_sha256: %s" % source_hash(PREFILL_F32_SOURCE if f32 else PREFILL_SOURCE))
     for k in sorted(per):
         print("  %-32s %.6g" % (k, per[k]))
     t = max(dur.values())
@@ -300,6 +304,11 @@ def summarize_config_counters(paths, wl):
     if g("SQ_VALU_MFMA_BUSY_CYCLES") is not None:
         print("  MFMA busy %.1f%% of SIMD cycles"
               % (100.0 * g("SQ_VALU_MFMA_BUSY_CYCLES") / (cycles * N_SIMD)))
+    if f32 and g("SQ_INSTS_MFMA"):
+        # v_mfma_f32_32x32x2_f32: 4096 FLOP, 64 cycles of a SIMD's matrix core
+        # (157.3 TFLOP/s = 1024 SIMDs x 2.4 GHz x 64 FLOP per cycle)
+        print("  fp32 matrix products %.4g = %.1f cycles each of the busy count"
+              % (g("SQ_INSTS_MFMA"), (g("SQ_VALU_MFMA_BUSY_CYCLES") or 0) / g("SQ_INSTS_MFMA")))
     if g("SQ_LDS_IDX_ACTIVE") is not None:
         print("  LDS busy (indexed access) %.1f%% of CU cycles"
               % (100.0 * g("SQ_LDS_IDX_ACTIVE") / (cycles * N_CU)))
@@ -835,6 +844,8 @@ def main():
     ap.add_argument("--summarize-config-counters", nargs="+", metavar="CSV",
                     help="SQ counters of a --pmc-config run (with --config N)")
     ap.add_argument("--config", type=int, default=5, help="configuration of the summary")
+    ap.add_argument("--pmc-dtype", choices=("bf16", "f32"), default="bf16",
+                    help="input type of the --pmc-config workload")
     ap.add_argument("--trace-global", type=int, metavar="N",
                     help="instead of the benchmark line: 13 flushed calls of the window plus "
                          "global tokens configuration N (run under rocprofv3 --kernel-trace)")
@@ -860,7 +871,7 @@ def main():
     if args.pmc_small:
         return pmc_small()
     if args.pmc_config:
-        return pmc_config(args.pmc_config)
+        return pmc_config(args.pmc_config, args.pmc_dtype)
     if args.summarize_config_counters:
         return summarize_config_counters(args.summarize_config_counters, args.config)
     if args.trace_global:
