@@ -209,19 +209,21 @@ def test_largest_scale_is_a_hard_maximum(swa, dtype, scale, mode, T, W, d):
         assert_fp32_exponent_bound(got, ref, q, k, v, scale, what)
 
 
-def test_deterministic(swa):
-    q, k, v = small_inputs(12, 1, 8, 2, 1000, 128, "bf16")
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_deterministic(swa, dtype):
+    q, k, v = small_inputs(12, 1, 8, 2, 1000, 128, dtype)
     a = run(swa, q, k, v, 300, 0)
     b = run(swa, q, k, v, 300, 0)
     assert torch.equal(a, b)
 
 
-def test_scale_argument_and_negative_scale(swa):
-    q, k, v = small_inputs(13, 1, 2, 1, 200, 64, "bf16")
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_scale_argument_and_negative_scale(swa, dtype):
+    q, k, v = small_inputs(13, 1, 2, 1, 200, 64, dtype)
     for scale in (0.5, -0.2, 0.0):
         got = to_f64(run(swa, q, k, v, 50, 0, scale=scale))
         ref = oracle.attention_dense(q.values, k.values, v.values, 50, 0, scale)
-        assert_parity(got, ref, "bf16", "scale=%g" % scale)
+        assert_parity(got, ref, dtype, "scale=%g" % scale)
 
 
 # fp32 on the matrix cores: plain windows spanning many 64-key tiles and
