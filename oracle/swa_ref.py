@@ -30,7 +30,7 @@ Shapes (head-major, contiguous):
 Query head h reads KV head h // (Hq // Hkv) (grouped-query attention with
 contiguous groups; the pages only say "GQA 32/8").
 
-Readings of points the pages leave open (each also listed in the design doc):
+Readings of points the pages leave open:
   * symmetric window: |i-j| <= floor(W/2), inclusive on both sides, so an
     interior row sees W+1 keys when W is even;
   * windows are clipped to [0, T): no padding, no sink tokens;
