@@ -601,10 +601,23 @@ def measured_peaks(swa, dev, timed):
         ms = timed(lambda: swa.calib_stream_read(src, rsink, grid), False)
         best = max(best, src.numel() * 4 / ms / 1e6)
     del src
+    # the vector ALU: fp32 FMA and v_exp_f32 chains at eight waves per SIMD;
+    # ns per wave instruction per SIMD, and the exponential's cost in FMAs
+    vsink = torch.empty(2048 * 256, dtype=torch.float32, device=dev)
+    ns_per = {}
+    for op in (0, 1):
+        iters = 8000
+        n_instr = swa.calib_vector(op, vsink, 2048, iters)
+        ms = timed(lambda: swa.calib_vector(op, vsink, 2048, iters), False)
+        ns_per[op] = ms * 1e6 / (n_instr / N_SIMD)
     return {"config": "measured peaks", "mfma_bf16_tflops": round(mfma_tflops, 1),
             "frac_of_published_mfma": round(mfma_tflops / PEAK_BF16_TFLOPS, 3),
             "stream_read_gbs": round(best, 1),
-            "frac_of_published_hbm": round(best / PEAK_HBM_GBS, 3)}
+            "frac_of_published_hbm": round(best / PEAK_HBM_GBS, 3),
+            "fma_f32_ns_per_wave_instr": round(ns_per[0], 3),
+            "exp_f32_ns_per_wave_instr": round(ns_per[1], 3),
+            "exp_cost_in_fmas": round(ns_per[1] / ns_per[0], 2),
+            "fma_f32_tflops": round(2 * 64 * N_SIMD / ns_per[0] / 1e3, 1)}
 
 
 def all_configs(reps, peaks_only=False):

@@ -78,6 +78,8 @@ def load():
     lib.swa_calib_mfma_bf16.restype = i
     lib.swa_calib_stream_read.argtypes = [vp, sz, vp, i, vp]
     lib.swa_calib_stream_read.restype = i
+    lib.swa_calib_vector.argtypes = [i, vp, i, i, vp]
+    lib.swa_calib_vector.restype = i
     lib.swa_status_string.argtypes = [i]
     lib.swa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -447,3 +449,16 @@ def calib_stream_read(src, sink, n_wg, stream=None):
                                       _stream(stream))
     _raise("swa_calib_stream_read", st)
     return nbytes
+
+
+def calib_vector(op, sink, n_wg, iters, stream=None):
+    """Vector-ALU calibration (see swa_calib_vector): op 0 fp32 FMA chains, op
+    1 exp2 chains; `sink` a float32 tensor of at least n_wg * 256 elements.
+    Returns the wave instructions it issues."""
+    import torch
+    _check(sink, "sink", sink.dim(), torch.float32)
+    if sink.numel() < n_wg * 256:
+        raise ValueError("sink needs n_wg * 256 elements")
+    st = load().swa_calib_vector(int(op), sink.data_ptr(), int(n_wg), int(iters), _stream(stream))
+    _raise("swa_calib_vector", st)
+    return n_wg * 4 * iters * 16

@@ -348,6 +348,15 @@ int swa_calib_stream_read(const void* src, size_t bytes, unsigned* sink, int n_w
   return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH;
 }
 
+int swa_calib_vector(int op, float* sink, int n_wg, int iters, void* stream) {
+  if (op != 0 && op != 1) return SWA_ERR_INVALID_ARG;
+  if (!sink || !aligned16(sink)) return SWA_ERR_INVALID_ARG;
+  if (n_wg <= 0 || n_wg > (1 << 20) || iters < 0) return SWA_ERR_INVALID_ARG;
+  const hipError_t e =
+      swa::launch_calib_vector(op, sink, n_wg, iters, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH;
+}
+
 const char* swa_status_string(int status) {
   switch (status) {
     case SWA_OK:

@@ -6,7 +6,9 @@
 //     operands (the chip lowers its clock under random-data matrix load, so
 //     constant or zero operands would overstate what attention can reach);
 //   * HBM: a streaming read of a buffer larger than the Infinity Cache with
-//     16-byte non-temporal loads, several in flight per lane.
+//     16-byte non-temporal loads, several in flight per lane;
+//   * the vector ALU: the issue rate of fp32 FMAs and of v_exp_f32 (the
+//     softmax's exponential), sixteen independent chains per lane.
 
 #include "swa_device.h"
 #include "swa_launch.h"
@@ -69,7 +71,40 @@ __global__ __launch_bounds__(256) void calib_read_kernel(const u32x4* __restrict
   sink[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
+// OP 0: x = fma(x, 0.999, 0.001); OP 1: x = -exp2(x).  Both chains stay in
+// [-1.1, 1] from the starting values below, so no lane meets a special value.
+template <int OP>
+__global__ __launch_bounds__(256) void calib_vector_kernel(float* __restrict__ sink, int iters) {
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  float x[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) x[j] = -1.0e-3f * (float)((threadIdx.x + 16 * j) & 1023);
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if constexpr (OP == 0) {
+        x[j] = fmaf(x[j], 0.999f, 0.001f);
+      } else {
+        x[j] = -__builtin_amdgcn_exp2f(x[j]);
+      }
+    }
+  }
+  float t = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) t += x[j];
+  sink[gid] = t;  // keeps the chains live
+}
+
 }  // namespace
+
+hipError_t launch_calib_vector(int op, float* sink, int n_wg, int iters, hipStream_t stream) {
+  if (op == 0) {
+    hipLaunchKernelGGL(calib_vector_kernel<0>, dim3((unsigned)n_wg), dim3(256), 0, stream, sink, iters);
+  } else {
+    hipLaunchKernelGGL(calib_vector_kernel<1>, dim3((unsigned)n_wg), dim3(256), 0, stream, sink, iters);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_calib_mfma(const void* ops, int nfrag, float* sink, int n_wg, int iters,
                              hipStream_t stream) {

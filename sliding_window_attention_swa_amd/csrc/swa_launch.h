@@ -99,10 +99,12 @@ hipError_t launch_decode(const void* q, const void* k_ring, const void* v_ring,
                          float scale, int dtype, float* workspace, hipStream_t stream);
 
 // Calibration: a matrix-core loop on random bf16 operands (nfrag 16-byte
-// fragments) and a streaming non-temporal read of n16 16-byte vectors.
+// fragments), a streaming non-temporal read of n16 16-byte vectors, and
+// vector-ALU chains (op 0 fp32 FMA, op 1 exp2).
 hipError_t launch_calib_mfma(const void* ops, int nfrag, float* sink, int n_wg, int iters,
                              hipStream_t stream);
 hipError_t launch_calib_read(const void* src, size_t n16, unsigned* sink, int n_wg,
                              hipStream_t stream);
+hipError_t launch_calib_vector(int op, float* sink, int n_wg, int iters, hipStream_t stream);
 
 }  // namespace swa

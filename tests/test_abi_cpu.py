@@ -44,7 +44,8 @@ def test_headers_declare_the_entry_points():
         "swa_prefill_dilated_global",
         "swa_decode_sinks", "swa_decode_sinks_workspace_bytes", "swa_decode_noalloc"])
     # the calibration kernels compute nothing of the method: a header of their own
-    assert declared_functions(HEADERS[1:]) == ["swa_calib_mfma_bf16", "swa_calib_stream_read"]
+    assert declared_functions(HEADERS[1:]) == ["swa_calib_mfma_bf16", "swa_calib_stream_read",
+                                               "swa_calib_vector"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -333,6 +334,19 @@ def calib_read(lib, src=P, nbytes=2**20, sink=P, n_wg=8):
 ])
 def test_calib_read_rejects(lib, kw, status):
     assert calib_read(lib, **kw) == status
+
+
+def calib_vector(lib, op=0, sink=P, n_wg=8, iters=10):
+    return lib.swa_calib_vector(op, sink, n_wg, iters, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(op=-1), INVALID), (dict(op=2), INVALID), (dict(sink=None), INVALID),
+    (dict(sink=MIS), INVALID), (dict(n_wg=0), INVALID), (dict(n_wg=2**20 + 1), INVALID),
+    (dict(iters=-1), INVALID), (dict(op=1, iters=-5), INVALID),
+])
+def test_calib_vector_rejects(lib, kw, status):
+    assert calib_vector(lib, **kw) == status
 
 
 def test_status_strings(lib):

@@ -4,7 +4,10 @@ The streaming read is checked exactly: each lane's XOR equals the XOR of the
 16-byte vectors it is assigned (workgroup w reads the w-th contiguous chunk,
 lane t every 256th vector of it from the t-th), computed on the host, for
 sizes with ragged chunks and tails.  The matrix-core loop is checked for
-finite, repeatable sums (its FLOP count is fixed by construction)."""
+finite, repeatable sums (its FLOP count is fixed by construction).  The
+vector chains are checked against a host recurrence: the FMA chain in float64
+(the chain contracts, so one rounding per step keeps it within 1e-5), the
+exp2 chain against float64 exp2 within the instruction's accuracy."""
 
 import numpy as np
 import pytest
@@ -64,3 +67,20 @@ def test_mfma_loop_is_finite_and_repeatable(swa):
     assert torch.isfinite(a).all()
     assert torch.equal(a, b)
     assert a.abs().sum() > 0
+
+
+@pytest.mark.parametrize("op", [0, 1])
+def test_vector_chains_follow_their_recurrence(swa, op):
+    n_wg, iters = 4, 37
+    sink = torch.empty(n_wg * 256, dtype=torch.float32, device="cuda")
+    assert swa.calib_vector(op, sink, n_wg, iters) == n_wg * 4 * iters * 16
+    torch.cuda.synchronize()
+    got = sink.cpu().numpy().astype(np.float64)
+    # lane t (of its workgroup) starts chain j at -1e-3 * ((t + 16 j) mod 1024)
+    t = np.arange(256)
+    x = np.stack([-1e-3 * ((t + 16 * j) % 1024) for j in range(16)]).astype(np.float32).astype(np.float64)
+    for _ in range(iters):
+        x = x * 0.999 + 0.001 if op == 0 else -np.exp2(x)
+    want = np.tile(x.sum(axis=0), n_wg)
+    assert np.all(np.isfinite(got))
+    assert np.max(np.abs(got - want)) < 1e-4
